@@ -1,0 +1,361 @@
+/*
+ * oracle.c - plain, slow CPU oracle of the BitNet b1.58 BitLinear forward pass
+ * and of its BitNet v2 H-BitLinear variant.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  The GPU library never
+ * links, includes or calls it, and it shares no code with the GPU library.
+ *
+ * Every function below is the literal definition of one step, written as
+ * nested loops in IEEE float32 / float64 with no blocking, fusion or
+ * reordering.  Build with `-O2 -ffp-contract=off` (no FMA contraction, no
+ * fast-math) so that each float operation written here is one IEEE rounding.
+ *
+ * Pages cited (titles as they appear on the pages):
+ *   [FT]  "LLM을 1.58비트로 파인튜닝: BitNet을 이용한 극단적인 양자화"
+ *         (Hugging Face fine-tuning write-up), sections
+ *         "양자화 메커니즘" (quantization mechanism), "계산 패러다임"
+ *         (computation paradigm), "주요 결과" (main results).
+ *   [V2]  "초저용량 LLM의 진화: BitNet v2 파헤치기 (1비트 LLM을 위한 4비트 활성화)",
+ *         section "방법론" (method).
+ *   [2B]  "AI 혁신의 선두: 마이크로소프트의 1비트 LLM, BitNet b1.58 2B4T",
+ *         sections "주요 아키텍처 혁신" (architecture) and
+ *         "훈련 안정성 및 효율성 향상" (normalisation before quantisation).
+ *   [QP]  endplan.ai quantization primer "양자화(quantization) 1.58bit",
+ *         sections "그러면 크기를 더 못줄이나요?" (absmax example) and
+ *         "1.58비트는 어디서 나온거에요?" (three weight values).
+ *
+ * Readings where the pages are silent (each one is listed in the design notes):
+ *   - "round" is round-half-to-even (rintf under the default rounding mode).
+ *   - The weight absmean is accumulated in float64: each row left to right,
+ *     then the row sums top to bottom.
+ *   - The normalisation is RMSNorm without mean subtraction.  Its positive
+ *     per-token factor 1/rms is folded into the dequantisation scale, so the
+ *     activation codes are computed from u = x * gain alone (absmax
+ *     quantisation is invariant to a positive per-token factor).
+ *   - int8 codes use the factor 127/absmax; int4 codes use 7/absmax and the
+ *     range [-8, 7].
+ *   - The Hadamard transform is the unnormalised Sylvester-order transform,
+ *     computed by butterflies with the stage distance ascending 1, 2, 4, ...;
+ *     its 1/sqrt(K) normalisation is folded into the float scales.
+ *   - Packed layout: row n of the [N][K] weight matrix owns K/4 bytes; the
+ *     32-bit little-endian word g of the row holds weights 16g .. 16g+15, and
+ *     weight 16g + 4i + b lives in bits 2i..2i+1 of byte b of that word.  The
+ *     stored 2-bit field is q + 1, so it takes the values 0, 1 and 2.
+ *
+ * Parity pins for every function live in the oracle self-tests.  Nothing here
+ * is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_VERSION 1
+
+int oracle_version(void) { return ORACLE_VERSION; }
+
+/* bfloat16 bits -> float32 (exact: bf16 is the top half of a float32). */
+static float bf16_bits_to_float(uint16_t h) {
+    uint32_t u = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Packed-weight layout helpers.                                             */
+/* ------------------------------------------------------------------------- */
+
+/* Byte offset (inside one packed row) and bit shift of weight k. */
+static int64_t packed_byte_of(int64_t k) { return 4 * (k / 16) + (k % 4); }
+static int packed_shift_of(int64_t k) { return (int)(2 * ((k % 16) / 4)); }
+
+/*
+ * Unpack a packed [N][K/4] matrix into ternary values q in {-1, 0, +1}.
+ * Returns the number of 2-bit fields equal to 3 (an invalid code; 0 for any
+ * matrix written by oracle_pack_weights).  Invalid fields are stored as 0.
+ */
+int64_t oracle_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* q) {
+    int64_t bad = 0;
+    const int64_t row_bytes = K / 4;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            int field = (packed[n * row_bytes + packed_byte_of(k)] >> packed_shift_of(k)) & 3;
+            if (field == 3) {
+                bad++;
+                q[n * K + k] = 0;
+            } else {
+                q[n * K + k] = (int8_t)(field - 1);
+            }
+        }
+    }
+    return bad;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Walsh-Hadamard transform ([V2] "방법론": Hadamard transform of the        */
+/* activations before 4-bit quantisation).                                   */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * In-place unnormalised Walsh-Hadamard transform of v[0..n) in float32,
+ * Sylvester (natural) order: the result is H v with H[i][j] = (-1)^popcount(i&j).
+ * n must be a power of two.  Stages run with the butterfly distance h
+ * ascending; each butterfly replaces (a, b) by (a + b, a - b), one float32
+ * rounding each.
+ */
+void oracle_fwht_f32(float* v, int64_t n) {
+    for (int64_t h = 1; h < n; h *= 2) {
+        for (int64_t i = 0; i < n; i++) {
+            if ((i & h) == 0) {
+                float a = v[i];
+                float b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* O1: weight quantisation and packing ([FT] "양자화 메커니즘", Weights;     */
+/* [2B] "주요 아키텍처 혁신": absmean mapping to {-1, 0, +1};                 */
+/* [FT] "주요 결과": weights stored packed in int8 tensors).                  */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * W: float32 [N][K] row-major (out features x in features).
+ * hadamard = 1: first replace every row by its Walsh-Hadamard transform
+ *   (weights pre-rotated by the same transform the H-BitLinear activations
+ *   get), then quantise the rotated rows.
+ * Outputs:
+ *   packed  [N][K/4] bytes in the layout described at the top of this file.
+ *   w_scale [2]: w_scale[0] = d_w, the dequantisation multiplier
+ *                (mean |W|, divided by sqrt(K) when hadamard = 1);
+ *                w_scale[1] = s_w, the quantisation factor 1 / mean |W|.
+ *   q_out   [N][K] ternary values (may be NULL).
+ * Requires K % 16 == 0 (and K a power of two when hadamard = 1).
+ * Returns 0 on success, -1 on bad arguments or allocation failure.
+ */
+int oracle_pack_weights(const float* W, int64_t N, int64_t K, int hadamard,
+                        uint8_t* packed, float* w_scale, int8_t* q_out) {
+    if (N < 1 || K < 16 || K % 16 != 0) return -1;
+    if (hadamard && (K & (K - 1)) != 0) return -1;
+
+    float* R = (float*)malloc((size_t)N * (size_t)K * sizeof(float));
+    if (!R) return -1;
+    memcpy(R, W, (size_t)N * (size_t)K * sizeof(float));
+    if (hadamard) {
+        for (int64_t n = 0; n < N; n++) oracle_fwht_f32(R + n * K, K);
+    }
+
+    /* Mean absolute value in float64: rows left to right, then rows in order. */
+    double* row_sum = (double*)malloc((size_t)N * sizeof(double));
+    if (!row_sum) {
+        free(R);
+        return -1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        double r = 0.0;
+        for (int64_t k = 0; k < K; k++) r += fabs((double)R[n * K + k]);
+        row_sum[n] = r;
+    }
+    double S = 0.0;
+    for (int64_t n = 0; n < N; n++) S += row_sum[n];
+    free(row_sum);
+
+    const double gamma = S / ((double)N * (double)K);
+    float s_w, d_w;
+    if (gamma == 0.0) {
+        s_w = 0.0f; /* all-zero matrix: every code is 0 */
+        d_w = 0.0f;
+    } else {
+        s_w = (float)(1.0 / gamma);
+        d_w = hadamard ? (float)(gamma / sqrt((double)K)) : (float)gamma;
+    }
+    w_scale[0] = d_w;
+    w_scale[1] = s_w;
+
+    /* Scale, round half to even, clamp to [-1, 1]; store q + 1 in 2 bits. */
+    const int64_t row_bytes = K / 4;
+    memset(packed, 0, (size_t)N * (size_t)row_bytes);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            float v = R[n * K + k] * s_w;
+            float r = rintf(v);
+            int q = (r > 1.0f) ? 1 : (r < -1.0f ? -1 : (int)r);
+            if (q_out) q_out[n * K + k] = (int8_t)q;
+            packed[n * row_bytes + packed_byte_of(k)] |= (uint8_t)((q + 1) << packed_shift_of(k));
+        }
+    }
+    free(R);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O2: RMSNorm + per-token absmax int8 quantisation ([FT] "양자화 메커니즘", */
+/* Activations: absmax per token into [-128, 127], normalisation first;      */
+/* [QP] absmax example: multiply by 127/absmax, dequantise by dividing).     */
+/* ------------------------------------------------------------------------- */
+
+/* Tokens whose absmax is below this are treated as all-zero. */
+static const float TINY_ABSMAX = 0x1p-120f;
+
+/*
+ * x: bf16 bits [M][K]; gain: float32 [K] or NULL (no gain); eps: RMSNorm eps.
+ * Outputs per token m:
+ *   q[m][k]  int8 codes in [-128, 127]
+ *   d_x[m]   float32 dequantisation multiplier absmax * rstd / 127
+ *   qsum[m]  int32 sum of the token's codes
+ */
+int oracle_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
+                     int8_t* q, float* d_x, int32_t* qsum) {
+    if (M < 0 || K < 1) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        float* u = (float*)malloc((size_t)K * sizeof(float));
+        double sum_sq = 0.0;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; k++) {
+            float xk = bf16_bits_to_float(x[m * K + k]);
+            sum_sq += (double)xk * (double)xk;
+            u[k] = gain ? xk * gain[k] : xk;
+            if (fabsf(u[k]) > a) a = fabsf(u[k]);
+        }
+        const double rstd = 1.0 / sqrt(sum_sq / (double)K + (double)eps);
+        int64_t s = 0;
+        if (a < TINY_ABSMAX) {
+            for (int64_t k = 0; k < K; k++) q[m * K + k] = 0;
+            d_x[m] = 0.0f;
+        } else {
+            const float c = 127.0f / a;
+            for (int64_t k = 0; k < K; k++) {
+                float r = rintf(u[k] * c);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -128.0f) r = -128.0f;
+                q[m * K + k] = (int8_t)r;
+                s += (int64_t)r;
+            }
+            d_x[m] = (float)(((double)a * rstd) / 127.0);
+        }
+        qsum[m] = (int32_t)s;
+        free(u);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O3: RMSNorm + Walsh-Hadamard transform + per-token absmax int4            */
+/* quantisation ([V2] "방법론": Hadamard transform before 4-bit activation    */
+/* quantisation; 1/sqrt(K) normalisation folded into d_x).                    */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Same arguments as oracle_quant_act; K must be a power of two.
+ * Codes are in [-8, 7] (stored one per int8); d_x = absmax(t) * rstd / (7 sqrt K)
+ * where t is the unnormalised transform of u.
+ */
+int oracle_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
+                              int64_t K, int8_t* q, float* d_x, int32_t* qsum) {
+    if (M < 0 || K < 1 || (K & (K - 1)) != 0) return -1;
+    const double sqrt_k = sqrt((double)K);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        float* t = (float*)malloc((size_t)K * sizeof(float));
+        double sum_sq = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            float xk = bf16_bits_to_float(x[m * K + k]);
+            sum_sq += (double)xk * (double)xk;
+            t[k] = gain ? xk * gain[k] : xk;
+        }
+        const double rstd = 1.0 / sqrt(sum_sq / (double)K + (double)eps);
+        oracle_fwht_f32(t, K);
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; k++)
+            if (fabsf(t[k]) > a) a = fabsf(t[k]);
+        int64_t s = 0;
+        if (a < TINY_ABSMAX) {
+            for (int64_t k = 0; k < K; k++) q[m * K + k] = 0;
+            d_x[m] = 0.0f;
+        } else {
+            const float c = 7.0f / a;
+            for (int64_t k = 0; k < K; k++) {
+                float r = rintf(t[k] * c);
+                if (r > 7.0f) r = 7.0f;
+                if (r < -8.0f) r = -8.0f;
+                q[m * K + k] = (int8_t)r;
+                s += (int64_t)r;
+            }
+            d_x[m] = (float)(((double)a * rstd) / (7.0 * sqrt_k));
+        }
+        qsum[m] = (int32_t)s;
+        free(t);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O4: integer contraction ([FT] "계산 패러다임": the ternary matmul needs    */
+/* only integer additions; accumulated in int32).                            */
+/* ------------------------------------------------------------------------- */
+
+/* acc[m][n] = sum_k xq[m][k] * q_w[n][k], q_w unpacked from packed [N][K/4]. */
+int oracle_int_gemm(const int8_t* xq, const uint8_t* packed, int64_t M, int64_t N, int64_t K,
+                    int32_t* acc) {
+    if (M < 0 || N < 0 || K < 16 || K % 16 != 0) return -1;
+    int8_t* qw = (int8_t*)malloc((size_t)N * (size_t)K);
+    if (!qw) return -1;
+    oracle_unpack_weights(packed, N, K, qw);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t n = 0; n < N; n++) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; k++) s += (int64_t)xq[m * K + k] * (int64_t)qw[n * K + k];
+            acc[m * N + n] = (int32_t)s;
+        }
+    }
+    free(qw);
+    return 0;
+}
+
+/*
+ * The same contraction for a list of (m, n) output positions only, for
+ * spot checks of full-size problems.  acc_out[i] = acc[rows[i]][cols[i]].
+ */
+int oracle_int_gemm_sampled(const int8_t* xq, const uint8_t* packed, int64_t M, int64_t N,
+                            int64_t K, const int64_t* rows, const int64_t* cols, int64_t count,
+                            int32_t* acc_out) {
+    if (K < 16 || K % 16 != 0) return -1;
+    const int64_t row_bytes = K / 4;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++) {
+        const int64_t m = rows[i], n = cols[i];
+        int64_t s = 0;
+        if (m < 0 || m >= M || n < 0 || n >= N) {
+            acc_out[i] = 0;
+            continue;
+        }
+        for (int64_t k = 0; k < K; k++) {
+            int field = (packed[n * row_bytes + packed_byte_of(k)] >> packed_shift_of(k)) & 3;
+            s += (int64_t)xq[m * K + k] * (int64_t)(field - 1);
+        }
+        acc_out[i] = (int32_t)s;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O5: dequantisation by both scales ([FT] "양자화 메커니즘": weights are     */
+/* rescaled after rounding; [QP]: dequantise by dividing by the factor).     */
+/* ------------------------------------------------------------------------- */
+
+/* y[m][n] = acc[m][n] * d_x[m] * d_w, in float64. */
+void oracle_dequant(const int32_t* acc, const float* d_x, float d_w, int64_t M, int64_t N,
+                    double* y) {
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t n = 0; n < N; n++)
+            y[m * N + n] = (double)acc[m * N + n] * (double)d_x[m] * (double)d_w;
+}
