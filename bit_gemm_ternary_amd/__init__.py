@@ -1,1 +1,196 @@
-"""bit_gemm_ternary_amd: BitNet b1.58 BitLinear forward on MI355X (gfx950)."""
+"""bit_gemm_ternary_amd: BitNet b1.58 BitLinear forward on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libbitnet_hip.so`` (declared in
+``include/bitnet.h``).  The functions below only check and marshal arguments
+(torch device tensors in, torch device tensors out, the current torch stream
+passed through); every step of the computation runs in the library's HIP
+kernels.  There is no CPU fallback: if the library is missing the calls raise.
+
+    packed, w_scale = pack_weights(W)                 # once per layer
+    xq, x_scale, x_qsum = quant_act(x)                # bf16 [M][K] -> int8 codes
+    y = linear_forward(xq, x_scale, x_qsum, packed, w_scale)
+    y = bitlinear(x, packed, w_scale)                 # both steps
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "BitnetError", "lib", "library_path", "pack_weights", "pack_weights_workspace_bytes",
+    "quant_act", "hadamard_quant_act", "linear_forward", "bitlinear", "BitLinear",
+    "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libbitnet_hip.so")
+_LIB = None
+
+STATUS = {
+    0: "BITNET_OK", 1: "BITNET_ERR_NULL", 2: "BITNET_ERR_SHAPE", 3: "BITNET_ERR_UNSUPPORTED",
+    4: "BITNET_ERR_ALIGN", 5: "BITNET_ERR_WORKSPACE", 6: "BITNET_ERR_HIP", 7: "BITNET_ERR_VALUE",
+}
+
+
+class BitnetError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libbitnet_hip.so`` (built by ``bit_gemm_ternary_amd.build``) and declare its ABI."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m bit_gemm_ternary_amd.build` (there is no fallback path)")
+    L = ctypes.CDLL(_LIB_PATH)
+    p, i64, f32, i32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int,
+                            ctypes.c_size_t)
+    L.bitnet_pack_weights_workspace_bytes.argtypes = [i64, i64, i32]
+    L.bitnet_pack_weights_workspace_bytes.restype = sz
+    L.bitnet_pack_weights.argtypes = [p, i64, i64, i32, p, p, p, sz, p]
+    L.bitnet_pack_weights.restype = i32
+    for name in ("bitnet_quant_act", "bitnet_hadamard_quant_act"):
+        fn = getattr(L, name)
+        fn.argtypes = [p, p, f32, i64, i64, p, p, p, p]
+        fn.restype = i32
+    L.bitnet_linear_forward.argtypes = [p, p, p, p, p, i64, i64, i64, p, p, p]
+    L.bitnet_linear_forward.restype = i32
+    L.bitnet_status_string.argtypes = [i32]
+    L.bitnet_status_string.restype = ctypes.c_char_p
+    L.bitnet_last_error.argtypes = []
+    L.bitnet_last_error.restype = ctypes.c_char_p
+    L.bitnet_version.argtypes = []
+    L.bitnet_version.restype = i32
+    _LIB = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise BitnetError(status, lib().bitnet_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pack_weights_workspace_bytes(N: int, K: int, hadamard: bool = False) -> int:
+    return int(lib().bitnet_pack_weights_workspace_bytes(N, K, int(bool(hadamard))))
+
+
+def pack_weights(W, hadamard: bool = False):
+    """float32 [N][K] device weights -> (packed uint8 [N][K/4], w_scale float32 [2] = (d_w, s_w))."""
+    torch = _torch()
+    _require(W, "W", torch.float32, 2)
+    N, K = W.shape
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    w_scale = torch.empty(2, dtype=torch.float32, device=W.device)
+    ws_bytes = pack_weights_workspace_bytes(N, K, hadamard)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=W.device)
+    _check(lib().bitnet_pack_weights(_ptr(W), N, K, int(bool(hadamard)), _ptr(packed),
+                                     _ptr(w_scale), _ptr(workspace), workspace.numel(),
+                                     _stream(W.device)))
+    return packed, w_scale
+
+
+def _quant(name, x, gain, eps):
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if gain is not None:
+        _require(gain, "gain", torch.float32, 1)
+        if gain.shape[0] != K:
+            raise ValueError(f"gain has {gain.shape[0]} entries, x has K={K}")
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+    x_qsum = torch.empty(M, dtype=torch.int32, device=x.device)
+    _check(getattr(lib(), name)(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K, _ptr(xq),
+                                _ptr(x_scale), _ptr(x_qsum), _stream(x.device)))
+    return xq, x_scale, x_qsum
+
+
+def quant_act(x, gain=None, eps: float = 1e-5):
+    """bf16 [M][K] -> (int8 codes [M][K], d_x float32 [M], code sums int32 [M])."""
+    return _quant("bitnet_quant_act", x, gain, eps)
+
+
+def hadamard_quant_act(x, gain=None, eps: float = 1e-5):
+    """H-BitLinear: bf16 [M][K] (K = 2^p) -> (int4 codes as int8 [M][K], d_x, code sums)."""
+    return _quant("bitnet_hadamard_quant_act", x, gain, eps)
+
+
+def linear_forward(xq, x_scale, x_qsum, packed, w_scale, return_acc: bool = False):
+    """Ternary contraction + dequant: y float32 [M][N] (and int32 accumulators if asked)."""
+    torch = _torch()
+    _require(xq, "xq", torch.int8, 2)
+    _require(x_scale, "x_scale", torch.float32, 1)
+    _require(x_qsum, "x_qsum", torch.int32, 1)
+    _require(packed, "packed", torch.uint8, 2)
+    _require(w_scale, "w_scale", torch.float32, 1)
+    M, K = xq.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}] for K={K}")
+    if x_scale.shape[0] != M or x_qsum.shape[0] != M or w_scale.shape[0] < 1:
+        raise ValueError("x_scale / x_qsum must have M entries and w_scale at least one")
+    y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if return_acc else None
+    _check(lib().bitnet_linear_forward(_ptr(xq), _ptr(x_scale), _ptr(x_qsum), _ptr(packed),
+                                       _ptr(w_scale), M, N, K, _ptr(y), _ptr(acc),
+                                       _stream(xq.device)))
+    return (y, acc) if return_acc else y
+
+
+def bitlinear(x, packed, w_scale, hadamard: bool = False, gain=None, eps: float = 1e-5):
+    """One BitLinear forward: quantise bf16 activations, contract, dequantise."""
+    q = hadamard_quant_act if hadamard else quant_act
+    xq, x_scale, x_qsum = q(x, gain, eps)
+    return linear_forward(xq, x_scale, x_qsum, packed, w_scale)
+
+
+class BitLinear:
+    """A bias-free linear layer with ternary weights, packed once at construction."""
+
+    def __init__(self, weight, hadamard: bool = False, gain=None, eps: float = 1e-5):
+        self.out_features, self.in_features = weight.shape
+        self.hadamard = bool(hadamard)
+        self.gain = gain
+        self.eps = float(eps)
+        self.packed, self.w_scale = pack_weights(weight, hadamard=self.hadamard)
+
+    def __call__(self, x):
+        return bitlinear(x, self.packed, self.w_scale, self.hadamard, self.gain, self.eps)

@@ -1,0 +1,169 @@
+// api.cpp - the C ABI declared in include/bitnet.h: argument validation (before
+// any HIP call), kernel selection and launch on the caller's stream, and
+// thread-local error reporting.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+
+#include "../../include/bitnet.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return BITNET_OK;
+    return fail(BITNET_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxRows = 2147483647;  // 2^31 - 1
+constexpr int64_t kMinK = 64, kMaxK = 65536;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int check_k(int64_t K, const char* fn) {
+    if (K < kMinK || K > kMaxK || K % 64 != 0)
+        return fail(BITNET_ERR_SHAPE, "%s: K=%lld must be a multiple of 64 in [64, 65536]", fn,
+                    (long long)K);
+    return BITNET_OK;
+}
+
+int check_hadamard_k(int64_t K, const char* fn) {
+    if (!is_pow2(K) || K < 256 || K > 32768)
+        return fail(BITNET_ERR_UNSUPPORTED,
+                    "%s: the Hadamard transform needs K a power of two in [256, 32768], got %lld",
+                    fn, (long long)K);
+    return BITNET_OK;
+}
+
+int check_eps(float eps, const char* fn) {
+    if (!std::isfinite(eps) || eps < 0.f)
+        return fail(BITNET_ERR_VALUE, "%s: eps must be finite and >= 0", fn);
+    return BITNET_OK;
+}
+
+int validate_quant(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
+                   int8_t* xq, float* x_scale, int32_t* x_qsum, bool hadamard, const char* fn) {
+    if (M < 0 || M > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (hadamard && (s = check_hadamard_k(K, fn)) != BITNET_OK) return s;
+    if ((s = check_eps(eps, fn)) != BITNET_OK) return s;
+    if (M == 0) return BITNET_OK;
+    if (!x || !xq || !x_scale || !x_qsum)
+        return fail(BITNET_ERR_NULL, "%s: x, xq, x_scale and x_qsum must not be NULL", fn);
+    if (!aligned(x, 16) || !aligned(xq, 16) || (gain && !aligned(gain, 16)))
+        return fail(BITNET_ERR_ALIGN, "%s: x, xq and gain must be 16-byte aligned", fn);
+    if (!aligned(x_scale, 4) || !aligned(x_qsum, 4))
+        return fail(BITNET_ERR_ALIGN, "%s: x_scale and x_qsum must be 4-byte aligned", fn);
+    return BITNET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bitnet_pack_weights_workspace_bytes(int64_t N, int64_t K, int hadamard) {
+    if (N < 1 || N > kMaxRows || K < kMinK || K > kMaxK) return 0;
+    return bitnet::pack_workspace_bytes(N, K, hadamard ? 1 : 0);
+}
+
+int bitnet_pack_weights(const float* W, int64_t N, int64_t K, int hadamard, uint8_t* packed,
+                        float* w_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "bitnet_pack_weights";
+    if (N < 1 || N > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (hadamard != 0 && hadamard != 1) return fail(BITNET_ERR_VALUE, "%s: hadamard must be 0 or 1", fn);
+    if (hadamard && (s = check_hadamard_k(K, fn)) != BITNET_OK) return s;
+    if (!W || !packed || !w_scale || !workspace)
+        return fail(BITNET_ERR_NULL, "%s: W, packed, w_scale and workspace must not be NULL", fn);
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(workspace, 16) || !aligned(w_scale, 4))
+        return fail(BITNET_ERR_ALIGN, "%s: W, packed and workspace must be 16-byte aligned", fn);
+    const size_t need = bitnet::pack_workspace_bytes(N, K, hadamard);
+    if (workspace_bytes < need)
+        return fail(BITNET_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
+                    workspace_bytes, need);
+    const double sqrt_k = std::sqrt((double)K);
+    return hip_status(bitnet::launch_pack_weights(W, N, K, hadamard, sqrt_k, packed, w_scale,
+                                                  workspace, (hipStream_t)stream),
+                      fn);
+}
+
+int bitnet_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
+                     int8_t* xq, float* x_scale, int32_t* x_qsum, void* stream) {
+    const char* fn = "bitnet_quant_act";
+    int s = validate_quant(x, gain, eps, M, K, xq, x_scale, x_qsum, false, fn);
+    if (s != BITNET_OK || M == 0) return s;
+    return hip_status(bitnet::launch_quant_act(x, gain, eps, M, K, xq, x_scale, x_qsum,
+                                               (hipStream_t)stream),
+                      fn);
+}
+
+int bitnet_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
+                              int64_t K, int8_t* xq, float* x_scale, int32_t* x_qsum,
+                              void* stream) {
+    const char* fn = "bitnet_hadamard_quant_act";
+    int s = validate_quant(x, gain, eps, M, K, xq, x_scale, x_qsum, true, fn);
+    if (s != BITNET_OK || M == 0) return s;
+    return hip_status(bitnet::launch_hadamard_quant_act(x, gain, eps, M, K, std::sqrt((double)K), xq,
+                                                        x_scale, x_qsum, (hipStream_t)stream),
+                      fn);
+}
+
+int bitnet_linear_forward(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
+                          const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc, void* stream) {
+    const char* fn = "bitnet_linear_forward";
+    if (M < 0 || M > kMaxRows || N < 0 || N > kMaxRows)
+        return fail(BITNET_ERR_SHAPE, "%s: M=%lld or N=%lld out of range", fn, (long long)M, (long long)N);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!xq || !x_scale || !x_qsum || !packed || !w_scale || !y)
+        return fail(BITNET_ERR_NULL, "%s: only acc may be NULL", fn);
+    if (!aligned(xq, 16) || !aligned(packed, 16))
+        return fail(BITNET_ERR_ALIGN, "%s: xq and packed must be 16-byte aligned", fn);
+    if (!aligned(x_scale, 4) || !aligned(x_qsum, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+        (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "%s: scales, sums, y and acc must be 4-byte aligned", fn);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = bitnet::gemv_supported(M, K)
+                       ? bitnet::launch_gemv(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, st)
+                       : bitnet::launch_gemm(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, st);
+    return hip_status(e, fn);
+}
+
+const char* bitnet_status_string(int status) {
+    switch (status) {
+        case BITNET_OK: return "ok";
+        case BITNET_ERR_NULL: return "a required pointer is NULL";
+        case BITNET_ERR_SHAPE: return "shape out of range";
+        case BITNET_ERR_UNSUPPORTED: return "unsupported shape";
+        case BITNET_ERR_ALIGN: return "misaligned pointer";
+        case BITNET_ERR_WORKSPACE: return "workspace missing or too small";
+        case BITNET_ERR_HIP: return "HIP error";
+        case BITNET_ERR_VALUE: return "invalid scalar argument";
+        default: return "unknown status";
+    }
+}
+
+const char* bitnet_last_error(void) { return g_last_error; }
+
+int bitnet_version(void) { return BITNET_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+/*
+ * bitnet.h - C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear forward pass.
+ *
+ * A BitLinear layer replaces a bias-free linear layer y = W x.  Its weights are
+ * quantised once to the three values {-1, 0, +1} with one per-tensor scale and
+ * stored packed, four weights per byte; at every forward the activations are
+ * RMS-normalised and quantised per token (int8 absmax, or, for the BitNet v2
+ * H-BitLinear variant, Walsh-Hadamard transform + int4 absmax), contracted
+ * against the ternary weights with integer arithmetic accumulated in int32,
+ * and dequantised by both scales into float32.
+ *
+ * Pages this follows (titles as printed on them):
+ *   [FT] "LLM을 1.58비트로 파인튜닝: BitNet을 이용한 극단적인 양자화"
+ *        (Hugging Face fine-tuning write-up): section "양자화 메커니즘"
+ *        (per-tensor absmean weight scale, round, clamp to [-1, 1], rescale;
+ *        per-token absmax int8 activations after normalisation), "계산 패러다임"
+ *        (the matmul becomes integer additions), "주요 결과" (weights packed in
+ *        int8 tensors), "추론 최적화 및 커스텀 커널" (weights unpacked on the fly
+ *        inside the matmul), "Transformers와의 통합" (drop-in linear layer).
+ *   [V2] "초저용량 LLM의 진화: BitNet v2 파헤치기 (1비트 LLM을 위한 4비트 활성화)",
+ *        section "방법론" (Hadamard transform of the activations before 4-bit
+ *        quantisation).
+ *   [2B] "AI 혁신의 선두: 마이크로소프트의 1비트 LLM, BitNet b1.58 2B4T", section
+ *        "주요 아키텍처 혁신" (ternary weights by absmean; no bias term).
+ *   [QP] endplan.ai primer "양자화(quantization) 1.58bit", section
+ *        "그러면 크기를 더 못줄이나요?" (absmax factor 127/absmax; dequantise by
+ *        dividing by it).
+ *
+ * Conventions shared by every call:
+ *   - All array arguments are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or keeps them after the call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *     default stream) and the call returns before it completes.  Outputs are
+ *     valid, and inputs may be released, once the stream has been synchronised.
+ *   - Outputs must not alias inputs.
+ *   - Every argument is validated on the host before anything is enqueued; on
+ *     a non-OK status nothing was launched and no output was touched.  A HIP
+ *     launch failure returns BITNET_ERR_HIP.  Device faults surface at the
+ *     caller's next synchronising HIP call.
+ *   - bitnet_last_error() returns a thread-local description of the last
+ *     non-OK status returned on the calling thread.
+ *   - Calls are re-entrant; concurrent calls on different streams are allowed.
+ *   - Matrices are row-major.  Weights are [N][K] (out features x in
+ *     features); activations and outputs are [M][K] and [M][N] (tokens first).
+ *   - Shape limits: 0 <= M, N <= 2^31 - 1; 64 <= K <= 65536 with K % 64 == 0.
+ *     The Hadamard calls need K to be a power of two with 256 <= K <= 32768.
+ */
+#ifndef BITNET_H
+#define BITNET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BITNET_ABI_VERSION 1
+
+typedef enum {
+    BITNET_OK = 0,
+    BITNET_ERR_NULL = 1,         /* a required pointer is NULL */
+    BITNET_ERR_SHAPE = 2,        /* M, N or K out of range, or K % 64 != 0 */
+    BITNET_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement
+                                    (Hadamard with K not a power of two in [256, 32768]) */
+    BITNET_ERR_ALIGN = 4,        /* a device pointer is not aligned as documented */
+    BITNET_ERR_WORKSPACE = 5,    /* pack workspace missing or too small */
+    BITNET_ERR_HIP = 6,          /* a HIP launch or runtime call failed */
+    BITNET_ERR_VALUE = 7         /* a scalar argument is invalid (eps < 0 or not finite,
+                                    hadamard not 0 or 1) */
+} bitnet_status;
+
+/*
+ * Packed weight layout (a format of this library; the pages only say that the
+ * ternary weights are stored packed in int8 tensors, [FT] "주요 결과"):
+ *   packed is uint8 [N][K/4]; row n holds the K weights of output feature n.
+ *   Read as little-endian 32-bit words, word g of a row holds weights
+ *   16g .. 16g+15, weight 16g + 4i + b in bits 2i..2i+1 of byte b of the word.
+ *   The 2-bit field is q + 1 (0, 1 or 2 for q = -1, 0, +1; 3 is never written).
+ *   So (word >> 2i) & 0x03030303 gives the fields of weights 16g+4i .. 16g+4i+3
+ *   as four bytes in order, ready for byte-wise dot products.
+ */
+
+/* Bytes of device workspace bitnet_pack_weights needs for an N x K matrix. */
+size_t bitnet_pack_weights_workspace_bytes(int64_t N, int64_t K, int hadamard);
+
+/*
+ * Weight quantisation and packing ([FT] "양자화 메커니즘", weights;
+ * [2B] "주요 아키텍처 혁신"; [FT] "주요 결과").  Run once per layer.
+ *
+ *   W          in   float32 [N][K], 16-byte aligned.
+ *   N, K            N >= 1; K as in the shape limits.
+ *   hadamard        0: quantise W.  1: first replace every row of W by its
+ *                   unnormalised Walsh-Hadamard transform (Sylvester order),
+ *                   so the layer can take Hadamard-transformed activations
+ *                   (bitnet_hadamard_quant_act); needs K a power of two.
+ *   packed     out  uint8 [N][K/4] in the layout above, 16-byte aligned.
+ *   w_scale    out  float32 [2]: w_scale[0] = d_w, the dequantisation
+ *                   multiplier: gamma = mean |W| over all N*K entries
+ *                   (accumulated in float64, each row left to right then the
+ *                   rows in order), rounded to float32 (hadamard = 1: gamma of
+ *                   the transformed rows divided by sqrt(K));
+ *                   w_scale[1] = s_w = float32(1 / gamma), the quantisation
+ *                   factor.  Codes are q = clamp(rint(w * s_w), -1, 1) with
+ *                   w * s_w one float32 multiply and rint round-half-to-even.
+ *                   An all-zero W gives d_w = s_w = 0 and every q = 0.
+ *   workspace       device scratch of at least
+ *                   bitnet_pack_weights_workspace_bytes(N, K, hadamard) bytes,
+ *                   16-byte aligned; contents undefined afterwards.
+ */
+int bitnet_pack_weights(const float* W, int64_t N, int64_t K, int hadamard, uint8_t* packed,
+                        float* w_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused RMSNorm + per-token absmax int8 activation quantisation
+ * ([FT] "양자화 메커니즘", activations; [QP] absmax factor 127/absmax).
+ *
+ *   x          in   bf16 [M][K] (raw uint16 bit patterns), 16-byte aligned.
+ *   gain       in   float32 [K] RMSNorm gain, or NULL for none; 16-byte aligned.
+ *   eps             RMSNorm epsilon (finite, >= 0).
+ *   xq         out  int8 [M][K] codes, 16-byte aligned.
+ *   x_scale    out  float32 [M]: d_x[m] = absmax * rstd / 127 (float64, then
+ *                   rounded to float32), the dequantisation multiplier.
+ *   x_qsum     out  int32 [M]: sum of the token's codes (needed by
+ *                   bitnet_linear_forward).
+ * Per token: u = x * gain (float32), a = max |u|, rstd = 1/sqrt(mean(x^2) + eps)
+ * (float64).  Codes q = clamp(rint(u * float32(127 / a)), -128, 127); the
+ * positive factor rstd multiplies all of a token's values, so it does not
+ * change the codes and is applied only in d_x.  A token with a < 2^-120 gets
+ * all-zero codes and d_x = 0.  M = 0 is a no-op.
+ */
+int bitnet_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
+                     int8_t* xq, float* x_scale, int32_t* x_qsum, void* stream);
+
+/*
+ * H-BitLinear activations: RMSNorm + Walsh-Hadamard transform + per-token
+ * absmax int4 quantisation ([V2] "방법론").
+ *
+ * Same arguments as bitnet_quant_act; K must be a power of two in
+ * [256, 32768].  Per token: u = x * gain, t = H u with H the unnormalised
+ * Sylvester Hadamard matrix (float32 butterflies, stage distance ascending
+ * 1, 2, 4, ...), a = max |t|, codes q = clamp(rint(t * float32(7 / a)), -8, 7)
+ * stored one per int8, d_x = a * rstd / (7 sqrt(K)) (the transform's 1/sqrt(K)
+ * normalisation is folded in here).  Weights for this path are packed with
+ * hadamard = 1.
+ */
+int bitnet_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
+                              int64_t K, int8_t* xq, float* x_scale, int32_t* x_qsum,
+                              void* stream);
+
+/*
+ * Ternary integer contraction + dequantisation ([FT] "계산 패러다임",
+ * "추론 최적화 및 커스텀 커널", "양자화 메커니즘" rescale; [QP] dequantise).
+ *
+ *   xq, x_scale, x_qsum  in  outputs of bitnet_quant_act or
+ *                            bitnet_hadamard_quant_act ([M][K], [M], [M]);
+ *                            xq 16-byte aligned.
+ *   packed, w_scale      in  outputs of bitnet_pack_weights ([N][K/4], [2]);
+ *                            packed 16-byte aligned.
+ *   y                    out float32 [M][N]: y = acc * d_x[m] * d_w.
+ *   acc                  out int32 [M][N] accumulators, or NULL to skip.
+ * acc[m][n] = sum_k q_x[m][k] * q_w[n][k], exact in int32.  y and acc need
+ * 4-byte alignment.  M = 0 or N = 0 is a no-op.  Token counts M <= 4 run a
+ * bandwidth-bound GEMV; larger M run an int8 matrix-core GEMM.
+ */
+int bitnet_linear_forward(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
+                          const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc, void* stream);
+
+/* Static text for a status code. */
+const char* bitnet_status_string(int status);
+
+/* Thread-local detail of the last non-OK status on this thread ("" if none). */
+const char* bitnet_last_error(void);
+
+/* BITNET_ABI_VERSION of the loaded library. */
+int bitnet_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITNET_H */

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every symbol include/bitnet.h declares, and
+rejects bad arguments on the host before any HIP call (CPU only: nothing here
+launches work or touches device memory; the pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_gemm_ternary_amd as bt
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "bitnet.h")
+
+A16 = 0x10000      # 16-byte-aligned stand-in addresses, never dereferenced
+A4 = 0x10004
+BAD = 0x10001
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitnet_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bt.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"bitnet_pack_weights", "bitnet_quant_act", "bitnet_hadamard_quant_act",
+            "bitnet_linear_forward"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_header_enum_matches_binding():
+    text = open(HEADER).read()
+    enum = dict((name, int(v)) for name, v in re.findall(r"(BITNET_[A-Z_]+)\s*=\s*(\d+)", text))
+    assert {v: k for k, v in enum.items()} == bt.STATUS
+
+
+def test_version_and_status_strings(L):
+    assert L.bitnet_version() == 1
+    for s in range(8):
+        assert L.bitnet_status_string(s)
+    assert L.bitnet_status_string(99) == b"unknown status"
+
+
+def _quant(L, name, x=A16, gain=None, eps=1e-5, M=4, K=256, xq=A16, sx=A4, qs=A4):
+    return getattr(L, name)(ctypes.c_void_p(x), None if gain is None else ctypes.c_void_p(gain),
+                            ctypes.c_float(eps), M, K, ctypes.c_void_p(xq), ctypes.c_void_p(sx),
+                            ctypes.c_void_p(qs), None)
+
+
+@pytest.mark.parametrize("name", ["bitnet_quant_act", "bitnet_hadamard_quant_act"])
+def test_quant_argument_errors(L, name):
+    assert _quant(L, name, M=-1) == 2
+    for K in (0, 32, 100, 65600):
+        assert _quant(L, name, K=K) == 2
+    assert _quant(L, name, eps=-1.0) == 7
+    assert _quant(L, name, eps=float("nan")) == 7
+    assert _quant(L, name, x=0) == 1
+    assert _quant(L, name, qs=0) == 1
+    assert _quant(L, name, x=BAD) == 4
+    assert _quant(L, name, xq=A4) == 4
+    assert _quant(L, name, gain=A4) == 4
+    assert _quant(L, name, M=0, x=0) == 0     # empty batch: no-op, nothing dereferenced
+    assert b"must" in L.bitnet_last_error() or b"out of range" in L.bitnet_last_error()
+
+
+def test_hadamard_needs_power_of_two(L):
+    assert _quant(L, "bitnet_hadamard_quant_act", K=192) == 3
+    assert _quant(L, "bitnet_hadamard_quant_act", K=128) == 3
+    assert _quant(L, "bitnet_hadamard_quant_act", K=65536) == 3
+    assert b"power of two" in L.bitnet_last_error()
+
+
+def _pack(L, W=A16, N=8, K=256, had=0, packed=A16, ws=A4, work=A16, work_bytes=1 << 20):
+    return L.bitnet_pack_weights(ctypes.c_void_p(W), N, K, had, ctypes.c_void_p(packed),
+                                 ctypes.c_void_p(ws), ctypes.c_void_p(work), work_bytes, None)
+
+
+def test_pack_argument_errors(L):
+    assert _pack(L, N=0) == 2
+    assert _pack(L, K=100) == 2
+    assert _pack(L, had=2) == 7
+    assert _pack(L, had=1, K=192) == 3
+    assert _pack(L, W=0) == 1
+    assert _pack(L, work=0) == 1
+    assert _pack(L, W=BAD) == 4
+    assert _pack(L, work_bytes=8) == 5
+    assert b"needed" in L.bitnet_last_error()
+
+
+def test_pack_workspace_size(L):
+    assert L.bitnet_pack_weights_workspace_bytes(100, 256, 0) == 1024      # 800 B of sums, padded
+    assert L.bitnet_pack_weights_workspace_bytes(100, 256, 1) == 1024 + 100 * 256 * 4
+    assert L.bitnet_pack_weights_workspace_bytes(0, 256, 0) == 0
+
+
+def _fwd(L, xq=A16, sx=A4, qs=A4, P=A16, ws=A4, M=2, N=8, K=256, y=A4, acc=None):
+    return L.bitnet_linear_forward(ctypes.c_void_p(xq), ctypes.c_void_p(sx), ctypes.c_void_p(qs),
+                                   ctypes.c_void_p(P), ctypes.c_void_p(ws), M, N, K,
+                                   ctypes.c_void_p(y), None if acc is None else ctypes.c_void_p(acc),
+                                   None)
+
+
+def test_forward_argument_errors(L):
+    assert _fwd(L, M=-1) == 2
+    assert _fwd(L, N=-5) == 2
+    assert _fwd(L, K=96) == 2
+    assert _fwd(L, y=0) == 1
+    assert _fwd(L, P=0) == 1
+    assert _fwd(L, xq=A4) == 4
+    assert _fwd(L, P=BAD) == 4
+    assert _fwd(L, y=BAD) == 4
+    assert _fwd(L, acc=BAD) == 4
+    assert _fwd(L, M=0, xq=0, y=0) == 0       # empty: no-op
+    assert _fwd(L, N=0, xq=0, y=0) == 0
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError):
+        bt.quant_act(torch.zeros((2, 64), dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        bt.quant_act(torch.zeros((2, 64), dtype=torch.float32))

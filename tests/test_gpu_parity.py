@@ -1,0 +1,270 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bar: packed bytes, codes, code sums and int32 accumulators bit-exact; float32
+scales and outputs within 1e-5 relative (outputs with acc == 0 exactly 0); on
+the Hadamard path at most 0.01% of codes may differ, by one, at rounding ties.
+Full-size workloads (the benchmark's shapes and launch configuration) are
+checked on sampled outputs the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import bit_gemm_ternary_amd as bt
+from bit_gemm_ternary_amd import synth
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need the MI355X"
+    bt.lib()
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def bf16_to_dev(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close_rel(got, want, rtol=RTOL):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    err = np.abs(got - want)
+    bad = err > rtol * np.abs(want)
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} values off by more than {rtol} relative; "
+                           f"first at {np.argwhere(bad)[0]}: got {got[bad][0]} want {want[bad][0]}")
+
+
+# ---------------------------------------------------------------------------
+# Weight quantisation and packing.
+# ---------------------------------------------------------------------------
+
+PACK_CASES = [
+    (512, 256, False),       # tiny BitLinear
+    (4096, 4096, False),     # decode q/o projection
+    (11008, 4096, False),    # decode up projection (N = 11008)
+    (4096, 11008, False),    # decode down projection (K = 11008)
+    (1, 64, False),          # smallest
+    (37, 192, False),        # ragged rows, K not a power of two
+    (300, 4096, True),       # H-BitLinear weights
+    (4096, 16384, True),     # H-BitLinear down projection
+    (33, 256, True),
+    (5, 32768, True),        # largest Hadamard
+]
+
+
+@pytest.mark.parametrize("N,K,hadamard", PACK_CASES)
+def test_pack_weights(orc, dev, N, K, hadamard):
+    W = synth.weights(N, K, seed=100 + N % 97 + K % 89)
+    want_packed, want_dw, want_sw, _ = orc.pack_weights(W, hadamard=hadamard)
+    packed, w_scale = bt.pack_weights(to_dev(W, dev), hadamard=hadamard)
+    got = host(packed)
+    mism = np.count_nonzero(got != want_packed)
+    assert mism == 0, f"{mism} packed bytes differ"
+    ws = host(w_scale)
+    assert ws[1] == want_sw, (ws[1], want_sw)
+    assert ws[0] == want_dw, (ws[0], want_dw)
+
+
+def test_pack_all_zero_and_ternary_inputs(orc, dev):
+    packed, w_scale = bt.pack_weights(torch.zeros((9, 128), dtype=torch.float32, device=dev))
+    assert (host(packed) == 0x55).all() and (host(w_scale) == 0).all()
+    q = np.random.default_rng(7).integers(-1, 2, size=(64, 256)).astype(np.float32)
+    want, _, _, _ = orc.pack_weights(q)
+    got, _ = bt.pack_weights(to_dev(q, dev))
+    np.testing.assert_array_equal(host(got), want)
+
+
+# ---------------------------------------------------------------------------
+# Activation quantisation (int8) and Hadamard + int4.
+# ---------------------------------------------------------------------------
+
+def _activation(M, K, seed, dist="normal", frac=0.01, factor=20.0):
+    return synth.activations(M, K, seed, seed + 1, dist=dist, outlier_frac=frac, outlier_factor=factor)
+
+
+QUANT_CASES = [
+    (4, 256, False), (1, 4096, False), (1, 11008, False), (3, 14336, True), (2048, 4096, False),
+    (17, 65536, True), (5, 64, False), (33, 192, True),
+]
+
+
+@pytest.mark.parametrize("M,K,with_gain", QUANT_CASES)
+def test_quant_act(orc, dev, M, K, with_gain):
+    x = _activation(M, K, seed=200 + K % 101, frac=0.005, factor=50.0)
+    gain = (np.random.default_rng(K).uniform(0.5, 1.5, K).astype(np.float32) if with_gain else None)
+    wq, wdx, wqs = orc.quant_act(x, gain=gain, eps=1e-5)
+    q, dx, qs = bt.quant_act(bf16_to_dev(x, dev), None if gain is None else to_dev(gain, dev), 1e-5)
+    np.testing.assert_array_equal(host(q), wq)
+    np.testing.assert_array_equal(host(qs), wqs)
+    assert_close_rel(host(dx), wdx)
+
+
+def test_quant_act_zero_tiny_and_tie_tokens(orc, dev):
+    x = np.zeros((4, 256), np.float32)
+    x[1, 3] = 2.0 ** -126
+    x[2, :5] = [127.0, 2.5, 3.5, -2.5, -3.5]
+    x[3] = np.linspace(-3, 3, 256)
+    bits = synth.bf16_bits(x)
+    wq, wdx, wqs = orc.quant_act(bits)
+    q, dx, qs = bt.quant_act(bf16_to_dev(bits, dev))
+    np.testing.assert_array_equal(host(q), wq)
+    np.testing.assert_array_equal(host(qs), wqs)
+    assert_close_rel(host(dx), wdx)
+    assert host(dx)[0] == 0 and host(dx)[1] == 0
+
+
+HQ_CASES = [
+    (4, 256, False), (3, 512, True), (5, 1024, False), (7, 2048, True), (512, 4096, False),
+    (2, 8192, True), (512, 16384, False), (3, 32768, True),
+]
+
+
+@pytest.mark.parametrize("M,K,with_gain", HQ_CASES)
+def test_hadamard_quant_act(orc, dev, M, K, with_gain):
+    x = _activation(M, K, seed=300 + K % 103, dist="student_t", frac=0.0)
+    gain = (np.random.default_rng(K + 1).uniform(0.5, 1.5, K).astype(np.float32) if with_gain else None)
+    wq, wdx, wqs = orc.hadamard_quant_act(x, gain=gain, eps=1e-5)
+    q, dx, qs = bt.hadamard_quant_act(bf16_to_dev(x, dev), None if gain is None else to_dev(gain, dev))
+    q = host(q)
+    diff = np.abs(q.astype(np.int16) - wq.astype(np.int16))
+    assert diff.max() <= 1
+    assert np.count_nonzero(diff) <= 1e-4 * q.size
+    assert np.count_nonzero(diff) == 0, "same stage order should give identical codes"
+    np.testing.assert_array_equal(host(qs), wqs)
+    assert_close_rel(host(dx), wdx)
+
+
+# ---------------------------------------------------------------------------
+# Contraction + dequantisation.
+# ---------------------------------------------------------------------------
+
+def _forward_inputs(orc, M, N, K, seed, hadamard=False):
+    W = synth.weights(N, K, seed)
+    packed, d_w, _, _ = orc.pack_weights(W, hadamard=hadamard)
+    x = _activation(M, K, seed + 7, dist="student_t" if hadamard else "normal")
+    quant = orc.hadamard_quant_act if hadamard else orc.quant_act
+    xq, d_x, qsum = quant(x)
+    return packed, np.array([d_w, 0], np.float32), xq, d_x, qsum
+
+
+def _run_forward(dev, packed, w_scale, xq, d_x, qsum):
+    y, acc = bt.linear_forward(to_dev(xq, dev), to_dev(d_x, dev), to_dev(qsum, dev),
+                               to_dev(packed, dev), to_dev(w_scale, dev), return_acc=True)
+    return host(y), host(acc)
+
+
+FORWARD_FULL_CASES = [
+    # GEMV (M <= 4)
+    (1, 512, 256), (1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008), (2, 1000, 4096),
+    (3, 77, 14336), (4, 4097, 8192), (1, 1, 64), (1, 130, 32768), (2, 9, 16384),
+    # matrix-core GEMM
+    (5, 512, 256), (16, 4096, 4096), (17, 1000, 4096), (64, 1024, 4096), (100, 333, 192),
+    (128, 128, 128), (256, 1024, 4096), (300, 4099, 1024), (1, 70, 65536), (33, 65, 64),
+]
+
+
+@pytest.mark.parametrize("M,N,K", FORWARD_FULL_CASES)
+def test_linear_forward(orc, dev, M, N, K):
+    packed, w_scale, xq, d_x, qsum = _forward_inputs(orc, M, N, K, seed=400 + M + N % 113)
+    y, acc = _run_forward(dev, packed, w_scale, xq, d_x, qsum)
+    want_acc, want_y = orc.linear_forward(xq, d_x, packed, w_scale[0], K)
+    mism = np.count_nonzero(acc != want_acc)
+    assert mism == 0, f"{mism} of {acc.size} accumulators differ; first {np.argwhere(acc != want_acc)[0]}"
+    assert_close_rel(y, want_y)
+    assert (y[want_acc == 0] == 0).all()
+
+
+FORWARD_SAMPLED_CASES = [
+    (2048, 14336, 4096, False),   # prefill FFN up projection
+    (512, 4096, 4096, True),      # H-BitLinear
+    (512, 4096, 16384, True),     # H-BitLinear down projection
+    (256, 14336, 4096, False),    # Llama-3-8B block gate/up at M = 256
+    (16, 14336, 4096, False),     # ... at M = 16
+    (256, 4096, 14336, False),    # down projection at M = 256
+]
+
+
+@pytest.mark.parametrize("M,N,K,hadamard", FORWARD_SAMPLED_CASES)
+def test_linear_forward_full_size_sampled(orc, dev, M, N, K, hadamard):
+    packed, w_scale, xq, d_x, qsum = _forward_inputs(orc, M, N, K, seed=500 + M, hadamard=hadamard)
+    y, acc = _run_forward(dev, packed, w_scale, xq, d_x, qsum)
+    rng = np.random.default_rng(M + N + K)
+    rows = np.concatenate([rng.integers(0, M, 3000), np.full(N, M - 1), np.zeros(64, np.int64)])
+    cols = np.concatenate([rng.integers(0, N, 3000), np.arange(N), np.arange(N - 64, N)])
+    want = orc.int_gemm_sampled(xq, packed, K, rows, cols)
+    got = acc[rows, cols]
+    assert np.count_nonzero(got != want) == 0
+    want_y = want.astype(np.float64) * d_x[rows].astype(np.float64) * np.float64(w_scale[0])
+    assert_close_rel(y[rows, cols], want_y)
+    # properties at every output: y is the dequantised accumulator
+    assert_close_rel(y, acc.astype(np.float64) * d_x[:, None].astype(np.float64) * np.float64(w_scale[0]))
+
+
+def test_forward_determinism(orc, dev):
+    packed, w_scale, xq, d_x, qsum = _forward_inputs(orc, 64, 4096, 4096, seed=600)
+    args = [to_dev(a, dev) for a in (xq, d_x, qsum, packed, w_scale)]
+    first = None
+    for _ in range(5):
+        y, acc = bt.linear_forward(*args, return_acc=True)
+        cur = (host(y), host(acc))
+        if first is None:
+            first = cur
+        else:
+            np.testing.assert_array_equal(cur[1], first[1])
+            np.testing.assert_array_equal(cur[0], first[0])
+
+
+def test_empty_inputs(dev):
+    xq = torch.empty((0, 256), dtype=torch.int8, device=dev)
+    packed = torch.full((8, 64), 0x55, dtype=torch.uint8, device=dev)
+    ws = torch.ones(2, dtype=torch.float32, device=dev)
+    y = bt.linear_forward(xq, torch.empty(0, device=dev), torch.empty(0, dtype=torch.int32, device=dev),
+                          packed, ws)
+    assert tuple(y.shape) == (0, 8)
+    q, dx, qs = bt.quant_act(torch.empty((0, 128), dtype=torch.bfloat16, device=dev))
+    assert q.shape[0] == 0 and dx.shape[0] == 0
+    xq = torch.ones((3, 256), dtype=torch.int8, device=dev)
+    y = bt.linear_forward(xq, torch.ones(3, device=dev), torch.zeros(3, dtype=torch.int32, device=dev),
+                          torch.empty((0, 64), dtype=torch.uint8, device=dev), ws)
+    assert tuple(y.shape) == (3, 0)
+
+
+# ---------------------------------------------------------------------------
+# End to end through the GPU path only, compared with the oracle end to end.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("workload", ["tiny", "decode"])
+def test_bitlinear_end_to_end(orc, dev, workload):
+    for layer in synth.workload(workload):
+        W, x = layer.weights(), layer.activations()
+        packed, d_w, _, _ = orc.pack_weights(W)
+        xq, d_x, _ = orc.quant_act(x)
+        want_acc, want_y = orc.linear_forward(xq, d_x, packed, d_w, layer.K)
+        layer_gpu = bt.BitLinear(to_dev(W, dev))
+        y = host(layer_gpu(bf16_to_dev(x, dev)))
+        assert_close_rel(y, want_y)
+
+
+def test_hadamard_bitlinear_end_to_end(orc, dev):
+    M, N, K = 32, 256, 1024
+    W = synth.weights(N, K, 700)
+    x = _activation(M, K, 701, dist="student_t", frac=0.0)
+    packed, d_w, _, _ = orc.pack_weights(W, hadamard=True)
+    xq, d_x, _ = orc.hadamard_quant_act(x)
+    _, want_y = orc.linear_forward(xq, d_x, packed, d_w, K)
+    layer = bt.BitLinear(to_dev(W, dev), hadamard=True)
+    assert_close_rel(host(layer(bf16_to_dev(x, dev))), want_y)
