@@ -1,0 +1,400 @@
+#!/usr/bin/env python3
+"""BitLinear forward benchmark on one MI355X.
+
+Headline (one JSON line on stdout): decode GEMV weight GB/s.  A step is one
+W1.58A8 decode forward (M = 1) through the three Llama-7B-shaped projections
+(K, N) = (4096, 4096), (4096, 11008), (11008, 4096): per projection, RMSNorm +
+int8 quantisation of the bf16 token fused into the ternary GEMV with its
+dequantisation epilogue (bitnet_bitlinear_forward, one kernel).  Inputs are
+resident in HBM; the packed weights rotate over enough distinct copies
+(> 1 GiB) that the 256 MB Infinity Cache cannot serve them, so every step
+streams its weights from HBM.  Steps are replayed from HIP graphs (one graph per
+rotation copy and one per full rotation), so the timed region measures the GPU,
+not Python launch overhead.
+
+  value            packed weight bytes per step / step time (GB/s)
+  roofline         the fused decode kernel alone: algorithmic bytes (packed
+                   weights, bf16 activations, codes and outputs) per launch /
+                   average kernel duration, from HIP events that the kernel's
+                   own dispatch stamps (hipExtLaunchKernelGGL), on its stream
+  prefill          W1.58A8 prefill M=2048, K=4096, N=14336: int8 TOPS of the
+                   matrix-core GEMM against the dense int8 peak
+  hadamard         H-BitLinear M=512: FWHT + int4 quantisation GB/s and GEMM TOPS
+  cpu_baseline     the CPU oracle on this host running the same decode step
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix-core peak, 5.0 POP/s
+ROTATE_BYTES = 1 << 30      # > 4 x the 256 MB Infinity Cache
+METRIC = "BitLinear decode GEMV weight GB/s (%HBM peak); prefill int8 TOPS (%MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--prefill-iters", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall time budget of the CPU-oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the prefill / H-BitLinear legs")
+    ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of from graphs")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the process's HIP runtime (the one torch and the library share)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.events.append(ev.value)
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+        self.events = []
+
+
+class DecodeLayer:
+    """Device buffers of one M=1 projection with R rotating copies of its packed weights."""
+
+    def __init__(self, layer, copies, dev, bt, torch):
+        self.layer = layer
+        M, K, N = layer.M, layer.K, layer.N
+        W = torch.from_numpy(layer.weights()).to(dev)
+        packed, self.w_scale = bt.pack_weights(W)
+        del W
+        self.packed = [packed] + [packed.clone() for _ in range(copies - 1)]
+        x = layer.activations()
+        self.x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.codes = (torch.empty((M, K), dtype=torch.int8, device=dev),
+                      torch.empty(M, dtype=torch.float32, device=dev),
+                      torch.empty(M, dtype=torch.int32, device=dev))
+        self.y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        self.weight_bytes = N * K // 4
+        # Fused kernel algorithmic bytes: packed weights + bf16 token + w_scale in;
+        # codes, scale, sum and float32 outputs out.
+        self.kernel_bytes = self.weight_bytes + 2 * M * K + 8 + M * K + 8 * M + 4 * M * N
+
+    def forward(self, bt, r):
+        bt.bitlinear_forward(self.x, self.packed[r], self.w_scale, None, 1e-5, out=self.y,
+                             codes=self.codes)
+
+
+def decode_bench(args, dev, bt, torch, synth):
+    layers_spec = synth.workload("decode")
+    step_bytes = sum(l.N * l.K // 4 for l in layers_spec)
+    copies = max(1, math.ceil(ROTATE_BYTES / step_bytes))
+    layers = [DecodeLayer(l, copies, dev, bt, torch) for l in layers_spec]
+    torch.cuda.synchronize()
+    log(f"decode: {len(layers)} projections, {step_bytes / 1e6:.2f} MB packed per step, "
+        f"{copies} rotating copies ({copies * step_bytes / 2**30:.2f} GiB)")
+
+    def step(r):
+        for L in layers:
+            L.forward(bt, r)
+
+    # Warm-up (also loads the kernels).
+    for s in range(args.warmup):
+        step(s % copies)
+    torch.cuda.synchronize()
+
+    graphs, cycle = None, None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        with torch.cuda.stream(side):
+            for r in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(r)
+                graphs.append(g)
+            cycle = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(cycle, stream=side):
+                for r in range(copies):
+                    step(r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for g in graphs[: min(len(graphs), 8)]:
+            g.replay()
+        cycle.replay()
+        torch.cuda.synchronize()
+
+    def run_steps(n):
+        if graphs is None:
+            for s in range(n):
+                step(s % copies)
+            return
+        full, rest = divmod(n, copies)
+        for _ in range(full):
+            cycle.replay()
+        for s in range(rest):
+            graphs[s].replay()
+
+    # Timed region: exactly `steps` steps between two synchronisations.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    run_steps(args.steps)
+    end.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    ms_per_step = gpu_ms / args.steps
+
+    # Per-kernel durations: the same steps again, launched eagerly with the
+    # kernel-timing hook armed before every launch, so each event pair is
+    # stamped by that kernel's own dispatch on the stream it runs on.
+    hev = HipEvents()
+    n_instr = min(args.steps, 1000)
+    pairs = [[(hev.create(), hev.create()) for _ in layers] for _ in range(n_instr)]
+    torch.cuda.synchronize()
+    for s in range(n_instr):
+        r = s % copies
+        for i, L in enumerate(layers):
+            bt.set_kernel_events(*pairs[s][i])
+            L.forward(bt, r)
+    torch.cuda.synchronize()
+    per_layer_us = [float(np.mean([hev.elapsed_ms(*pairs[s][i]) for s in range(n_instr)])) * 1e3
+                    for i in range(len(layers))]
+    hev.close()
+    kernel_bytes = sum(L.kernel_bytes for L in layers)
+    kernel_us = sum(per_layer_us)
+    per_layer = [{"K": L.layer.K, "N": L.layer.N, "packed_bytes": L.weight_bytes,
+                  "kernel_bytes": L.kernel_bytes, "avg_us": round(us, 3),
+                  "GB_s": round(L.kernel_bytes / us / 1e3, 1)}
+                 for L, us in zip(layers, per_layer_us)]
+    return {
+        "step_bytes": step_bytes, "copies": copies, "ms_per_step": ms_per_step,
+        "wall_s": wall_s, "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "kernel_bytes": kernel_bytes, "kernel_us": kernel_us, "per_layer": per_layer,
+        "instrumented_steps": n_instr, "layers": layers,
+    }
+
+
+def time_launches(fn, iters, bt):
+    """Average kernel duration (us) of fn() over `iters` launches, from event pairs
+    stamped by each launch's own dispatch (the library's kernel-timing hook)."""
+    import torch
+
+    hev = HipEvents()
+    pairs = [(hev.create(), hev.create()) for _ in range(iters)]
+    for a, b in pairs:
+        bt.set_kernel_events(a, b)
+        fn()
+    torch.cuda.synchronize()
+    us = float(np.mean([hev.elapsed_ms(a, b) for a, b in pairs])) * 1e3
+    hev.close()
+    return us
+
+
+def prefill_bench(args, dev, bt, torch, synth):
+    layer = synth.workload("prefill")[0]
+    M, K, N = layer.M, layer.K, layer.N
+    packed, w_scale = bt.pack_weights(torch.from_numpy(layer.weights()).to(dev))
+    x = torch.from_numpy(layer.activations().view(np.int16)).to(dev).view(torch.bfloat16)
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    xs = torch.empty(M, dtype=torch.float32, device=dev)
+    qs = torch.empty(M, dtype=torch.int32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    quant = lambda: bt.quant_act(x, None, 1e-5, out=(xq, xs, qs))
+    gemm = lambda: bt.linear_forward(xq, xs, qs, packed, w_scale, out=y)
+    for _ in range(5):
+        quant()
+        gemm()
+    torch.cuda.synchronize()
+    quant_us = time_launches(quant, args.prefill_iters, bt)
+    gemm_us = time_launches(gemm, args.prefill_iters, bt)
+    tops = 2.0 * M * N * K / (gemm_us * 1e-6) / 1e12
+    quant_bytes = M * K * 2 + M * K + 8 * M
+    return {
+        "workload": f"W1.58A8 prefill M={M} K={K} N={N} (FFN up)",
+        "gemm_us": round(gemm_us, 2), "TOPS": round(tops, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS,
+                     "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4)},
+        "quant_us": round(quant_us, 2), "quant_GB_s": round(quant_bytes / quant_us / 1e3, 1),
+        "step_ms": round((gemm_us + quant_us) / 1e3, 4),
+    }
+
+
+def hadamard_bench(args, dev, bt, torch, synth):
+    out = []
+    for layer in synth.workload("hadamard"):
+        M, K, N = layer.M, layer.K, layer.N
+        packed, w_scale = bt.pack_weights(torch.from_numpy(layer.weights()).to(dev), hadamard=True)
+        x = torch.from_numpy(layer.activations().view(np.int16)).to(dev).view(torch.bfloat16)
+        xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        xs = torch.empty(M, dtype=torch.float32, device=dev)
+        qs = torch.empty(M, dtype=torch.int32, device=dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        hq = lambda: bt.hadamard_quant_act(x, None, 1e-5, out=(xq, xs, qs))
+        gemm = lambda: bt.linear_forward(xq, xs, qs, packed, w_scale, out=y)
+        for _ in range(5):
+            hq()
+            gemm()
+        torch.cuda.synchronize()
+        hq_us = time_launches(hq, args.prefill_iters, bt)
+        gemm_us = time_launches(gemm, args.prefill_iters, bt)
+        hq_bytes = M * K * 2 + M * K + 8 * M
+        out.append({"M": M, "K": K, "N": N,
+                    "fwht_int4_us": round(hq_us, 2),
+                    "fwht_int4_GB_s": round(hq_bytes / hq_us / 1e3, 1),
+                    "fwht_int4_frac_hbm": round(hq_bytes / hq_us / 1e3 / HBM_PEAK_GBS, 4),
+                    "gemm_us": round(gemm_us, 2),
+                    "gemm_TOPS": round(2.0 * M * N * K / (gemm_us * 1e-6) / 1e12, 1)})
+    return out
+
+
+def cpu_baseline(args, synth):
+    import oracle
+
+    orc = oracle.default()
+    layers = []
+    for l in synth.workload("decode"):
+        packed, d_w, _, _ = orc.pack_weights(l.weights())
+        layers.append((l, packed, d_w, l.activations()))
+    step_bytes = sum(l.N * l.K // 4 for l, *_ in layers)
+
+    def step():
+        for l, packed, d_w, x in layers:
+            xq, d_x, _ = orc.quant_act(x)
+            orc.linear_forward(xq, d_x, packed, d_w, l.K)
+
+    step()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds:
+            break
+    return {"value": round(step_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} decode steps (int8 quant + int32 contraction + dequant of the three "
+                      f"M=1 projections) in {el:.1f} s on {os.cpu_count()} host CPUs"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this BitLinear build has no multi-GPU path "
+              "(the workload would shard by tokens or output features; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_gemm_ternary_amd as bt
+    from bit_gemm_ternary_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs the GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bt.lib()
+
+    dec = decode_bench(args, dev, bt, torch, synth)
+    log(f"decode: {dec['ms_per_step'] * 1e3:.2f} us/step, {dec['value']:.1f} GB/s; "
+        f"GEMV kernels {dec['per_layer']}")
+    del dec["layers"]
+    torch.cuda.empty_cache()
+
+    secondary = {}
+    if not args.no_secondary:
+        secondary["prefill"] = prefill_bench(args, dev, bt, torch, synth)
+        log(f"prefill: {secondary['prefill']}")
+        torch.cuda.empty_cache()
+        secondary["hadamard"] = hadamard_bench(args, dev, bt, torch, synth)
+        log(f"hadamard: {secondary['hadamard']}")
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
+
+    achieved = dec["kernel_bytes"] / dec["kernel_us"] / 1e3
+    line = {
+        "metric": METRIC,
+        "value": round(dec["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode GEMV W1.58A8, M=1, (K,N) in (4096,4096), (4096,11008), (11008,4096); "
+                        "bf16 N(0,1) tokens with 1% outlier channels x20; N(0,0.02) weights, absmean "
+                        "ternary, 2 bits/weight",
+            "step": "per projection: RMSNorm + int8 quant fused into the ternary GEMV + dequant "
+                    "(3 kernels per step)",
+            "packed_bytes_per_step": dec["step_bytes"],
+            "weight_rotation_copies": dec["copies"],
+            "launch": "eager" if args.eager else "hip graphs",
+            "frac_hbm_peak": round(dec["value"] / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "fused_decode_kernel (3 launches per step)",
+            "bytes_per_step": dec["kernel_bytes"],
+            "us_per_step": round(dec["kernel_us"], 3),
+            "per_launch": dec["per_layer"],
+        },
+        "cpu_baseline": cpu,
+    }
+    line.update(secondary)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

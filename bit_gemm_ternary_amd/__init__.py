@@ -18,8 +18,9 @@ import os
 
 __all__ = [
     "BitnetError", "lib", "library_path", "pack_weights", "pack_weights_workspace_bytes",
-    "quant_act", "hadamard_quant_act", "linear_forward", "bitlinear", "BitLinear",
-    "STATUS",
+    "quant_act", "hadamard_quant_act", "linear_forward", "bitlinear", "bitlinear_forward",
+    "BitLinear",
+    "STATUS", "set_kernel_events",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -65,12 +66,16 @@ def lib() -> ctypes.CDLL:
         fn.restype = i32
     L.bitnet_linear_forward.argtypes = [p, p, p, p, p, i64, i64, i64, p, p, p]
     L.bitnet_linear_forward.restype = i32
+    L.bitnet_bitlinear_forward.argtypes = [p, p, f32, p, p, i64, i64, i64, p, p, p, p, p, p]
+    L.bitnet_bitlinear_forward.restype = i32
     L.bitnet_status_string.argtypes = [i32]
     L.bitnet_status_string.restype = ctypes.c_char_p
     L.bitnet_last_error.argtypes = []
     L.bitnet_last_error.restype = ctypes.c_char_p
     L.bitnet_version.argtypes = []
     L.bitnet_version.restype = i32
+    L.bitnet_set_kernel_events.argtypes = [p, p]
+    L.bitnet_set_kernel_events.restype = i32
     _LIB = L
     return L
 
@@ -108,6 +113,11 @@ def _require(t, name, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def set_kernel_events(start_event, stop_event) -> None:
+    """Arm two raw hipEvent_t handles (ints) to time the next kernel a call on this thread launches."""
+    lib().bitnet_set_kernel_events(ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event))
+
+
 def pack_weights_workspace_bytes(N: int, K: int, hadamard: bool = False) -> int:
     return int(lib().bitnet_pack_weights_workspace_bytes(N, K, int(bool(hadamard))))
 
@@ -127,7 +137,7 @@ def pack_weights(W, hadamard: bool = False):
     return packed, w_scale
 
 
-def _quant(name, x, gain, eps):
+def _quant(name, x, gain, eps, out):
     torch = _torch()
     _require(x, "x", torch.bfloat16, 2)
     M, K = x.shape
@@ -135,26 +145,41 @@ def _quant(name, x, gain, eps):
         _require(gain, "gain", torch.float32, 1)
         if gain.shape[0] != K:
             raise ValueError(f"gain has {gain.shape[0]} entries, x has K={K}")
-    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
-    x_qsum = torch.empty(M, dtype=torch.int32, device=x.device)
+    if out is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
+        x_qsum = torch.empty(M, dtype=torch.int32, device=x.device)
+    else:
+        xq, x_scale, x_qsum = out
+        _require(xq, "xq", torch.int8, 2)
+        _require(x_scale, "x_scale", torch.float32, 1)
+        _require(x_qsum, "x_qsum", torch.int32, 1)
+        if tuple(xq.shape) != (M, K) or x_scale.shape[0] != M or x_qsum.shape[0] != M:
+            raise ValueError("out tensors do not match x")
     _check(getattr(lib(), name)(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K, _ptr(xq),
                                 _ptr(x_scale), _ptr(x_qsum), _stream(x.device)))
     return xq, x_scale, x_qsum
 
 
-def quant_act(x, gain=None, eps: float = 1e-5):
-    """bf16 [M][K] -> (int8 codes [M][K], d_x float32 [M], code sums int32 [M])."""
-    return _quant("bitnet_quant_act", x, gain, eps)
+def quant_act(x, gain=None, eps: float = 1e-5, out=None):
+    """bf16 [M][K] -> (int8 codes [M][K], d_x float32 [M], code sums int32 [M]).
+
+    ``out`` may hold preallocated (codes, d_x, sums) tensors to write into.
+    """
+    return _quant("bitnet_quant_act", x, gain, eps, out)
 
 
-def hadamard_quant_act(x, gain=None, eps: float = 1e-5):
+def hadamard_quant_act(x, gain=None, eps: float = 1e-5, out=None):
     """H-BitLinear: bf16 [M][K] (K = 2^p) -> (int4 codes as int8 [M][K], d_x, code sums)."""
-    return _quant("bitnet_hadamard_quant_act", x, gain, eps)
+    return _quant("bitnet_hadamard_quant_act", x, gain, eps, out)
 
 
-def linear_forward(xq, x_scale, x_qsum, packed, w_scale, return_acc: bool = False):
-    """Ternary contraction + dequant: y float32 [M][N] (and int32 accumulators if asked)."""
+def linear_forward(xq, x_scale, x_qsum, packed, w_scale, return_acc: bool = False, out=None,
+                   acc_out=None):
+    """Ternary contraction + dequant: y float32 [M][N] (and int32 accumulators if asked).
+
+    ``out`` / ``acc_out`` may be preallocated [M][N] float32 / int32 tensors.
+    """
     torch = _torch()
     _require(xq, "xq", torch.int8, 2)
     _require(x_scale, "x_scale", torch.float32, 1)
@@ -167,18 +192,75 @@ def linear_forward(xq, x_scale, x_qsum, packed, w_scale, return_acc: bool = Fals
         raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}] for K={K}")
     if x_scale.shape[0] != M or x_qsum.shape[0] != M or w_scale.shape[0] < 1:
         raise ValueError("x_scale / x_qsum must have M entries and w_scale at least one")
-    y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
-    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if return_acc else None
+    if out is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    else:
+        _require(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be [{M}][{N}]")
+        y = out
+    acc = acc_out
+    if acc is not None:
+        _require(acc, "acc_out", torch.int32, 2)
+        if tuple(acc.shape) != (M, N):
+            raise ValueError(f"acc_out must be [{M}][{N}]")
+    elif return_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
     _check(lib().bitnet_linear_forward(_ptr(xq), _ptr(x_scale), _ptr(x_qsum), _ptr(packed),
                                        _ptr(w_scale), M, N, K, _ptr(y), _ptr(acc),
                                        _stream(xq.device)))
-    return (y, acc) if return_acc else y
+    return (y, acc) if (return_acc or acc_out is not None) else y
+
+
+def bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5, out=None, codes=None,
+                      acc_out=None):
+    """Fused int8 BitLinear forward (bitnet_bitlinear_forward): bf16 [M][K] -> y float32 [M][N].
+
+    ``codes`` may hold preallocated (xq, x_scale, x_qsum) for the intermediate
+    codes (they are written); ``out`` / ``acc_out`` preallocated outputs.
+    Returns y, or (y, acc) when ``acc_out`` is given.
+    """
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    _require(packed, "packed", torch.uint8, 2)
+    _require(w_scale, "w_scale", torch.float32, 1)
+    M, K = x.shape
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}] for K={K}")
+    if gain is not None:
+        _require(gain, "gain", torch.float32, 1)
+    if codes is None:
+        codes = (torch.empty((M, K), dtype=torch.int8, device=x.device),
+                 torch.empty(M, dtype=torch.float32, device=x.device),
+                 torch.empty(M, dtype=torch.int32, device=x.device))
+    xq, x_scale, x_qsum = codes
+    _require(xq, "xq", torch.int8, 2)
+    _require(x_scale, "x_scale", torch.float32, 1)
+    _require(x_qsum, "x_qsum", torch.int32, 1)
+    if tuple(xq.shape) != (M, K) or x_scale.shape[0] != M or x_qsum.shape[0] != M:
+        raise ValueError("codes tensors do not match x")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _require(out, "out", torch.float32, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}][{N}]")
+    if acc_out is not None:
+        _require(acc_out, "acc_out", torch.int32, 2)
+        if tuple(acc_out.shape) != (M, N):
+            raise ValueError(f"acc_out must be [{M}][{N}]")
+    _check(lib().bitnet_bitlinear_forward(_ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(packed),
+                                          _ptr(w_scale), M, N, K, _ptr(xq), _ptr(x_scale),
+                                          _ptr(x_qsum), _ptr(out), _ptr(acc_out),
+                                          _stream(x.device)))
+    return (out, acc_out) if acc_out is not None else out
 
 
 def bitlinear(x, packed, w_scale, hadamard: bool = False, gain=None, eps: float = 1e-5):
     """One BitLinear forward: quantise bf16 activations, contract, dequantise."""
-    q = hadamard_quant_act if hadamard else quant_act
-    xq, x_scale, x_qsum = q(x, gain, eps)
+    if not hadamard:
+        return bitlinear_forward(x, packed, w_scale, gain, eps)
+    xq, x_scale, x_qsum = hadamard_quant_act(x, gain, eps)
     return linear_forward(xq, x_scale, x_qsum, packed, w_scale)
 
 

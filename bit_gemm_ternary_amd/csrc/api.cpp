@@ -14,6 +14,13 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+// Disarms the timing events when an entry point returns, launched or not.
+struct DisarmEvents {
+    ~DisarmEvents() { g_ev_start = g_ev_stop = nullptr; }
+};
 
 int fail(int status, const char* fmt, ...) {
     va_list ap;
@@ -75,7 +82,21 @@ int validate_quant(const uint16_t* x, const float* gain, float eps, int64_t M, i
 
 }  // namespace
 
+namespace bitnet {
+void take_kernel_events(hipEvent_t* start, hipEvent_t* stop) {
+    *start = g_ev_start;
+    *stop = g_ev_stop;
+    g_ev_start = g_ev_stop = nullptr;
+}
+}  // namespace bitnet
+
 extern "C" {
+
+int bitnet_set_kernel_events(void* start_event, void* stop_event) {
+    g_ev_start = (hipEvent_t)start_event;
+    g_ev_stop = (hipEvent_t)stop_event;
+    return BITNET_OK;
+}
 
 size_t bitnet_pack_weights_workspace_bytes(int64_t N, int64_t K, int hadamard) {
     if (N < 1 || N > kMaxRows || K < kMinK || K > kMaxK) return 0;
@@ -84,6 +105,7 @@ size_t bitnet_pack_weights_workspace_bytes(int64_t N, int64_t K, int hadamard) {
 
 int bitnet_pack_weights(const float* W, int64_t N, int64_t K, int hadamard, uint8_t* packed,
                         float* w_scale, void* workspace, size_t workspace_bytes, void* stream) {
+    DisarmEvents disarm;
     const char* fn = "bitnet_pack_weights";
     if (N < 1 || N > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
     int s = check_k(K, fn);
@@ -106,6 +128,7 @@ int bitnet_pack_weights(const float* W, int64_t N, int64_t K, int hadamard, uint
 
 int bitnet_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
                      int8_t* xq, float* x_scale, int32_t* x_qsum, void* stream) {
+    DisarmEvents disarm;
     const char* fn = "bitnet_quant_act";
     int s = validate_quant(x, gain, eps, M, K, xq, x_scale, x_qsum, false, fn);
     if (s != BITNET_OK || M == 0) return s;
@@ -117,6 +140,7 @@ int bitnet_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
 int bitnet_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
                               int64_t K, int8_t* xq, float* x_scale, int32_t* x_qsum,
                               void* stream) {
+    DisarmEvents disarm;
     const char* fn = "bitnet_hadamard_quant_act";
     int s = validate_quant(x, gain, eps, M, K, xq, x_scale, x_qsum, true, fn);
     if (s != BITNET_OK || M == 0) return s;
@@ -128,6 +152,7 @@ int bitnet_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, i
 int bitnet_linear_forward(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                           const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                           int64_t K, float* y, int32_t* acc, void* stream) {
+    DisarmEvents disarm;
     const char* fn = "bitnet_linear_forward";
     if (M < 0 || M > kMaxRows || N < 0 || N > kMaxRows)
         return fail(BITNET_ERR_SHAPE, "%s: M=%lld or N=%lld out of range", fn, (long long)M, (long long)N);
@@ -145,6 +170,33 @@ int bitnet_linear_forward(const int8_t* xq, const float* x_scale, const int32_t*
     hipError_t e = bitnet::gemv_supported(M, K)
                        ? bitnet::launch_gemv(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, st)
                        : bitnet::launch_gemm(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, st);
+    return hip_status(e, fn);
+}
+
+int bitnet_bitlinear_forward(const uint16_t* x, const float* gain, float eps,
+                             const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, int8_t* xq, float* x_scale, int32_t* x_qsum, float* y,
+                             int32_t* acc, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_bitlinear_forward";
+    int s = validate_quant(x, gain, eps, M, K, xq, x_scale, x_qsum, false, fn);
+    if (s != BITNET_OK) return s;
+    if (N < 0 || N > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+    if (M == 0) return BITNET_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (N == 0)
+        return hip_status(bitnet::launch_quant_act(x, gain, eps, M, K, xq, x_scale, x_qsum, st), fn);
+    if (!packed || !w_scale || !y) return fail(BITNET_ERR_NULL, "%s: packed, w_scale and y must not be NULL", fn);
+    if (!aligned(packed, 16)) return fail(BITNET_ERR_ALIGN, "%s: packed must be 16-byte aligned", fn);
+    if (!aligned(w_scale, 4) || !aligned(y, 4) || (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "%s: w_scale, y and acc must be 4-byte aligned", fn);
+    if (bitnet::gemv_supported(M, K))
+        return hip_status(bitnet::launch_fused_decode(x, gain, eps, packed, w_scale, M, N, K, y, xq,
+                                                      x_scale, x_qsum, acc, st),
+                          fn);
+    hipError_t e = bitnet::launch_quant_act(x, gain, eps, M, K, xq, x_scale, x_qsum, st);
+    if (e == hipSuccess)
+        e = bitnet::launch_gemm(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, st);
     return hip_status(e, fn);
 }
 

@@ -176,9 +176,8 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_q
                       const uint8_t* packed, const float* w_scale, int64_t M, int64_t N, int64_t K,
                       float* y, int32_t* acc, hipStream_t stream) {
     const int64_t tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
-    hipLaunchKernelGGL(gemm_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, stream, xq, packed, x_scale, x_qsum,
+    return launch_kernel(gemm_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, stream, xq, packed, x_scale, x_qsum,
                        w_scale, (int)M, (int)N, (int)K, y, acc);
-    return hipGetLastError();
 }
 
 using CfgLarge = GemmCfg<128, 128, 2, 2, 128>;   // wave tile 64 x 64

@@ -226,17 +226,15 @@ template <int P>
 hipError_t launch_hq(const uint16_t* x, const float* gain, float eps, int64_t M, double sqrt_k,
                      int8_t* xq, float* x_scale, int32_t* x_qsum, hipStream_t stream) {
     constexpr int E = elems_per_thread<P>();
-    hipLaunchKernelGGL((hadamard_quant_kernel<P, E>), dim3((unsigned)M), dim3(Fwht<P, E>::B), 0,
+    return launch_kernel((hadamard_quant_kernel<P, E>), dim3((unsigned)M), dim3(Fwht<P, E>::B), 0,
                        stream, x, gain, eps, sqrt_k, xq, x_scale, x_qsum);
-    return hipGetLastError();
 }
 
 template <int P>
 hipError_t launch_rows(const float* src, float* dst, int64_t N, hipStream_t stream) {
     constexpr int E = elems_per_thread<P>();
-    hipLaunchKernelGGL((fwht_rows_kernel<P, E>), dim3((unsigned)N), dim3(Fwht<P, E>::B), 0, stream,
+    return launch_kernel((fwht_rows_kernel<P, E>), dim3((unsigned)N), dim3(Fwht<P, E>::B), 0, stream,
                        src, dst);
-    return hipGetLastError();
 }
 
 int log2_exact(int64_t k) {

@@ -6,11 +6,31 @@
 // the status of hipGetLastError() after its launches.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace bitnet {
+
+// Timing events armed by bitnet_set_kernel_events() for the next kernel launched
+// on this thread; returns them and disarms (both NULL when none are armed).
+void take_kernel_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Launch `kernel` on `stream`; when timing events are armed, through
+// hipExtLaunchKernelGGL so that the events are stamped by the kernel's own
+// dispatch (start and end of execution) rather than by separate markers.
+template <typename F, typename... Args>
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t stream,
+                         Args... args) {
+    hipEvent_t ev_start = nullptr, ev_stop = nullptr;
+    take_kernel_events(&ev_start, &ev_stop);
+    if (ev_start != nullptr || ev_stop != nullptr)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ev_start, ev_stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, shmem, stream, args...);
+    return hipGetLastError();
+}
 
 // --- weight quantisation / packing (pack.hip) ------------------------------
 // Workspace layout: [row sums: N doubles, padded to 256 B][rotated W: N*K floats
@@ -37,6 +57,11 @@ bool gemv_supported(int64_t M, int64_t K);
 hipError_t launch_gemv(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                        const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream);
+// Fused RMSNorm + int8 quantisation + GEMV (requires gemv_supported(M, K)).
+hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
+                               const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                               int64_t K, float* y, int8_t* xq, float* x_scale, int32_t* x_qsum,
+                               int32_t* acc, hipStream_t stream);
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                        const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream);

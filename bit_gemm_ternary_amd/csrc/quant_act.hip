@@ -124,9 +124,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
 template <int CH>
 hipError_t launch_ch(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
                      int8_t* xq, float* x_scale, int32_t* x_qsum, hipStream_t stream) {
-    hipLaunchKernelGGL(quant_act_kernel<CH>, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, x,
+    return launch_kernel(quant_act_kernel<CH>, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, x,
                        gain, eps, (int)K, xq, x_scale, x_qsum);
-    return hipGetLastError();
 }
 
 }  // namespace

@@ -167,6 +167,37 @@ int bitnet_linear_forward(const int8_t* xq, const float* x_scale, const int32_t*
                           const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                           int64_t K, float* y, int32_t* acc, void* stream);
 
+/*
+ * Fused BitLinear forward: bitnet_quant_act followed by bitnet_linear_forward
+ * in one call, with the same outputs ([FT] "양자화 메커니즘", "계산 패러다임").
+ *
+ *   x, gain, eps         in   as bitnet_quant_act.
+ *   packed, w_scale      in   as bitnet_linear_forward.
+ *   xq, x_scale, x_qsum  out  as bitnet_quant_act (the codes the contraction used).
+ *   y, acc               out  as bitnet_linear_forward (acc may be NULL).
+ * For decode (M <= 4 tokens, and K <= 32768 / M * 4 bytes of codes per lane as
+ * in the GEMV) the normalisation and quantisation run inside the contraction
+ * kernel, one launch in all; larger M run the two kernels back to back.
+ * N = 0 only quantises; M = 0 is a no-op.
+ */
+int bitnet_bitlinear_forward(const uint16_t* x, const float* gain, float eps,
+                             const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, int8_t* xq, float* x_scale, int32_t* x_qsum, float* y,
+                             int32_t* acc, void* stream);
+
+/*
+ * Profiling hook: arm two hipEvent_t (passed as void*; either may be NULL) for
+ * the first kernel the next bitnet_* call on this thread launches (the
+ * contraction kernel of bitnet_linear_forward, the quantisation kernel of the
+ * quantisation calls and of bitnet_bitlinear_forward when M > 4, the fused
+ * kernel of bitnet_bitlinear_forward when M <= 4).  That kernel is then launched with
+ * hipExtLaunchKernelGGL, which records `start_event` / `stop_event` at the
+ * start and end of its execution, so hipEventElapsedTime gives the kernel's
+ * duration without dispatch gaps.  The events are disarmed when that call
+ * returns, whether it launched or not.  Always returns BITNET_OK.
+ */
+int bitnet_set_kernel_events(void* start_event, void* stop_event);
+
 /* Static text for a status code. */
 const char* bitnet_status_string(int status);
 

@@ -39,6 +39,7 @@ def load(path: str):
     lib = ctypes.CDLL(path)
     p, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     lib.oracle_version.restype = i32
+    lib.oracle_num_threads.restype = i32
     lib.oracle_unpack_weights.argtypes = [p, i64, i64, p]
     lib.oracle_unpack_weights.restype = i64
     lib.oracle_fwht_f32.argtypes = [p, i64]
@@ -71,6 +72,10 @@ class Oracle:
 
     def __init__(self, lib=None):
         self.lib = lib if lib is not None else _lib()
+
+    def num_threads(self) -> int:
+        """OpenMP threads the oracle's parallel loops use."""
+        return int(self.lib.oracle_num_threads())
 
     def unpack_weights(self, packed: np.ndarray, K: int) -> np.ndarray:
         packed = _c(packed, np.uint8)

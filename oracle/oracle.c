@@ -47,6 +47,7 @@
  * is "parity unpinned".
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -54,6 +55,9 @@
 #define ORACLE_VERSION 1
 
 int oracle_version(void) { return ORACLE_VERSION; }
+
+/* Threads the OpenMP loops below use (for reporting CPU timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* bfloat16 bits -> float32 (exact: bf16 is the top half of a float32). */
 static float bf16_bits_to_float(uint16_t h) {
@@ -79,6 +83,7 @@ static int packed_shift_of(int64_t k) { return (int)(2 * ((k % 16) / 4)); }
 int64_t oracle_unpack_weights(const uint8_t* packed, int64_t N, int64_t K, int8_t* q) {
     int64_t bad = 0;
     const int64_t row_bytes = K / 4;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
     for (int64_t n = 0; n < N; n++) {
         for (int64_t k = 0; k < K; k++) {
             int field = (packed[n * row_bytes + packed_byte_of(k)] >> packed_shift_of(k)) & 3;
@@ -309,7 +314,7 @@ int oracle_int_gemm(const int8_t* xq, const uint8_t* packed, int64_t M, int64_t 
     int8_t* qw = (int8_t*)malloc((size_t)N * (size_t)K);
     if (!qw) return -1;
     oracle_unpack_weights(packed, N, K, qw);
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (int64_t m = 0; m < M; m++) {
         for (int64_t n = 0; n < N; n++) {
             int64_t s = 0;

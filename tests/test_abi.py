@@ -128,3 +128,29 @@ def test_binding_rejects_cpu_tensors():
         bt.quant_act(torch.zeros((2, 64), dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         bt.quant_act(torch.zeros((2, 64), dtype=torch.float32))
+
+
+def _fused(L, x=A16, gain=None, eps=1e-5, P=A16, ws=A4, M=1, N=8, K=256, xq=A16, sx=A4, qs=A4,
+           y=A4, acc=None):
+    return L.bitnet_bitlinear_forward(
+        ctypes.c_void_p(x), None if gain is None else ctypes.c_void_p(gain), ctypes.c_float(eps),
+        ctypes.c_void_p(P), ctypes.c_void_p(ws), M, N, K, ctypes.c_void_p(xq), ctypes.c_void_p(sx),
+        ctypes.c_void_p(qs), ctypes.c_void_p(y), None if acc is None else ctypes.c_void_p(acc), None)
+
+
+def test_fused_forward_argument_errors(L):
+    assert _fused(L, M=-1) == 2
+    assert _fused(L, N=-1) == 2
+    assert _fused(L, K=100) == 2
+    assert _fused(L, eps=-1.0) == 7
+    assert _fused(L, x=0) == 1
+    assert _fused(L, P=0) == 1
+    assert _fused(L, y=0) == 1
+    assert _fused(L, x=BAD) == 4
+    assert _fused(L, P=A4) == 4
+    assert _fused(L, acc=BAD) == 4
+    assert _fused(L, M=0, x=0, P=0, y=0) == 0
+
+
+def test_kernel_events_hook_is_exported(L):
+    assert L.bitnet_set_kernel_events(None, None) == 0

@@ -268,3 +268,67 @@ def test_hadamard_bitlinear_end_to_end(orc, dev):
     _, want_y = orc.linear_forward(xq, d_x, packed, d_w, K)
     layer = bt.BitLinear(to_dev(W, dev), hadamard=True)
     assert_close_rel(host(layer(bf16_to_dev(x, dev))), want_y)
+
+
+# ---------------------------------------------------------------------------
+# Fused forward (quantisation inside the contraction kernel for M <= 4).
+# ---------------------------------------------------------------------------
+
+FUSED_CASES = [
+    (1, 4096, 4096, False), (1, 11008, 4096, False), (1, 4096, 11008, True), (2, 1000, 4096, False),
+    (3, 77, 8192, True), (4, 4097, 8192, False), (1, 33, 32768, False), (1, 1, 64, True),
+    (1, 14336, 4096, False), (1, 4096, 14336, False), (4, 300, 256, True),
+    (5, 100, 1024, False), (64, 257, 4096, True),     # two-kernel path (M > 4)
+    (2, 50, 32768, False),                             # M * K beyond the fused limit
+]
+
+
+@pytest.mark.parametrize("M,N,K,with_gain", FUSED_CASES)
+def test_bitlinear_forward_fused(orc, dev, M, N, K, with_gain):
+    W = synth.weights(N, K, seed=800 + N % 71)
+    x = _activation(M, K, seed=801 + K % 67)
+    gain = np.random.default_rng(N + K).uniform(0.5, 1.5, K).astype(np.float32) if with_gain else None
+    packed, d_w, _, _ = orc.pack_weights(W)
+    wq, wdx, wqs = orc.quant_act(x, gain=gain)
+    want_acc, want_y = orc.linear_forward(wq, wdx, packed, d_w, K)
+    w_scale = np.array([d_w, 0], np.float32)
+    codes = (torch.empty((M, K), dtype=torch.int8, device=dev), torch.empty(M, device=dev),
+             torch.empty(M, dtype=torch.int32, device=dev))
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    y, acc = bt.bitlinear_forward(bf16_to_dev(x, dev), to_dev(packed, dev), to_dev(w_scale, dev),
+                                  None if gain is None else to_dev(gain, dev), 1e-5, codes=codes,
+                                  acc_out=acc)
+    np.testing.assert_array_equal(host(codes[0]), wq)
+    np.testing.assert_array_equal(host(codes[2]), wqs)
+    assert_close_rel(host(codes[1]), wdx)
+    np.testing.assert_array_equal(host(acc), want_acc)
+    assert_close_rel(host(y), want_y)
+
+
+def test_bitlinear_forward_graph_replays(orc, dev):
+    """The fused decode captured in a HIP graph: every replay matches the eager result."""
+    M, N, K = 1, 4096, 4096
+    W = synth.weights(N, K, 900)
+    packed_np, d_w, _, _ = orc.pack_weights(W)
+    packed, w_scale = to_dev(packed_np, dev), to_dev(np.array([d_w, 0], np.float32), dev)
+    xs = [bf16_to_dev(_activation(M, K, 901 + i), dev) for i in range(3)]
+    x = xs[0].clone()
+    codes = (torch.empty((M, K), dtype=torch.int8, device=dev), torch.empty(M, device=dev),
+             torch.empty(M, dtype=torch.int32, device=dev))
+    y = torch.empty((M, N), device=dev)
+    eager = []
+    for xi in xs:
+        eager.append(host(bt.bitlinear_forward(xi, packed, w_scale)).copy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            bt.bitlinear_forward(x, packed, w_scale, out=y, codes=codes)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(6):
+        i = rep % 3
+        x.copy_(xs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), eager[i])
