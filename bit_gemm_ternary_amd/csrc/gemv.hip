@@ -25,8 +25,9 @@
 // Fused variant: each 256-thread workgroup first quantises the (<= 4) tokens
 // itself (RMSNorm + absmax int8, the same arithmetic as quant_act.hip) from the
 // bf16 input, which every workgroup reads from L2, and shares the codes through
-// LDS; the weight loads of the first batch are issued before that prologue.
-// This removes the separate quantisation launch from the decode critical path.
+// LDS; the weight loads of the first batch are issued right after the
+// activation loads and stay in flight through that prologue.  This removes the
+// separate quantisation launch from the decode critical path.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -185,6 +186,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 // Fused RMSNorm + int8 quantisation + GEMV.  Every workgroup quantises the MT
 // tokens (K <= CH * 4096) into LDS; workgroup 0 also writes the codes, scales
 // and sums to global memory.
+//
+// Order matters for latency: the bf16 activations are loaded first and the
+// weights second, so the prologue (which waits for its own loads, and loads
+// complete in issue order) does not wait for the weights; the weight loads
+// stay in flight through the prologue.  The prologue needs one workgroup
+// reduction (absmax and sum of squares of every token together); each wave
+// then sums the codes it reads back from LDS itself.
 template <int MT, int CH>
 __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
@@ -195,46 +203,50 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
     using G = GemvCore<MT, CH>;
     constexpr int XV = 2 * CH;  // 8-value bf16 vectors per thread per token (K <= CH*4096)
     __shared__ __align__(16) int8_t codes[MT][CH * 4096];
-    __shared__ float red_f[kGemvWaves];
-    __shared__ double red_d[kGemvWaves];
-    __shared__ int red_i[kGemvWaves];
-    __shared__ float tok_scale[MT];
-    __shared__ int tok_sum[MT];
+    __shared__ float red_f[MT][kGemvWaves];
+    __shared__ double red_d[MT][kGemvWaves];
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
-    const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + t / kWave) * rows_per_wave;
+    const int wave_id = t / kWave;
+    const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + wave_id) * rows_per_wave;
     const int64_t row1 = min((int64_t)N, row0 + rows_per_wave);
     const int nchunk = K / 64;
     const int64_t row_bytes = K / 4;
     const int nvec = K / 8;
 
-    // Weight loads first: they stay in flight through the quantisation prologue.
-    uint4 w[G::RB][CH];
-    G::load(w, packed, row_bytes, nchunk, row0, row1, lane);
-
+    // 1. Activation loads, then weight loads (in flight through the prologue).
+    uint4 raw[MT][XV];
+#pragma unroll
     for (int tok = 0; tok < MT; ++tok) {
         const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)tok * K);
-        uint4 raw[XV];
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int v = t + kGemvThreads * i;
-            raw[i] = v < nvec ? xr[v] : make_uint4(0, 0, 0, 0);
+            raw[tok][i] = v < nvec ? xr[v] : make_uint4(0, 0, 0, 0);
         }
-        auto values = [&](int i, int v, float (&u)[8], bool with_gain) {
-            const uint32_t ws[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    }
+    uint4 w[G::RB][CH];
+    G::load(w, packed, row_bytes, nchunk, row0, row1, lane);
+
+    auto values = [&](int tok, int i, int v, float (&u)[8], bool with_gain) {
+        const uint32_t ws[4] = {raw[tok][i].x, raw[tok][i].y, raw[tok][i].z, raw[tok][i].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u[2 * e] = bf16_lo(ws[e]);
-                u[2 * e + 1] = bf16_hi(ws[e]);
-            }
-            if (with_gain && gain != nullptr) {
-                const float4 g0 = reinterpret_cast<const float4*>(gain)[2 * v];
-                const float4 g1 = reinterpret_cast<const float4*>(gain)[2 * v + 1];
-                u[0] *= g0.x; u[1] *= g0.y; u[2] *= g0.z; u[3] *= g0.w;
-                u[4] *= g1.x; u[5] *= g1.y; u[6] *= g1.z; u[7] *= g1.w;
-            }
-        };
+        for (int e = 0; e < 4; ++e) {
+            u[2 * e] = bf16_lo(ws[e]);
+            u[2 * e + 1] = bf16_hi(ws[e]);
+        }
+        if (with_gain && gain != nullptr) {
+            const float4 g0 = reinterpret_cast<const float4*>(gain)[2 * v];
+            const float4 g1 = reinterpret_cast<const float4*>(gain)[2 * v + 1];
+            u[0] *= g0.x; u[1] *= g0.y; u[2] *= g0.z; u[3] *= g0.w;
+            u[4] *= g1.x; u[5] *= g1.y; u[6] *= g1.z; u[7] *= g1.w;
+        }
+    };
+
+    // 2. Per-token absmax of x*gain and sum of x^2: one workgroup reduction.
+#pragma unroll
+    for (int tok = 0; tok < MT; ++tok) {
         float amax = 0.f;
         double ss = 0.0;
 #pragma unroll
@@ -242,45 +254,83 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
             const int v = t + kGemvThreads * i;
             if (v < nvec) {
                 float u[8];
-                values(i, v, u, false);
+                values(tok, i, v, u, false);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += (double)u[e] * (double)u[e];
-                values(i, v, u, true);
+                values(tok, i, v, u, true);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(u[e]));
             }
         }
-        amax = block_reduce<kGemvThreads>(wave_max(amax), red_f, MaxOp());
-        ss = block_reduce<kGemvThreads>(wave_sum(ss), red_d, SumOp());
+        amax = wave_max(amax);
+        ss = wave_sum(ss);
+        if (lane == 0) {
+            red_f[tok][wave_id] = amax;
+            red_d[tok][wave_id] = ss;
+        }
+    }
+    __syncthreads();
+
+    // 3. Codes into LDS; every thread derives the same scales.
+    float tok_scale[MT];
+#pragma unroll
+    for (int tok = 0; tok < MT; ++tok) {
+        float amax = red_f[tok][0];
+        double ss = red_d[tok][0];
+#pragma unroll
+        for (int wv = 1; wv < kGemvWaves; ++wv) {
+            amax = fmaxf(amax, red_f[tok][wv]);
+            ss += red_d[tok][wv];
+        }
         const bool zero = amax < kTinyAbsmax;
         const float scale = zero ? 0.f : 127.0f / amax;
-        int qs = 0;
+        const double rstd = 1.0 / sqrt(ss / (double)K + (double)eps);
+        tok_scale[tok] = zero ? 0.f : (float)(((double)amax * rstd) / 127.0);
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int v = t + kGemvThreads * i;
             if (v < nvec) {
                 float u[8];
-                values(i, v, u, true);
+                values(tok, i, v, u, true);
                 uint32_t lo = 0, hi = 0;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int q0 = zero ? 0 : round_clamp(u[e] * scale, -128.f, 127.f);
                     const int q1 = zero ? 0 : round_clamp(u[4 + e] * scale, -128.f, 127.f);
-                    qs += q0 + q1;
                     lo |= (uint32_t)(q0 & 0xff) << (8 * e);
                     hi |= (uint32_t)(q1 & 0xff) << (8 * e);
                 }
                 *reinterpret_cast<uint2*>(&codes[tok][8 * v]) = make_uint2(lo, hi);
             }
         }
-        qs = block_reduce<kGemvThreads>(wave_sum(qs), red_i, SumOp());
-        if (t == 0) {
-            const double rstd = 1.0 / sqrt(ss / (double)K + (double)eps);
-            tok_scale[tok] = zero ? 0.f : (float)(((double)amax * rstd) / 127.0);
-            tok_sum[tok] = qs;
-        }
     }
     __syncthreads();
+
+    // 4. Codes of my chunks into registers; the wave sums them itself.
+    uint32_t xv[MT][CH][16];
+    int tok_sum[MT];
+#pragma unroll
+    for (int tok = 0; tok < MT; ++tok) {
+        int part = 0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = lane + kWave * j;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint4 a = make_uint4(0, 0, 0, 0);
+                if (c < nchunk) a = reinterpret_cast<const uint4*>(&codes[tok][64 * c])[q];
+                xv[tok][j][4 * q] = a.x;
+                xv[tok][j][4 * q + 1] = a.y;
+                xv[tok][j][4 * q + 2] = a.z;
+                xv[tok][j][4 * q + 3] = a.w;
+                part = dot4(a.x, 0x01010101u, part);
+                part = dot4(a.y, 0x01010101u, part);
+                part = dot4(a.z, 0x01010101u, part);
+                part = dot4(a.w, 0x01010101u, part);
+            }
+        }
+        tok_sum[tok] = wave_sum_dpp(part);
+    }
 
     if (blockIdx.x == 0) {
         for (int tok = 0; tok < MT; ++tok) {
@@ -295,23 +345,6 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
     }
     if (row0 >= N) return;  // after the last barrier: wave-uniform exit
 
-    uint32_t xv[MT][CH][16];
-#pragma unroll
-    for (int tok = 0; tok < MT; ++tok) {
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int c = lane + kWave * j;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint4 a = make_uint4(0, 0, 0, 0);
-                if (c < nchunk) a = reinterpret_cast<const uint4*>(&codes[tok][64 * c])[q];
-                xv[tok][j][4 * q] = a.x;
-                xv[tok][j][4 * q + 1] = a.y;
-                xv[tok][j][4 * q + 2] = a.z;
-                xv[tok][j][4 * q + 3] = a.w;
-            }
-        }
-    }
     int my_acc[MT];
 #pragma unroll
     for (int tok = 0; tok < MT; ++tok) my_acc[tok] = 0;
