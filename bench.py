@@ -20,7 +20,16 @@ not Python launch overhead.
   prefill          W1.58A8 prefill M=2048, K=4096, N=14336: int8 TOPS of the
                    matrix-core GEMM against the dense int8 peak
   hadamard         H-BitLinear M=512: FWHT + int4 quantisation GB/s and GEMM TOPS
+  block            the seven BitLinear projections of a Llama-3-8B block at
+                   M = 1, 16 and 256 tokens: time per block, packed weight GB/s,
+                   int TOPS
   cpu_baseline     the CPU oracle on this host running the same decode step
+
+roofline.traffic is the HBM bytes per launch of the fused decode kernel that
+rocprofv3's FETCH_SIZE and WRITE_SIZE counters read, scaled by what the same
+counters read for a plain device copy of known size (--copy-calibration); it is
+read from the committed counter summary and reported as null when the kernel
+source has changed since those counters were taken.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -61,7 +70,103 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the prefill / H-BitLinear legs")
     ap.add_argument("--eager", action="store_true", help="launch steps eagerly instead of from graphs")
+    ap.add_argument("--block-steps", type=int, default=200, help="timed steps per token count of the block leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of COPY_BYTES, ten times (HBM counter calibration)")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_decode_kernel.decode_M1.hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_gemm_ternary_amd", "csrc", f)
+                  for f in ("gemv.hip", "common.hpp")]
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per step of the fused decode kernels from the committed counter
+    summary, or None if there is none or the kernel source has changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            for line in f:
+                if line.startswith("bench-data: "):
+                    data = json.loads(line[len("bench-data: "):])
+                    break
+            else:
+                return None
+    except OSError:
+        return None
+    if data.get("source_sha256") != kernel_source_digest():
+        return None
+    return data
+
+
+def copy_calibration(torch):
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 10}), flush=True)
+
+
+def graph_runner(step, copies, eager, torch):
+    """run(n): n steps, step s using rotation copy s % copies, replayed from HIP
+    graphs (one per copy and one per full rotation) unless eager."""
+    if eager:
+        def run(n):
+            for s in range(n):
+                step(s % copies)
+        return run
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for r in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(r)
+            graphs.append(g)
+        cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cycle, stream=side):
+            for r in range(copies):
+                step(r)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for g in graphs[: min(len(graphs), 8)]:
+        g.replay()
+    cycle.replay()
+    torch.cuda.synchronize()
+
+    def run(n):
+        full, rest = divmod(n, copies)
+        for _ in range(full):
+            cycle.replay()
+        for s in range(rest):
+            graphs[s].replay()
+    return run
+
+
+def timed(run, steps, torch):
+    """(ms per step, wall seconds) of run(steps) between two synchronisations."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    run(steps)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, time.perf_counter() - t0
 
 
 class HipEvents:
@@ -99,13 +204,12 @@ class HipEvents:
 class DecodeLayer:
     """Device buffers of one M=1 projection with R rotating copies of its packed weights."""
 
-    def __init__(self, layer, copies, dev, bt, torch):
+    def __init__(self, layer, copies, dev, bt, torch, packed=None):
         self.layer = layer
         M, K, N = layer.M, layer.K, layer.N
-        W = torch.from_numpy(layer.weights()).to(dev)
-        packed, self.w_scale = bt.pack_weights(W)
-        del W
-        self.packed = [packed] + [packed.clone() for _ in range(copies - 1)]
+        if packed is None:
+            packed = packed_copies(layer, copies, dev, bt, torch)
+        self.packed, self.w_scale = packed
         x = layer.activations()
         self.x = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         self.codes = (torch.empty((M, K), dtype=torch.int8, device=dev),
@@ -120,6 +224,14 @@ class DecodeLayer:
     def forward(self, bt, r):
         bt.bitlinear_forward(self.x, self.packed[r], self.w_scale, None, 1e-5, out=self.y,
                              codes=self.codes)
+
+
+def packed_copies(layer, copies, dev, bt, torch):
+    """(copies of the layer's packed weights, w_scale)."""
+    W = torch.from_numpy(layer.weights()).to(dev)
+    packed, w_scale = bt.pack_weights(W)
+    del W
+    return [packed] + [packed.clone() for _ in range(copies - 1)], w_scale
 
 
 def decode_bench(args, dev, bt, torch, synth):
@@ -140,50 +252,8 @@ def decode_bench(args, dev, bt, torch, synth):
         step(s % copies)
     torch.cuda.synchronize()
 
-    graphs, cycle = None, None
-    if not args.eager:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        graphs = []
-        with torch.cuda.stream(side):
-            for r in range(copies):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    step(r)
-                graphs.append(g)
-            cycle = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(cycle, stream=side):
-                for r in range(copies):
-                    step(r)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        for g in graphs[: min(len(graphs), 8)]:
-            g.replay()
-        cycle.replay()
-        torch.cuda.synchronize()
-
-    def run_steps(n):
-        if graphs is None:
-            for s in range(n):
-                step(s % copies)
-            return
-        full, rest = divmod(n, copies)
-        for _ in range(full):
-            cycle.replay()
-        for s in range(rest):
-            graphs[s].replay()
-
-    # Timed region: exactly `steps` steps between two synchronisations.
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    run_steps(args.steps)
-    end.record()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    gpu_ms = start.elapsed_time(end)
-    ms_per_step = gpu_ms / args.steps
+    run_steps = graph_runner(step, copies, args.eager, torch)
+    ms_per_step, wall_s = timed(run_steps, args.steps, torch)
 
     # Per-kernel durations: the same steps again, launched eagerly with the
     # kernel-timing hook armed before every launch, so each event pair is
@@ -288,6 +358,40 @@ def hadamard_bench(args, dev, bt, torch, synth):
     return out
 
 
+def block_bench(args, dev, bt, torch, synth):
+    """The seven projections of a Llama-3-8B block, each RMSNorm + quantisation +
+    contraction + dequantisation through bitnet_bitlinear_forward, at M = 1, 16
+    and 256 tokens; weights rotate over > 1 GiB of copies as in the decode leg."""
+    spec = synth.workload("block", M=1)
+    block_bytes = sum(l.N * l.K // 4 for l in spec)
+    copies = max(1, math.ceil(ROTATE_BYTES / block_bytes))
+    packed = [packed_copies(l, copies, dev, bt, torch) for l in spec]
+    out = []
+    for M in (1, 16, 256):
+        layers = [DecodeLayer(l, copies, dev, bt, torch, packed=p)
+                  for l, p in zip(synth.workload("block", M=M), packed)]
+
+        def step(r, layers=layers):
+            for L in layers:
+                L.forward(bt, r)
+
+        for s in range(min(args.warmup, 2 * copies)):
+            step(s % copies)
+        torch.cuda.synchronize()
+        run = graph_runner(step, copies, args.eager, torch)
+        ms, _ = timed(run, args.block_steps, torch)
+        ops = 2.0 * M * sum(l.N * l.K for l in spec)
+        out.append({"M": M, "us_per_block": round(ms * 1e3, 2),
+                    "packed_GB_s": round(block_bytes / (ms * 1e-3) / 1e9, 1),
+                    "TOPS": round(ops / (ms * 1e-3) / 1e12, 2)})
+        del layers
+    return {"workload": "Llama-3-8B block: q 4096x4096, k/v 4096x1024, o 4096x4096, gate/up "
+                        "4096x14336, down 14336x4096; bf16 N(0,1) tokens, RMSNorm + int8 quant "
+                        "before each projection",
+            "packed_bytes_per_block": block_bytes, "weight_rotation_copies": copies,
+            "by_tokens": out}
+
+
 def cpu_baseline(args, synth):
     import oracle
 
@@ -333,6 +437,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs the GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     bt.lib()
@@ -350,10 +457,14 @@ def main():
         torch.cuda.empty_cache()
         secondary["hadamard"] = hadamard_bench(args, dev, bt, torch, synth)
         log(f"hadamard: {secondary['hadamard']}")
+        torch.cuda.empty_cache()
+        secondary["block"] = block_bench(args, dev, bt, torch, synth)
+        log(f"block: {secondary['block']}")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
 
     achieved = dec["kernel_bytes"] / dec["kernel_us"] / 1e3
+    traffic = measured_traffic()
     line = {
         "metric": METRIC,
         "value": round(dec["value"], 1),
@@ -384,7 +495,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else traffic["hbm_bytes_per_step"],
+            "traffic_per_launch": None if traffic is None else traffic["hbm_bytes_per_launch"],
             "kernel": "fused_decode_kernel (3 launches per step)",
             "bytes_per_step": dec["kernel_bytes"],
             "us_per_step": round(dec["kernel_us"], 3),

@@ -10,38 +10,66 @@
 // as the A operand and the int8 activations as the B operand; the offset is
 // removed in the epilogue with the per-token code sums.
 //
-// Tiling: a workgroup computes a BN (weight rows) x BM (tokens) tile with
-// WN x WM wavefronts, each owning (BN/WN) x (BM/WM) as 16x16 MFMA blocks.  Per
-// K-stage of BK values the workgroup copies the packed weight tile (BK/4 bytes
-// per row, 4x smaller than int8) and the int8 activation tile into LDS (double
-// buffered, one barrier per stage); A fragments are unpacked from one packed
-// dword per lane with shift/mask ((word >> 2i) & 0x03030303 is already in
-// natural byte order), B fragments are one 16-byte LDS read per lane.
+// Tiling.  A workgroup of WN x WM wavefronts computes a BN (weight rows) x BM
+// (tokens) tile, each wave (BN/WN) x (BM/WM) as 16x16 MFMA blocks.  K advances
+// in stages of 256: the int8 activation tile (BM rows x 256 B) and the packed
+// weight tile (BN rows x 64 B) are copied straight from HBM/L2 into LDS by
+// buffer_load ... lds (no register staging), double buffered, one barrier per
+// stage.  64 bytes per weight row per stage is the narrowest access that still
+// streams full memory sectors: at 32 bytes per row the weight loads ran at a
+// third of the activation loads' rate.  Large tiles (448 x 128 for big grids)
+// keep the bytes re-read per MFMA low.
 //
-// MFMA operand layout used (16x16x64, wave64): lane l supplies row (l % 16) of
-// A and column (l % 16) of B over the 16 K-values 16*(l/16) .. 16*(l/16)+15 of
-// the 64-wide step (any K assignment shared by A and B gives the same sum);
-// the result D[i][j] sits in lane j + 16*(i/4), element i % 4.
+// K assignment.  MFMA 16x16x64 takes, per lane, 16 K-values of one A row and
+// the same 16 K-values of one B column; any assignment of K-values to lanes
+// shared by A and B gives the same sum.  Here, in K step ks (0..3) of a stage,
+// lane group g = lane/16 covers the 16 weights of packed word 4g + ks of the
+// stage's 64 words per row (weights 64g + 16ks .. +15).  So one 16-byte LDS read
+// gives a lane its weight words for all four K steps, each unpacked to natural
+// order by (word >> 2i) & 0x03030303; the activation fragment is the matching
+// 16 bytes.  The result D[i][j] sits in lane j + 16*(i/4), element i % 4.
+//
+// LDS layouts (bank-conflict free for the 16-byte fragment reads):
+//   activations: row r of 256 B as 16 segments, segment s stored at s ^ (r & 15);
+//   weights: row r of 64 B as 4 pieces, piece f stored at f ^ ((r >> 2) & 3).
+// Rows past M or N and the K tail are zero-filled by the buffer loads' range
+// check (the resource covers only the block's valid rows).
+//
+// Block order.  Workgroups are dispatched round-robin over the 8 XCDs (each
+// with its own L2); the launch index is remapped so that each XCD works on a
+// contiguous range of tiles, ordered in groups of 8 token tiles per weight
+// tile column, so concurrently running blocks on one XCD share operands in L2.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace bitnet {
 namespace {
 
-template <int BN_, int BM_, int WN_, int WM_, int BK_>
+typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+constexpr int kBK = 256;                         // K values per LDS stage
+constexpr int kXcds = 8;                         // XCDs on MI355X
+constexpr int kGroupM = 8;                       // token tiles per group in the tile order
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9-family raw buffer descriptor word 3
+constexpr uint32_t kOutOfRange = 0x80000000u;    // offset past any block's buffer: loads 0
+
+template <int BN_, int BM_, int WN_, int WM_, int OCC_>
 struct GemmCfg {
-    static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, BK = BK_;
+    static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
+    static constexpr int OCC = OCC_;                // workgroups per CU the tile is sized for
     static constexpr int NT = WN * WM * kWave;
-    static constexpr int TN = BN / WN, TM = BM / WM;   // wave tile
-    static constexpr int FN = TN / 16, FM = TM / 16;   // MFMA blocks per wave
-    static constexpr int XS = BK + 16;                 // LDS row stride of the activation tile (bytes)
-    static constexpr int WS = BK / 4 + 16;             // LDS row stride of the packed weight tile
-    static constexpr int X_CHUNKS = BM * BK / 16;      // 16-byte chunks per stage
-    static constexpr int W_CHUNKS = BN * BK / 64;
-    static constexpr int X_LOADS = (X_CHUNKS + NT - 1) / NT;
-    static constexpr int W_LOADS = (W_CHUNKS + NT - 1) / NT;
-    static constexpr int LDS_X = BM * XS, LDS_W = BN * WS;
-    static_assert(TN % 16 == 0 && TM % 16 == 0 && BK % 64 == 0, "tile shape");
+    static constexpr int TN = BN / WN, TM = BM / WM;
+    static constexpr int FN = TN / 16, FM = TM / 16;
+    static constexpr int X_STAGE = BM * kBK;         // bytes
+    static constexpr int W_STAGE = BN * (kBK / 4);   // bytes
+    static constexpr int X_SLOTS = BM * 16;          // 16-byte slots per stage
+    static constexpr int W_SLOTS = BN * 4;
+    static constexpr int XL = (X_SLOTS + NT - 1) / NT;
+    static constexpr int WL = (W_SLOTS + NT - 1) / NT;
+    static_assert(TN % 16 == 0 && TM % 16 == 0, "wave tile must be whole MFMA blocks");
+    static_assert(X_SLOTS % kWave == 0 && W_SLOTS % kWave == 0, "whole waves per load");
+    static_assert(2 * (X_STAGE + W_STAGE) <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
@@ -53,56 +81,78 @@ __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
     return r;
 }
 
+// All of this wave's loads into LDS have landed and its LDS reads are done,
+// then the workgroup barrier.  Written as one asm statement with a memory
+// clobber so the compiler neither moves LDS accesses across it nor adds a
+// wait of its own for loads still in flight elsewhere.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_kernel(
+__global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     const int8_t* __restrict__ X, const uint8_t* __restrict__ P, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_qsum, const float* __restrict__ w_scale, int M, int N, int K,
-    float* __restrict__ y, int32_t* __restrict__ acc_out) {
-    __shared__ __align__(16) int8_t lds_x[2][C::LDS_X];
-    __shared__ __align__(16) uint8_t lds_w[2][C::LDS_W];
+    int vec_store, float* __restrict__ y, int32_t* __restrict__ acc_out) {
+    __shared__ __align__(16) int8_t lds[2][C::X_STAGE + C::W_STAGE];
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
     const int wave = t / kWave;
     const int wn = wave % C::WN, wm = wave / C::WN;
-    const int64_t tiles_n = (N + C::BN - 1) / C::BN;
-    const int64_t n0 = ((int64_t)blockIdx.x % tiles_n) * C::BN;
-    const int64_t m0 = ((int64_t)blockIdx.x / tiles_n) * C::BM;
-    const int64_t row_bytes = K / 4;
 
-    uint4 rx[C::X_LOADS], rw[C::W_LOADS];
+    // Launch index -> tile: contiguous ranges per XCD, grouped order.
+    const int tiles_n = (N + C::BN - 1) / C::BN;
+    const int tiles_m = (M + C::BM - 1) / C::BM;
+    const int total = tiles_n * tiles_m;
+    const int per = total / kXcds, rem = total % kXcds;
+    const int xcd = (int)blockIdx.x % kXcds, idx = (int)blockIdx.x / kXcds;
+    const int tile = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+    const int group = tile / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    const int in_group = tile % (kGroupM * tiles_n);
+    const int tm = first_m + in_group % gsize;
+    const int tn = in_group / gsize;
+    const int64_t n0 = (int64_t)tn * C::BN;
+    const int64_t m0 = (int64_t)tm * C::BM;
+    const int row_bytes = K / 4;
 
-    // Global -> registers for the stage starting at k0 (zero outside M, N, K).
-    auto load_stage = [&](int k0) {
+    // Buffer resources cover only this block's valid rows.
+    const int x_rows = (int)min((int64_t)C::BM, (int64_t)M - m0);
+    const int w_rows = (int)min((int64_t)C::BN, (int64_t)N - n0);
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(X + m0 * K), (short)0, x_rows * K, (int)kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(P + n0 * row_bytes), (short)0, w_rows * row_bytes, (int)kBufferWord3);
+
+    // Copy one stage into LDS buffer `buf`.  Each load instruction moves 1 KiB:
+    // lane l of the wave fills the 16-byte slot base + l, so the global address
+    // each lane reads is chosen to realise the swizzled layout.
+    auto issue = [&](int buf, int k0) {
 #pragma unroll
-        for (int i = 0; i < C::X_LOADS; ++i) {
-            const int idx = t + i * C::NT;
-            const int r = idx / (C::BK / 16), c = idx % (C::BK / 16);
-            rx[i] = make_uint4(0, 0, 0, 0);
-            if (idx < C::X_CHUNKS && m0 + r < M && k0 + 16 * c < K)
-                rx[i] = *reinterpret_cast<const uint4*>(X + (m0 + r) * K + k0 + 16 * c);
+        for (int i = 0; i < C::XL; ++i) {
+            const int base = i * C::NT + wave * kWave;   // wave-uniform
+            if (base < C::X_SLOTS) {
+                const int p = base + lane;
+                const int r = p >> 4, s = (p & 15) ^ (r & 15);
+                const int k = k0 + 16 * s;
+                const uint32_t off = k < K ? (uint32_t)(r * K + k) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)&lds[buf][base * 16], 16,
+                                                         (int)off, 0, 0, 0);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < C::W_LOADS; ++i) {
-            const int idx = t + i * C::NT;
-            const int r = idx / (C::BK / 64), c = idx % (C::BK / 64);
-            rw[i] = make_uint4(0, 0, 0, 0);
-            if (idx < C::W_CHUNKS && n0 + r < N && k0 + 64 * c < K)
-                rw[i] = *reinterpret_cast<const uint4*>(P + (n0 + r) * row_bytes + k0 / 4 + 16 * c);
-        }
-    };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < C::X_LOADS; ++i) {
-            const int idx = t + i * C::NT;
-            const int r = idx / (C::BK / 16), c = idx % (C::BK / 16);
-            if (idx < C::X_CHUNKS) *reinterpret_cast<uint4*>(&lds_x[buf][r * C::XS + 16 * c]) = rx[i];
-        }
-#pragma unroll
-        for (int i = 0; i < C::W_LOADS; ++i) {
-            const int idx = t + i * C::NT;
-            const int r = idx / (C::BK / 64), c = idx % (C::BK / 64);
-            if (idx < C::W_CHUNKS) *reinterpret_cast<uint4*>(&lds_w[buf][r * C::WS + 16 * c]) = rw[i];
+        for (int i = 0; i < C::WL; ++i) {
+            const int base = i * C::NT + wave * kWave;
+            if (base < C::W_SLOTS) {
+                const int p = base + lane;
+                const int r = p >> 2, f = (p & 3) ^ ((r >> 2) & 3);
+                const int k = k0 + 64 * f;
+                const uint32_t off = k < K ? (uint32_t)(r * row_bytes + k / 4) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wres, (lds_void*)&lds[buf][C::X_STAGE + base * 16], 16, (int)off, 0, 0, 0);
+            }
         }
     };
 
@@ -112,77 +162,204 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    const int nk = (K + C::BK - 1) / C::BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-
-    const int frag_row = lane % 16;
-    const int frag_grp = lane / 16;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) load_stage((kt + 1) * C::BK);
+    const int fr = lane % 16, fg = lane / 16;
+    auto compute = [&](int buf) {
+        const int8_t* xs = &lds[buf][0];
+        const int8_t* ws = &lds[buf][C::X_STAGE];
+        v4u wv[C::FN];
 #pragma unroll
-        for (int kk = 0; kk < C::BK; kk += 64) {
-            v4i a[C::FN], b[C::FM];
+        for (int i = 0; i < C::FN; ++i) {
+            const int r = wn * C::TN + i * 16 + fr;
+            wv[i] = *reinterpret_cast<const v4u*>(&ws[r * 64 + 16 * (fg ^ ((r >> 2) & 3))]);
+        }
 #pragma unroll
-            for (int i = 0; i < C::FN; ++i) {
-                const int r = wn * C::TN + i * 16 + frag_row;
-                const uint32_t word =
-                    *reinterpret_cast<const uint32_t*>(&lds_w[buf][r * C::WS + kk / 4 + 4 * frag_grp]);
-                a[i] = unpack_codes(word);
-            }
+        for (int ks = 0; ks < 4; ++ks) {
+            v4i b[C::FM];
 #pragma unroll
             for (int j = 0; j < C::FM; ++j) {
-                const int r = wm * C::TM + j * 16 + frag_row;
-                b[j] = *reinterpret_cast<const v4i*>(&lds_x[buf][r * C::XS + kk + 16 * frag_grp]);
+                const int r = wm * C::TM + j * 16 + fr;
+                b[j] = *reinterpret_cast<const v4i*>(&xs[r * kBK + 16 * ((4 * fg + ks) ^ (r & 15))]);
             }
 #pragma unroll
-            for (int i = 0; i < C::FN; ++i)
+            for (int i = 0; i < C::FN; ++i) {
+                const v4i a = unpack_codes(wv[i][ks]);
 #pragma unroll
                 for (int j = 0; j < C::FM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[i][j], 0, 0, 0);
+            }
         }
-        if (kt + 1 < nk) store_stage(buf ^ 1);
-        __syncthreads();
+    };
+
+    const int nk = (K + kBK - 1) / kBK;
+    issue(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        stage_barrier();                       // stage kt landed; buffer (kt+1)&1 is free
+        if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kBK);
+        compute(kt & 1);
     }
 
     // Epilogue: D[n][m] -> y[m][n]; lane holds n = 4*(lane/16) + e, m = lane % 16.
     const float d_w = w_scale[0];
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) {
-        const int64_t m = m0 + wm * C::TM + j * 16 + frag_row;
+        const int64_t m = m0 + wm * C::TM + j * 16 + fr;
         if (m >= M) continue;
         const int32_t qs = x_qsum[m];
         const float sx = x_scale[m];
 #pragma unroll
         for (int i = 0; i < C::FN; ++i) {
-            const int64_t nb = n0 + wn * C::TN + i * 16 + 4 * frag_grp;
+            const int64_t nb = n0 + wn * C::TN + i * 16 + 4 * fg;
+            if (nb >= N) continue;
+            if (vec_store && nb + 3 < N) {
+                const v4i a = acc[i][j] - v4i{qs, qs, qs, qs};
+                if (acc_out != nullptr) *reinterpret_cast<v4i*>(&acc_out[m * N + nb]) = a;
+                float4 v;
+                v.x = ((float)a[0] * sx) * d_w;
+                v.y = ((float)a[1] * sx) * d_w;
+                v.z = ((float)a[2] * sx) * d_w;
+                v.w = ((float)a[3] * sx) * d_w;
+                *reinterpret_cast<float4*>(&y[m * N + nb]) = v;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t n = nb + e;
-                if (n < N) {
-                    const int a = acc[i][j][e] - qs;
-                    if (acc_out != nullptr) acc_out[m * N + n] = a;
-                    y[m * N + n] = ((float)a * sx) * d_w;
+                for (int e = 0; e < 4; ++e) {
+                    if (nb + e < N) {
+                        const int a = acc[i][j][e] - qs;
+                        if (acc_out != nullptr) acc_out[m * N + nb + e] = a;
+                        y[m * N + nb + e] = ((float)a * sx) * d_w;
+                    }
                 }
             }
         }
     }
 }
 
+// Skinny contraction (M <= 16 tokens).  One workgroup owns a 16-row block of
+// weights; its K range is split over the workgroup's KW waves (stage kt goes to
+// wave kt % KW, so at any time the waves read adjacent bytes of each row).  A
+// lane's MFMA fragments are contiguous in memory (16 bytes of packed weights,
+// 64 bytes of activations per stage, in the K assignment described above), so
+// they are loaded straight into registers with no LDS staging; the next
+// stage's loads are issued before the current stage's MFMAs.  The KW partial
+// accumulators are summed through LDS by wave 0, which runs the epilogue.
+template <int KW>
+__global__ __launch_bounds__(KW * kWave) void skinny_kernel(
+    const int8_t* __restrict__ X, const uint8_t* __restrict__ P, const float* __restrict__ x_scale,
+    const int32_t* __restrict__ x_qsum, const float* __restrict__ w_scale, int M, int N, int K,
+    int vec_store, float* __restrict__ y, int32_t* __restrict__ acc_out) {
+    __shared__ v4i part[KW][kWave];
+    const int lane = threadIdx.x % kWave;
+    const int wave = threadIdx.x / kWave;
+    const int fr = lane % 16, fg = lane / 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int row_bytes = K / 4;
+    const bool w_ok = n0 + fr < N;
+    const bool x_ok = fr < M;
+    // Rows past N or M read row 0 (always valid) and are masked to zero.
+    const uint8_t* wp = P + (w_ok ? (n0 + fr) * row_bytes : 0) + 16 * fg;
+    const int8_t* xp = X + (x_ok ? (int64_t)fr * K : 0) + 64 * fg;
+    const int nk = (K + kBK - 1) / kBK;
+
+    struct Frag {
+        v4u w;
+        v4i x[4];
+    };
+    auto load = [&](int kt, Frag& f) {
+        const int k0 = kt * kBK;
+        // K is a multiple of 64, so a lane group's 64 K-values are all in range or all out.
+        const bool in_k = kt < nk && k0 + 64 * fg < K;
+        if (in_k && w_ok) {
+            f.w = *reinterpret_cast<const v4u*>(wp + k0 / 4);
+        } else {
+            f.w = v4u{0, 0, 0, 0};
+        }
+        if (in_k && x_ok) {
+            const v4i* src = reinterpret_cast<const v4i*>(xp + k0);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) f.x[ks] = src[ks];
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) f.x[ks] = v4i{0, 0, 0, 0};
+        }
+    };
+
+    v4i acc = v4i{0, 0, 0, 0};
+    Frag cur, nxt;
+    load(wave, cur);
+    for (int kt = wave; kt < nk; kt += KW) {
+        load(kt + KW, nxt);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_codes(cur.w[ks]), cur.x[ks], acc, 0, 0, 0);
+        cur = nxt;
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < KW; ++w) acc += part[w][lane];
+
+    // D[n][m] sits in lane m + 16 * (n / 4), element n % 4.
+    const int m = fr;
+    const int64_t nb = n0 + 4 * fg;
+    if (m >= M || nb >= N) return;
+    const int32_t qs = x_qsum[m];
+    const float sx = x_scale[m];
+    const float d_w = w_scale[0];
+    if (vec_store && nb + 3 < N) {
+        const v4i a = acc - v4i{qs, qs, qs, qs};
+        if (acc_out != nullptr) *reinterpret_cast<v4i*>(&acc_out[m * N + nb]) = a;
+        float4 v;
+        v.x = ((float)a[0] * sx) * d_w;
+        v.y = ((float)a[1] * sx) * d_w;
+        v.z = ((float)a[2] * sx) * d_w;
+        v.w = ((float)a[3] * sx) * d_w;
+        *reinterpret_cast<float4*>(&y[m * N + nb]) = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (nb + e < N) {
+                const int a = acc[e] - qs;
+                if (acc_out != nullptr) acc_out[m * N + nb + e] = a;
+                y[m * N + nb + e] = ((float)a * sx) * d_w;
+            }
+        }
+    }
+}
+
+template <int KW>
+hipError_t launch_skinny(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
+                         const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                         int64_t K, float* y, int32_t* acc, hipStream_t stream) {
+    const int vec_store = (N % 4 == 0) && ((uintptr_t)y % 16 == 0) &&
+                          (acc == nullptr || (uintptr_t)acc % 16 == 0);
+    return launch_kernel(skinny_kernel<KW>, dim3((unsigned)((N + 15) / 16)), dim3(KW * kWave), 0,
+                         stream, xq, packed, x_scale, x_qsum, w_scale, (int)M, (int)N, (int)K,
+                         vec_store, y, acc);
+}
+
+template <class C>
+int64_t tiles_of(int64_t M, int64_t N) {
+    return ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+}
+
 template <class C>
 hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                       const uint8_t* packed, const float* w_scale, int64_t M, int64_t N, int64_t K,
                       float* y, int32_t* acc, hipStream_t stream) {
-    const int64_t tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
-    return launch_kernel(gemm_kernel<C>, dim3((unsigned)tiles), dim3(C::NT), 0, stream, xq, packed, x_scale, x_qsum,
-                       w_scale, (int)M, (int)N, (int)K, y, acc);
+    const int vec_store = (N % 4 == 0) && ((uintptr_t)y % 16 == 0) &&
+                          (acc == nullptr || (uintptr_t)acc % 16 == 0);
+    return launch_kernel(gemm_kernel<C>, dim3((unsigned)tiles_of<C>(M, N)), dim3(C::NT), 0, stream,
+                         xq, packed, x_scale, x_qsum, w_scale, (int)M, (int)N, (int)K, vec_store, y,
+                         acc);
 }
 
-using CfgLarge = GemmCfg<128, 128, 2, 2, 128>;   // wave tile 64 x 64
-using CfgMid = GemmCfg<128, 64, 2, 2, 128>;      // wave tile 64 x 32
-using CfgSkinny = GemmCfg<64, 16, 4, 1, 128>;    // wave tile 16 x 16
+// Tile configurations (weight rows x tokens, waves, workgroups per CU).
+using CfgLarge = GemmCfg<448, 128, 4, 2, 1>;   // 8 waves, wave tile 112 x 64, 120 KiB LDS
+using CfgMid = GemmCfg<256, 64, 4, 1, 2>;      // 4 waves, wave tile 64 x 64
+using CfgSmall = GemmCfg<128, 64, 2, 2, 2>;    // 4 waves, wave tile 64 x 32
+using CfgTiny = GemmCfg<64, 64, 2, 2, 2>;      // 4 waves, wave tile 32 x 32
+
+constexpr int64_t kCus = 256;
 
 }  // namespace
 
@@ -190,11 +367,23 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_
                        const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    if (M <= 16)
-        return launch_cfg<CfgSkinny>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
-    if (M <= 64)
+    // The largest tile that still gives every CU enough work: one round of the
+    // large tile, 1.5 rounds of the mid tile, two rounds of the small one.  With
+    // fewer tiles the stage loop is bound by load latency, not by the MFMAs, and
+    // more, smaller tiles keep more loads in flight.
+    if (M <= 16) {
+        // About 2048 waves in flight: split K eight ways when there are few row blocks.
+        if ((N + 15) / 16 < 2 * kCus)
+            return launch_skinny<8>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
+        return launch_skinny<4>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
+    }
+    if (tiles_of<CfgLarge>(M, N) >= kCus)
+        return launch_cfg<CfgLarge>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
+    if (tiles_of<CfgMid>(M, N) >= 3 * kCus / 2)
         return launch_cfg<CfgMid>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
-    return launch_cfg<CfgLarge>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
+    if (tiles_of<CfgSmall>(M, N) >= 2 * kCus)
+        return launch_cfg<CfgSmall>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
+    return launch_cfg<CfgTiny>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
 }
 
 }  // namespace bitnet

@@ -174,6 +174,13 @@ FORWARD_FULL_CASES = [
     # matrix-core GEMM
     (5, 512, 256), (16, 4096, 4096), (17, 1000, 4096), (64, 1024, 4096), (100, 333, 192),
     (128, 128, 128), (256, 1024, 4096), (300, 4099, 1024), (1, 70, 65536), (33, 65, 64),
+    # each matrix-core tile size at ragged M, N and K (K not a multiple of the 256-deep stage)
+    (2100, 7000, 192),   # 448 x 128 tiles
+    (1500, 5000, 64),    # 256 x 64 tiles
+    (999, 4100, 320),    # 128 x 64 tiles
+    (200, 900, 4160),    # 64 x 64 tiles
+    (9, 4100, 576),      # skinny, K split over eight waves
+    (16, 9000, 1088),    # skinny, K split over four waves
 ]
 
 
@@ -190,6 +197,8 @@ def test_linear_forward(orc, dev, M, N, K):
 
 FORWARD_SAMPLED_CASES = [
     (2048, 14336, 4096, False),   # prefill FFN up projection
+    (2048, 4096, 4096, False),    # prefill attention projection
+    (1024, 4096, 4096, False),
     (512, 4096, 4096, True),      # H-BitLinear
     (512, 4096, 16384, True),     # H-BitLinear down projection
     (256, 14336, 4096, False),    # Llama-3-8B block gate/up at M = 256
