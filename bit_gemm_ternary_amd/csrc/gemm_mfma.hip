@@ -6,32 +6,34 @@
 // packed weights on the fly (section 추론 최적화 및 커스텀 커널) over tiles held in
 // fast on-chip memory (section 타일링 매트릭스 곱셈).  At prefill sizes the
 // contraction is dense and MFMA-bound, so here it runs on
-// v_mfma_i32_16x16x64_i8 with the weights' offset codes (q + 1, values 0..2)
+// v_mfma_i32_32x32x32_i8 with the weights' offset codes (q + 1, values 0..2)
 // as the A operand and the int8 activations as the B operand; the offset is
-// removed in the epilogue with the per-token code sums.
+// removed in the epilogue with the per-token code sums.  (On gfx950 the
+// 32x32x32 form sustains about 1.7x the int8 rate of 16x16x64 in a pure
+// register loop, 4.8 vs 2.8 POP/s, so the tiles are built from 32x32 blocks.)
 //
 // Tiling.  A workgroup of WN x WM wavefronts computes a BN (weight rows) x BM
-// (tokens) tile, each wave (BN/WN) x (BM/WM) as 16x16 MFMA blocks.  K advances
+// (tokens) tile, each wave (BN/WN) x (BM/WM) as 32x32 MFMA blocks.  K advances
 // in stages of 256: the int8 activation tile (BM rows x 256 B) and the packed
 // weight tile (BN rows x 64 B) are copied straight from HBM/L2 into LDS by
 // buffer_load ... lds (no register staging), double buffered, one barrier per
 // stage.  64 bytes per weight row per stage is the narrowest access that still
 // streams full memory sectors: at 32 bytes per row the weight loads ran at a
-// third of the activation loads' rate.  Large tiles (448 x 128 for big grids)
-// keep the bytes re-read per MFMA low.
+// third of the activation loads' rate.
 //
-// K assignment.  MFMA 16x16x64 takes, per lane, 16 K-values of one A row and
-// the same 16 K-values of one B column; any assignment of K-values to lanes
-// shared by A and B gives the same sum.  Here, in K step ks (0..3) of a stage,
-// lane group g = lane/16 covers the 16 weights of packed word 4g + ks of the
-// stage's 64 words per row (weights 64g + 16ks .. +15).  So one 16-byte LDS read
-// gives a lane its weight words for all four K steps, each unpacked to natural
-// order by (word >> 2i) & 0x03030303; the activation fragment is the matching
-// 16 bytes.  The result D[i][j] sits in lane j + 16*(i/4), element i % 4.
+// K assignment.  MFMA 32x32x32 takes, per lane, 16 K-values of one A row and
+// the same 16 K-values of one B column (lane l: row/column l % 32, half
+// h = l / 32); any assignment of K-values to (half, byte) shared by A and B
+// gives the same sum.  Here, in K step s (0..7) of a stage, half h covers the
+// 16 weights of packed word 8h + s of the stage's 16 words per row (weights
+// 128h + 16s .. +15).  So two 16-byte LDS reads give a lane its weight words for
+// all eight K steps, each unpacked to natural order by (word >> 2i) & 0x03030303;
+// the activation fragment is the matching 16 bytes.  The result D[i][j] sits
+// in lane j + 32 * ((i / 4) % 2), element 4 * (i / 8) + i % 4.
 //
 // LDS layouts (bank-conflict free for the 16-byte fragment reads):
 //   activations: row r of 256 B as 16 segments, segment s stored at s ^ (r & 15);
-//   weights: row r of 64 B as 4 pieces, piece f stored at f ^ ((r >> 2) & 3).
+//   weights: row r of 64 B as 4 pieces, piece f stored at f ^ ((r >> 1) ^ (r >> 3)) & 3.
 // Rows past M or N and the K tail are zero-filled by the buffer loads' range
 // check (the resource covers only the block's valid rows).
 //
@@ -54,22 +56,34 @@ constexpr int kGroupM = 8;                       // token tiles per group in the
 constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9-family raw buffer descriptor word 3
 constexpr uint32_t kOutOfRange = 0x80000000u;    // offset past any block's buffer: loads 0
 
-template <int BN_, int BM_, int WN_, int WM_, int OCC_>
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <int BN_, int BM_, int WN_, int WM_, int OCC_, int S_ = 2>
 struct GemmCfg {
     static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
+    static constexpr int S = S_;                    // LDS stage buffers (S - 1 stages in flight)
     static constexpr int OCC = OCC_;                // workgroups per CU the tile is sized for
     static constexpr int NT = WN * WM * kWave;
     static constexpr int TN = BN / WN, TM = BM / WM;
-    static constexpr int FN = TN / 16, FM = TM / 16;
+    static constexpr int FN = TN / 32, FM = TM / 32;
     static constexpr int X_STAGE = BM * kBK;         // bytes
     static constexpr int W_STAGE = BN * (kBK / 4);   // bytes
     static constexpr int X_SLOTS = BM * 16;          // 16-byte slots per stage
     static constexpr int W_SLOTS = BN * 4;
     static constexpr int XL = (X_SLOTS + NT - 1) / NT;
     static constexpr int WL = (W_SLOTS + NT - 1) / NT;
-    static_assert(TN % 16 == 0 && TM % 16 == 0, "wave tile must be whole MFMA blocks");
+    static constexpr int ROW_F = TN + 4;             // epilogue staging row stride (floats)
+    static_assert((ROW_F / 4) % 2 == 1, "odd number of 16-byte units per staging row");
+    static_assert(WN * WM * 16 * ROW_F * 4 <= S * (X_STAGE + W_STAGE), "epilogue staging fits");
+    static_assert(TN % 32 == 0 && TM % 32 == 0, "wave tile must be whole MFMA blocks");
     static_assert(X_SLOTS % kWave == 0 && W_SLOTS % kWave == 0, "whole waves per load");
-    static_assert(2 * (X_STAGE + W_STAGE) <= 160 * 1024, "LDS");
+    static_assert(S * (X_STAGE + W_STAGE) <= 160 * 1024, "LDS");
+    // With more than one stage in flight the stage barrier counts outstanding
+    // loads, so every wave must issue the same number per stage.
+    static_assert(S == 2 || (X_SLOTS % NT == 0 && W_SLOTS % NT == 0), "uniform loads per wave");
+    static_assert(S >= 2 && (S - 2) * (XL + WL) <= 63, "vmcnt range");
+    static_assert(NT <= 1024, "workgroup size");
 };
 
 __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
@@ -81,12 +95,18 @@ __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
     return r;
 }
 
+// Weight-tile swizzle: piece f of row r is stored at piece f ^ w_swizzle(r).
+// Any 8 consecutive rows (and any 16 rows of a 16-row block) then hit distinct
+// 16-byte bank groups when a lane group reads the same piece of each row.
+__device__ __forceinline__ int w_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
 // All of this wave's loads into LDS have landed and its LDS reads are done,
 // then the workgroup barrier.  Written as one asm statement with a memory
 // clobber so the compiler neither moves LDS accesses across it nor adds a
 // wait of its own for loads still in flight elsewhere.
+template <int N>
 __device__ __forceinline__ void stage_barrier() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <class C>
@@ -94,7 +114,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     const int8_t* __restrict__ X, const uint8_t* __restrict__ P, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_qsum, const float* __restrict__ w_scale, int M, int N, int K,
     int vec_store, float* __restrict__ y, int32_t* __restrict__ acc_out) {
-    __shared__ __align__(16) int8_t lds[2][C::X_STAGE + C::W_STAGE];
+    __shared__ __align__(16) int8_t lds[C::S][C::X_STAGE + C::W_STAGE];
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
@@ -126,13 +146,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(P + n0 * row_bytes), (short)0, w_rows * row_bytes, (int)kBufferWord3);
 
-    // Copy one stage into LDS buffer `buf`.  Each load instruction moves 1 KiB:
-    // lane l of the wave fills the 16-byte slot base + l, so the global address
-    // each lane reads is chosen to realise the swizzled layout.
-    auto issue = [&](int buf, int k0) {
-#pragma unroll
-        for (int i = 0; i < C::XL; ++i) {
-            const int base = i * C::NT + wave * kWave;   // wave-uniform
+    // Copy one stage into LDS buffer `buf`: load instruction idx (0 .. XL + WL - 1)
+    // of this wave moves 1 KiB; lane l of the wave fills the 16-byte slot
+    // base + l, so the global address each lane reads is chosen to realise the
+    // swizzled layout.
+    constexpr int kLoads = C::XL + C::WL;
+    auto issue_one = [&](int buf, int k0, int idx) {
+        if (idx < C::XL) {
+            const int base = idx * C::NT + wave * kWave;   // wave-uniform
             if (base < C::X_SLOTS) {
                 const int p = base + lane;
                 const int r = p >> 4, s = (p & 15) ^ (r & 15);
@@ -141,13 +162,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)&lds[buf][base * 16], 16,
                                                          (int)off, 0, 0, 0);
             }
-        }
-#pragma unroll
-        for (int i = 0; i < C::WL; ++i) {
-            const int base = i * C::NT + wave * kWave;
+        } else {
+            const int base = (idx - C::XL) * C::NT + wave * kWave;
             if (base < C::W_SLOTS) {
                 const int p = base + lane;
-                const int r = p >> 2, f = (p & 3) ^ ((r >> 2) & 3);
+                const int r = p >> 2, f = (p & 3) ^ w_swizzle(r);
                 const int k = k0 + 64 * f;
                 const uint32_t off = k < K ? (uint32_t)(r * row_bytes + k / 4) : kOutOfRange;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -156,79 +175,142 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
         }
     };
 
-    v4i acc[C::FN][C::FM];
+    v16i acc[C::FN][C::FM];
 #pragma unroll
     for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-    const int fr = lane % 16, fg = lane / 16;
-    auto compute = [&](int buf) {
+    const int fr = lane % 32, fh = lane / 32;
+    // One stage of MFMAs on LDS buffer `buf`; the loads of a later stage (into
+    // buffer `nbuf`) are issued during the first four of the eight K steps, so
+    // the address unit works while the matrix cores do (instead of every wave
+    // issuing all its loads at once after the barrier) and the loads still have
+    // the rest of the stage to land.
+    auto compute = [&](int buf, bool has_next, int nbuf, int next_k0) {
         const int8_t* xs = &lds[buf][0];
         const int8_t* ws = &lds[buf][C::X_STAGE];
-        v4u wv[C::FN];
+        v4u wv[C::FN][2];
 #pragma unroll
         for (int i = 0; i < C::FN; ++i) {
-            const int r = wn * C::TN + i * 16 + fr;
-            wv[i] = *reinterpret_cast<const v4u*>(&ws[r * 64 + 16 * (fg ^ ((r >> 2) & 3))]);
+            const int r = wn * C::TN + i * 32 + fr;
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+                wv[i][p] = *reinterpret_cast<const v4u*>(
+                    &ws[r * 64 + 16 * ((2 * fh + p) ^ w_swizzle(r))]);
         }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int st = 0; st < 8; ++st) {
             v4i b[C::FM];
 #pragma unroll
             for (int j = 0; j < C::FM; ++j) {
-                const int r = wm * C::TM + j * 16 + fr;
-                b[j] = *reinterpret_cast<const v4i*>(&xs[r * kBK + 16 * ((4 * fg + ks) ^ (r & 15))]);
+                const int r = wm * C::TM + j * 32 + fr;
+                b[j] = *reinterpret_cast<const v4i*>(&xs[r * kBK + 16 * ((8 * fh + st) ^ (r & 15))]);
+            }
+            if (has_next) {
+#pragma unroll
+                for (int idx = 0; idx < kLoads; ++idx)
+                    if (idx * 4 / kLoads == st) issue_one(nbuf, next_k0, idx);
             }
 #pragma unroll
             for (int i = 0; i < C::FN; ++i) {
-                const v4i a = unpack_codes(wv[i][ks]);
+                const v4i a = unpack_codes(wv[i][st / 4][st % 4]);
 #pragma unroll
                 for (int j = 0; j < C::FM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j], acc[i][j], 0, 0, 0);
             }
         }
     };
 
     const int nk = (K + kBK - 1) / kBK;
-    issue(0, 0);
+#pragma unroll
+    for (int sp = 0; sp < C::S - 1; ++sp) {
+        if (sp < nk) {
+#pragma unroll
+            for (int idx = 0; idx < kLoads; ++idx) issue_one(sp, sp * kBK, idx);
+        }
+    }
     for (int kt = 0; kt < nk; ++kt) {
-        stage_barrier();                       // stage kt landed; buffer (kt+1)&1 is free
-        if (kt + 1 < nk) issue((kt + 1) & 1, (kt + 1) * kBK);
-        compute(kt & 1);
+        // Stage kt has landed once at most the loads of the stages issued after
+        // it are outstanding; every wave has finished reading buffer
+        // (kt - 1) % S, which the loads of stage kt + S - 1 overwrite.
+        if (kt + C::S - 2 < nk)
+            stage_barrier<(C::S - 2) * kLoads>();
+        else
+            stage_barrier<0>();
+        const int ahead = kt + C::S - 1;
+        compute(kt % C::S, ahead < nk, ahead % C::S, ahead * kBK);
     }
 
-    // Epilogue: D[n][m] -> y[m][n]; lane holds n = 4*(lane/16) + e, m = lane % 16.
+    // Epilogue.  D[n][m] of a 32x32 block sits in lane m + 32 * ((n / 4) % 2),
+    // element 4 * (n / 8) + n % 4: a lane holds four runs of 4 consecutive
+    // outputs of one token, so direct stores would each cover 32 rows of y with
+    // 16 bytes.  Instead each wave dequantises 16 tokens at a time into its own
+    // LDS region (row stride TN + 4 floats keeps the 16-byte writes conflict
+    // free) and writes them back as whole row segments of TN floats.
     const float d_w = w_scale[0];
+    __syncthreads();   // every wave is done with the stage buffers
+    float* stage = reinterpret_cast<float*>(&lds[0][0]) + wave * 16 * C::ROW_F;
+    constexpr int PPR = C::TN / 4;              // 16-byte pieces per row segment
+    constexpr int RPI = kWave / PPR;            // row segments per store instruction
+    static_assert(RPI >= 1 && 16 % RPI == 0, "row segments per store");
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) {
-        const int64_t m = m0 + wm * C::TM + j * 16 + fr;
-        if (m >= M) continue;
-        const int32_t qs = x_qsum[m];
-        const float sx = x_scale[m];
 #pragma unroll
-        for (int i = 0; i < C::FN; ++i) {
-            const int64_t nb = n0 + wn * C::TN + i * 16 + 4 * fg;
-            if (nb >= N) continue;
-            if (vec_store && nb + 3 < N) {
-                const v4i a = acc[i][j] - v4i{qs, qs, qs, qs};
-                if (acc_out != nullptr) *reinterpret_cast<v4i*>(&acc_out[m * N + nb]) = a;
-                float4 v;
-                v.x = ((float)a[0] * sx) * d_w;
-                v.y = ((float)a[1] * sx) * d_w;
-                v.z = ((float)a[2] * sx) * d_w;
-                v.w = ((float)a[3] * sx) * d_w;
-                *reinterpret_cast<float4*>(&y[m * N + nb]) = v;
-            } else {
+        for (int half = 0; half < 2; ++half) {
+            const int64_t mr = m0 + wm * C::TM + j * 32 + half * 16;   // first token staged
+            if (fr / 16 == half) {
+                const int64_t m = mr + fr % 16;
+                const int32_t qs = m < M ? x_qsum[m] : 0;
+                const float sx = m < M ? x_scale[m] : 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (nb + e < N) {
-                        const int a = acc[i][j][e] - qs;
-                        if (acc_out != nullptr) acc_out[m * N + nb + e] = a;
-                        y[m * N + nb + e] = ((float)a * sx) * d_w;
+                for (int i = 0; i < C::FN; ++i) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int nl = i * 32 + 8 * q + 4 * fh;   // wave-local output column
+                        const v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                          acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]} -
+                                      v4i{qs, qs, qs, qs};
+                        float4 v;
+                        v.x = ((float)a[0] * sx) * d_w;
+                        v.y = ((float)a[1] * sx) * d_w;
+                        v.z = ((float)a[2] * sx) * d_w;
+                        v.w = ((float)a[3] * sx) * d_w;
+                        *reinterpret_cast<float4*>(&stage[(fr % 16) * C::ROW_F + nl]) = v;
+                        if (acc_out != nullptr && m < M) {
+                            const int64_t nb = n0 + wn * C::TN + nl;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (nb + e < N) acc_out[m * N + nb + e] = a[e];
+                        }
                     }
                 }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int rr = 0; rr < 16; rr += RPI) {
+                const int row = rr + lane / PPR, piece = lane % PPR;
+                const int64_t m = mr + row;
+                const int64_t nb = n0 + wn * C::TN + 4 * piece;
+                if (lane < RPI * PPR && m < M && nb < N) {
+                    const float4 v =
+                        *reinterpret_cast<const float4*>(&stage[row * C::ROW_F + 4 * piece]);
+                    if (vec_store && nb + 3 < N) {
+                        // Streaming store: y is written once and not re-read by this
+                        // kernel, so it should not displace operand lines in L2.
+                        __builtin_nontemporal_store(f4{v.x, v.y, v.z, v.w},
+                                                    reinterpret_cast<f4*>(&y[m * N + nb]));
+                    } else {
+                        const float ve[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (nb + e < N) y[m * N + nb + e] = ve[e];
+                    }
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
     }
 }
@@ -353,11 +435,11 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_q
                          acc);
 }
 
-// Tile configurations (weight rows x tokens, waves, workgroups per CU).
-using CfgLarge = GemmCfg<448, 128, 4, 2, 1>;   // 8 waves, wave tile 112 x 64, 120 KiB LDS
-using CfgMid = GemmCfg<256, 64, 4, 1, 2>;      // 4 waves, wave tile 64 x 64
-using CfgSmall = GemmCfg<128, 64, 2, 2, 2>;    // 4 waves, wave tile 64 x 32
-using CfgTiny = GemmCfg<64, 64, 2, 2, 2>;      // 4 waves, wave tile 32 x 32
+// Tile configurations (weight rows x tokens, waves along N x along M,
+// workgroups per CU).
+using CfgLarge = GemmCfg<448, 128, 7, 2, 1>;   // 14 waves, wave tile 64 x 64, 120 KiB LDS
+using CfgMid = GemmCfg<256, 128, 4, 2, 1>;     // 8 waves, wave tile 64 x 64, 96 KiB LDS
+using CfgTiny = GemmCfg<64, 64, 2, 2, 2>;      // 4 waves, wave tile 32 x 32, 40 KiB LDS
 
 constexpr int64_t kCus = 256;
 
@@ -367,22 +449,20 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_
                        const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    // The largest tile that still gives every CU enough work: one round of the
-    // large tile, 1.5 rounds of the mid tile, two rounds of the small one.  With
-    // fewer tiles the stage loop is bound by load latency, not by the MFMAs, and
-    // more, smaller tiles keep more loads in flight.
     if (M <= 16) {
         // About 2048 waves in flight: split K eight ways when there are few row blocks.
         if ((N + 15) / 16 < 2 * kCus)
             return launch_skinny<8>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
         return launch_skinny<4>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
     }
-    if (tiles_of<CfgLarge>(M, N) >= kCus)
+    // The largest tile that still gives every CU enough work: two rounds of the
+    // large tile, one of the mid tile.  With fewer tiles the stage loop is bound
+    // by load latency, not by the matrix cores, and more, smaller tiles keep
+    // more loads in flight (measured on the prefill and Llama-block shapes).
+    if (tiles_of<CfgLarge>(M, N) >= 2 * kCus)
         return launch_cfg<CfgLarge>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
-    if (tiles_of<CfgMid>(M, N) >= 3 * kCus / 2)
+    if (tiles_of<CfgMid>(M, N) >= kCus)
         return launch_cfg<CfgMid>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
-    if (tiles_of<CfgSmall>(M, N) >= 2 * kCus)
-        return launch_cfg<CfgSmall>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
     return launch_cfg<CfgTiny>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
 }
 

@@ -36,7 +36,12 @@ namespace {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvWaves = kGemvThreads / kWave;
-constexpr int kMaxXRegsChunks = 8;  // MT * CH limit: 16 * MT * CH activation VGPRs
+constexpr int kMaxXRegsChunks = 8;
+// Fused decode launch shape: 256-thread workgroups, about 1024 waves in all
+// (measured on the decode projections against 512- and 1024-thread
+// workgroups and 2048 or 4096 waves).
+constexpr int kFusedThreads = 256;
+constexpr int kFusedWaves = 1024;  // MT * CH limit: 16 * MT * CH activation VGPRs
 
 // Sum of v over the 64 lanes, returned wave-uniform.  Four DPP steps give every
 // lane the sum of its 16-lane row; the four row sums are read out to scalars.
@@ -47,6 +52,46 @@ __device__ __forceinline__ int wave_sum_dpp(int v) {
     v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
     return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
            __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// Lane-to-lane moves within 16-lane rows (DPP), for 32- and 64-bit values.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ float read_lane(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double read_lane(double v, int l) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Wave-uniform max / sum over the 64 lanes, reduced within each 16-lane row by
+// DPP and then over the four rows; the combination order is fixed, so the
+// double sum is deterministic.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_move<0xB1>(v));
+    v = fmaxf(v, dpp_move<0x4E>(v));
+    v = fmaxf(v, dpp_move<0x141>(v));
+    v = fmaxf(v, dpp_move<0x140>(v));
+    return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
+}
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+    v += dpp_move<0xB1>(v);
+    v += dpp_move<0x4E>(v);
+    v += dpp_move<0x141>(v);
+    v += dpp_move<0x140>(v);
+    return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
@@ -85,9 +130,11 @@ struct GemvCore {
     // (r + rb - row0) of my_acc.
     __device__ static __forceinline__ void compute(const uint4 (&w)[RB][CH],
                                                    const uint32_t (&xv)[MT][CH][16], int64_t r,
-                                                   int64_t row0, int lane, int (&my_acc)[MT]) {
+                                                   int64_t row0, int64_t row1, int lane,
+                                                   int (&my_acc)[MT]) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+            if (r + rb >= row1) break;  // wave-uniform: the batch's last rows may be past row1
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
@@ -116,7 +163,7 @@ struct GemvCore {
                                                int (&my_acc)[MT]) {
         for (int64_t r = row0; r < row1; r += RB) {
             if (r != row0) load(w, packed, row_bytes, nchunk, r, row1, lane);
-            compute(w, xv, r, row0, lane, my_acc);
+            compute(w, xv, r, row0, row1, lane, my_acc);
         }
     }
 
@@ -193,23 +240,24 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 // stay in flight through the prologue.  The prologue needs one workgroup
 // reduction (absmax and sum of squares of every token together); each wave
 // then sums the codes it reads back from LDS itself.
-template <int MT, int CH>
-__global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
+template <int MT, int CH, int NT>
+__global__ __launch_bounds__(NT) void fused_decode_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
     const uint8_t* __restrict__ packed, const float* __restrict__ w_scale, int N, int K,
     int rows_per_wave, float* __restrict__ y, int8_t* __restrict__ xq_out,
     float* __restrict__ x_scale_out, int32_t* __restrict__ x_qsum_out,
     int32_t* __restrict__ acc_out) {
     using G = GemvCore<MT, CH>;
-    constexpr int XV = 2 * CH;  // 8-value bf16 vectors per thread per token (K <= CH*4096)
+    constexpr int NW = NT / kWave;
+    constexpr int XV = (CH * 512 + NT - 1) / NT;  // 8-value bf16 vectors per thread per token (K <= CH*4096)
     __shared__ __align__(16) int8_t codes[MT][CH * 4096];
-    __shared__ float red_f[MT][kGemvWaves];
-    __shared__ double red_d[MT][kGemvWaves];
+    __shared__ float red_f[MT][NW];
+    __shared__ double red_d[MT][NW];
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
     const int wave_id = t / kWave;
-    const int64_t row0 = ((int64_t)blockIdx.x * kGemvWaves + wave_id) * rows_per_wave;
+    const int64_t row0 = ((int64_t)blockIdx.x * NW + wave_id) * rows_per_wave;
     const int64_t row1 = min((int64_t)N, row0 + rows_per_wave);
     const int nchunk = K / 64;
     const int64_t row_bytes = K / 4;
@@ -222,7 +270,7 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
         const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)tok * K);
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
-            const int v = t + kGemvThreads * i;
+            const int v = t + NT * i;
             raw[tok][i] = v < nvec ? xr[v] : make_uint4(0, 0, 0, 0);
         }
     }
@@ -251,7 +299,7 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
         double ss = 0.0;
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
-            const int v = t + kGemvThreads * i;
+            const int v = t + NT * i;
             if (v < nvec) {
                 float u[8];
                 values(tok, i, v, u, false);
@@ -262,8 +310,8 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
                 for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(u[e]));
             }
         }
-        amax = wave_max(amax);
-        ss = wave_sum(ss);
+        amax = wave_max_dpp(amax);
+        ss = wave_sum_dpp(ss);
         if (lane == 0) {
             red_f[tok][wave_id] = amax;
             red_d[tok][wave_id] = ss;
@@ -271,24 +319,21 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
     }
     __syncthreads();
 
-    // 3. Codes into LDS; every thread derives the same scales.
-    float tok_scale[MT];
+    // 3. Codes into LDS; every thread derives the same scales.  The dequant
+    // factor (which needs a double square root and division) is only computed
+    // in the epilogue, off the path to the contraction.
+    float tok_amax[MT];
 #pragma unroll
     for (int tok = 0; tok < MT; ++tok) {
         float amax = red_f[tok][0];
-        double ss = red_d[tok][0];
 #pragma unroll
-        for (int wv = 1; wv < kGemvWaves; ++wv) {
-            amax = fmaxf(amax, red_f[tok][wv]);
-            ss += red_d[tok][wv];
-        }
+        for (int wv = 1; wv < NW; ++wv) amax = fmaxf(amax, red_f[tok][wv]);
+        tok_amax[tok] = amax;
         const bool zero = amax < kTinyAbsmax;
         const float scale = zero ? 0.f : 127.0f / amax;
-        const double rstd = 1.0 / sqrt(ss / (double)K + (double)eps);
-        tok_scale[tok] = zero ? 0.f : (float)(((double)amax * rstd) / 127.0);
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
-            const int v = t + kGemvThreads * i;
+            const int v = t + NT * i;
             if (v < nvec) {
                 float u[8];
                 values(tok, i, v, u, true);
@@ -332,13 +377,20 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
         tok_sum[tok] = wave_sum_dpp(part);
     }
 
+    auto dequant_scale = [&](int tok) {
+        double ss = red_d[tok][0];
+#pragma unroll
+        for (int wv = 1; wv < NW; ++wv) ss += red_d[tok][wv];
+        const double rstd = 1.0 / sqrt(ss / (double)K + (double)eps);
+        return tok_amax[tok] < kTinyAbsmax ? 0.f : (float)(((double)tok_amax[tok] * rstd) / 127.0);
+    };
     if (blockIdx.x == 0) {
         for (int tok = 0; tok < MT; ++tok) {
-            for (int v = t; v < K / 16; v += kGemvThreads)
+            for (int v = t; v < K / 16; v += NT)
                 reinterpret_cast<uint4*>(xq_out + (int64_t)tok * K)[v] =
                     reinterpret_cast<const uint4*>(codes[tok])[v];
             if (t == 0) {
-                x_scale_out[tok] = tok_scale[tok];
+                x_scale_out[tok] = dequant_scale(tok);
                 x_qsum_out[tok] = tok_sum[tok];
             }
         }
@@ -349,6 +401,9 @@ __global__ __launch_bounds__(kGemvThreads) void fused_decode_kernel(
 #pragma unroll
     for (int tok = 0; tok < MT; ++tok) my_acc[tok] = 0;
     G::run(w, xv, packed, row_bytes, nchunk, row0, row1, lane, my_acc);
+    float tok_scale[MT];
+#pragma unroll
+    for (int tok = 0; tok < MT; ++tok) tok_scale[tok] = dequant_scale(tok);
     G::store(my_acc, tok_scale, tok_sum, w_scale, N, row0, row1, lane, y, acc_out);
 }
 
@@ -391,13 +446,14 @@ struct Standalone {
 
 template <int MT, int CH>
 struct Fused {
+    static constexpr int NT = kFusedThreads;
     static hipError_t run(const Args& a) {
-        // Every workgroup repeats the quantisation, so fewer, fuller
-        // workgroups than the standalone kernel: about 1024 waves.
-        const int64_t rpw = rows_per_wave(a.N, 1024);
-        const int64_t blocks = ((a.N + rpw - 1) / rpw + kGemvWaves - 1) / kGemvWaves;
-        return launch_kernel((fused_decode_kernel<MT, CH>), dim3((unsigned)blocks),
-                             dim3(kGemvThreads), 0, a.stream, a.x, a.gain, a.eps, a.packed,
+        // Every workgroup repeats the quantisation, so about one workgroup
+        // per CU; its prologue is split over NT threads.
+        const int64_t rpw = rows_per_wave(a.N, kFusedWaves);
+        const int64_t blocks = ((a.N + rpw - 1) / rpw + NT / kWave - 1) / (NT / kWave);
+        return launch_kernel((fused_decode_kernel<MT, CH, NT>), dim3((unsigned)blocks),
+                             dim3(NT), 0, a.stream, a.x, a.gain, a.eps, a.packed,
                              a.w_scale, (int)a.N, (int)a.K, (int)rpw, a.y, a.xq_out,
                              a.x_scale_out, a.x_qsum_out, a.acc);
     }

@@ -175,10 +175,10 @@ FORWARD_FULL_CASES = [
     (5, 512, 256), (16, 4096, 4096), (17, 1000, 4096), (64, 1024, 4096), (100, 333, 192),
     (128, 128, 128), (256, 1024, 4096), (300, 4099, 1024), (1, 70, 65536), (33, 65, 64),
     # each matrix-core tile size at ragged M, N and K (K not a multiple of the 256-deep stage)
-    (2100, 7000, 192),   # 448 x 128 tiles
-    (1500, 5000, 64),    # 256 x 64 tiles
-    (999, 4100, 320),    # 128 x 64 tiles
-    (200, 900, 4160),    # 64 x 64 tiles
+    (2100, 14000, 192),  # 448 x 128 tiles
+    (2000, 4100, 64),    # 256 x 128 tiles
+    (999, 4100, 320),    # 64 x 64 tiles
+    (200, 900, 4160),    # 64 x 64 tiles, long K
     (9, 4100, 576),      # skinny, K split over eight waves
     (16, 9000, 1088),    # skinny, K split over four waves
 ]
