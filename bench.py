@@ -12,18 +12,23 @@ streams its weights from HBM.  Steps are replayed from HIP graphs (one graph per
 rotation copy and one per full rotation), so the timed region measures the GPU,
 not Python launch overhead.
 
-  value            packed weight bytes per step / step time (GB/s)
+  value            packed weight bytes per step / step time (GB/s); config also
+                   gives it as a fraction of a plain 2 GiB device read (torch sum)
+                   and the warm number (one weight copy, Infinity-Cache resident)
   roofline         the fused decode kernel alone: algorithmic bytes (packed
                    weights, bf16 activations, codes and outputs) per launch /
                    average kernel duration, from HIP events that the kernel's
                    own dispatch stamps (hipExtLaunchKernelGGL), on its stream
   prefill          W1.58A8 prefill M=2048, K=4096, N=14336: int8 TOPS of the
-                   matrix-core GEMM against the dense int8 peak
+                   matrix-core GEMM against the dense int8 peak, and against that
+                   peak scaled to the engine clock measured during the kernel
+                   (committed counter summary)
   hadamard         H-BitLinear M=512: FWHT + int4 quantisation GB/s and GEMM TOPS
   block            the seven BitLinear projections of a Llama-3-8B block at
                    M = 1, 16 and 256 tokens: time per block, packed weight GB/s,
                    int TOPS
-  cpu_baseline     the CPU oracle on this host running the same decode step
+  cpu_baseline     the CPU oracle on this host running the same decode step, on
+                   all cores and on one core
 
 roofline.traffic is the HBM bytes per launch of the fused decode kernel that
 rocprofv3's FETCH_SIZE and WRITE_SIZE counters read, scaled by what the same
@@ -51,6 +56,7 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix-core peak, 5.0 POP/s
+PEAK_CLOCK_GHZ = 2.4        # the engine clock that peak is quoted at
 ROTATE_BYTES = 1 << 30      # > 4 x the 256 MB Infinity Cache
 METRIC = "BitLinear decode GEMV weight GB/s (%HBM peak); prefill int8 TOPS (%MFMA peak)"
 
@@ -73,30 +79,37 @@ def parse_args():
     ap.add_argument("--block-steps", type=int, default=200, help="timed steps per token count of the block leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES, ten times (HBM counter calibration)")
+    ap.add_argument("--legs", default="decode,prefill,hadamard,block",
+                    help="comma-separated legs to run (the headline needs decode)")
+    ap.add_argument("--cpu-one-core-seconds", type=float, default=5.0,
+                    help="wall time budget of the one-core CPU-oracle sample")
     return ap.parse_args()
 
 
 COPY_BYTES = 256 << 20
+READ_REF_BYTES = 2 << 30
+CSRC = os.path.join(ROOT, "bit_gemm_ternary_amd", "csrc")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_decode_kernel.decode_M1.hbm_traffic.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_gemm_ternary_amd", "csrc", f)
-                  for f in ("gemv.hip", "common.hpp")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("gemv.hip", "common.hpp")]
+GEMM_SUMMARY = os.path.join(ROOT, "profiles", "gemm_kernel.prefill_M2048_K4096_N14336.counters.md")
+GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "common.hpp")]
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(paths=None) -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in paths or KERNEL_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per step of the fused decode kernels from the committed counter
-    summary, or None if there is none or the kernel source has changed since."""
+def summary_data(path, sources):
+    """The bench-data line of a committed counter summary, or None if there is
+    none or the kernel source has changed since the counters were taken."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(path) as f:
             for line in f:
                 if line.startswith("bench-data: "):
                     data = json.loads(line[len("bench-data: "):])
@@ -105,9 +118,35 @@ def measured_traffic():
                 return None
     except OSError:
         return None
-    if data.get("source_sha256") != kernel_source_digest():
+    if data.get("source_sha256") != kernel_source_digest(sources):
         return None
     return data
+
+
+def measured_traffic():
+    """HBM bytes per step of the fused decode kernels (committed counter summary)."""
+    return summary_data(TRAFFIC_SUMMARY, KERNEL_SOURCES)
+
+
+def hbm_stream_reference(torch):
+    """GB/s of a plain device copy of 1 GiB (torch copy_, read + write bytes
+    counted): the streaming rate a simple kernel reaches on this GPU."""
+    src = torch.ones(READ_REF_BYTES // 8, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    n = 10
+    for _ in range(n):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    gbs = 2 * src.numel() * 4 * n / (start.elapsed_time(end) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
 
 
 def copy_calibration(torch):
@@ -254,6 +293,10 @@ def decode_bench(args, dev, bt, torch, synth):
 
     run_steps = graph_runner(step, copies, args.eager, torch)
     ms_per_step, wall_s = timed(run_steps, args.steps, torch)
+    # Warm reference: the same steps on one weight copy, which then stays
+    # resident in the 256 MB Infinity Cache (and partly in L2).
+    warm_run = graph_runner(lambda r: step(0), 1, args.eager, torch)
+    warm_ms, _ = timed(warm_run, min(args.steps, 500), torch)
 
     # Per-kernel durations: the same steps again, launched eagerly with the
     # kernel-timing hook armed before every launch, so each event pair is
@@ -282,6 +325,7 @@ def decode_bench(args, dev, bt, torch, synth):
         "wall_s": wall_s, "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "kernel_bytes": kernel_bytes, "kernel_us": kernel_us, "per_layer": per_layer,
         "instrumented_steps": n_instr, "layers": layers,
+        "warm_value": step_bytes / (warm_ms * 1e-3) / 1e9,
     }
 
 
@@ -320,11 +364,19 @@ def prefill_bench(args, dev, bt, torch, synth):
     gemm_us = time_launches(gemm, args.prefill_iters, bt)
     tops = 2.0 * M * N * K / (gemm_us * 1e-6) / 1e12
     quant_bytes = M * K * 2 + M * K + 8 * M
+    counters = summary_data(GEMM_SUMMARY, GEMM_SOURCES)
+    # Engine clock of this run: the kernel's cycles per CU (counter summary)
+    # over its measured duration.
+    clock = None if counters is None else round(counters["cu_cycles_per_launch"] / (gemm_us * 1e3), 3)
     return {
         "workload": f"W1.58A8 prefill M={M} K={K} N={N} (FFN up)",
         "gemm_us": round(gemm_us, 2), "TOPS": round(tops, 1),
         "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS,
-                     "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4)},
+                     "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
+                     "traffic": None if counters is None else counters["hbm_bytes_per_launch"],
+                     "clock_ghz_measured": clock,
+                     "frac_at_measured_clock": None if clock is None else
+                     round(tops / (INT8_PEAK_TOPS * clock / PEAK_CLOCK_GHZ), 4)},
         "quant_us": round(quant_us, 2), "quant_GB_s": round(quant_bytes / quant_us / 1e3, 1),
         "step_ms": round((gemm_us + quant_us) / 1e3, 4),
     }
@@ -415,10 +467,26 @@ def cpu_baseline(args, synth):
         el = time.perf_counter() - t0
         if el >= args.cpu_seconds:
             break
-    return {"value": round(step_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
-            "kind": "oracle",
-            "sample": f"{n} decode steps (int8 quant + int32 contraction + dequant of the three "
-                      f"M=1 projections) in {el:.1f} s on {os.cpu_count()} host CPUs"}
+    all_cores = orc.num_threads()
+    out = {"value": round(step_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": all_cores,
+           "kind": "oracle",
+           "sample": f"{n} decode steps (int8 quant + int32 contraction + dequant of the three "
+                     f"M=1 projections) in {el:.1f} s on {os.cpu_count()} host CPUs"}
+    # The same steps on one core.
+    orc.set_num_threads(1)
+    try:
+        n1, t0 = 0, time.perf_counter()
+        while True:
+            step()
+            n1 += 1
+            el1 = time.perf_counter() - t0
+            if el1 >= args.cpu_one_core_seconds:
+                break
+    finally:
+        orc.set_num_threads(all_cores)
+    out["one_core"] = {"value": round(step_bytes * n1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                       "sample": f"{n1} decode steps in {el1:.1f} s"}
+    return out
 
 
 def main():
@@ -444,22 +512,32 @@ def main():
     torch.cuda.set_device(dev)
     bt.lib()
 
+    legs = set(args.legs.split(","))
+    secondary = {}
+    if "decode" not in legs:
+        # Secondary legs only (used for per-kernel counter runs); no headline line.
+        for name, fn in (("prefill", prefill_bench), ("hadamard", hadamard_bench),
+                         ("block", block_bench)):
+            if name in legs:
+                secondary[name] = fn(args, dev, bt, torch, synth)
+                torch.cuda.empty_cache()
+        print(json.dumps(secondary), flush=True)
+        return
+
     dec = decode_bench(args, dev, bt, torch, synth)
     log(f"decode: {dec['ms_per_step'] * 1e3:.2f} us/step, {dec['value']:.1f} GB/s; "
         f"GEMV kernels {dec['per_layer']}")
     del dec["layers"]
     torch.cuda.empty_cache()
+    stream_ref = hbm_stream_reference(torch)
 
-    secondary = {}
     if not args.no_secondary:
-        secondary["prefill"] = prefill_bench(args, dev, bt, torch, synth)
-        log(f"prefill: {secondary['prefill']}")
-        torch.cuda.empty_cache()
-        secondary["hadamard"] = hadamard_bench(args, dev, bt, torch, synth)
-        log(f"hadamard: {secondary['hadamard']}")
-        torch.cuda.empty_cache()
-        secondary["block"] = block_bench(args, dev, bt, torch, synth)
-        log(f"block: {secondary['block']}")
+        for name, fn in (("prefill", prefill_bench), ("hadamard", hadamard_bench),
+                         ("block", block_bench)):
+            if name in legs:
+                secondary[name] = fn(args, dev, bt, torch, synth)
+                log(f"{name}: {secondary[name]}")
+                torch.cuda.empty_cache()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, synth)
 
@@ -488,6 +566,9 @@ def main():
             "weight_rotation_copies": dec["copies"],
             "launch": "eager" if args.eager else "hip graphs",
             "frac_hbm_peak": round(dec["value"] / HBM_PEAK_GBS, 4),
+            "hbm_copy_reference_GB_s": stream_ref,
+            "frac_of_copy_reference": round(dec["value"] / stream_ref, 4),
+            "warm_value_GB_s": round(dec["warm_value"], 1),
         },
         "roofline": {
             "bound": "hbm",

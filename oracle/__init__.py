@@ -40,6 +40,8 @@ def load(path: str):
     p, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     lib.oracle_version.restype = i32
     lib.oracle_num_threads.restype = i32
+    lib.oracle_set_num_threads.argtypes = [i32]
+    lib.oracle_set_num_threads.restype = None
     lib.oracle_unpack_weights.argtypes = [p, i64, i64, p]
     lib.oracle_unpack_weights.restype = i64
     lib.oracle_fwht_f32.argtypes = [p, i64]
@@ -76,6 +78,10 @@ class Oracle:
     def num_threads(self) -> int:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """Thread count of the oracle's later calls (for one-core timings)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     def unpack_weights(self, packed: np.ndarray, K: int) -> np.ndarray:
         packed = _c(packed, np.uint8)

@@ -59,6 +59,9 @@ int oracle_version(void) { return ORACLE_VERSION; }
 /* Threads the OpenMP loops below use (for reporting CPU timings). */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Sets the thread count of later calls (n >= 1), for one-core timings. */
+void oracle_set_num_threads(int n) { omp_set_num_threads(n < 1 ? 1 : n); }
+
 /* bfloat16 bits -> float32 (exact: bf16 is the top half of a float32). */
 static float bf16_bits_to_float(uint16_t h) {
     uint32_t u = ((uint32_t)h) << 16;
