@@ -410,36 +410,66 @@ def hadamard_bench(args, dev, bt, torch, synth):
     return out
 
 
+class GroupedLayer:
+    """Projections sharing one input (q|k|v or gate|up) stacked row-wise, run
+    with one bitnet_bitlinear_forward_grouped call per step."""
+
+    def __init__(self, members, copies, dev, torch):
+        # members: [(DecodeLayer, ...)] sharing the first member's input
+        first = members[0]
+        self.x = first.x
+        self.codes = first.codes
+        self.rows = [m.layer.N for m in members]
+        self.packed = [torch.cat([m.packed[r] for m in members]) for r in range(copies)]
+        self.w_scales = torch.stack([m.w_scale for m in members])
+        M = first.layer.M
+        self.y = torch.empty((M, sum(self.rows)), dtype=torch.float32, device=dev)
+
+    def forward(self, bt, r):
+        bt.bitlinear_forward_grouped(self.x, self.packed[r], self.w_scales, self.rows, None, 1e-5,
+                                     out=self.y, codes=self.codes)
+
+
 def block_bench(args, dev, bt, torch, synth):
     """The seven projections of a Llama-3-8B block, each RMSNorm + quantisation +
-    contraction + dequantisation through bitnet_bitlinear_forward, at M = 1, 16
-    and 256 tokens; weights rotate over > 1 GiB of copies as in the decode leg."""
+    contraction + dequantisation, at M = 1, 16 and 256 tokens; weights rotate
+    over > 1 GiB of copies as in the decode leg.  Timed twice: seven separate
+    bitnet_bitlinear_forward calls, and four calls with q|k|v and gate|up
+    grouped (bitnet_bitlinear_forward_grouped: one quantisation and one launch
+    per shared input)."""
     spec = synth.workload("block", M=1)
     block_bytes = sum(l.N * l.K // 4 for l in spec)
     copies = max(1, math.ceil(ROTATE_BYTES / block_bytes))
     packed = [packed_copies(l, copies, dev, bt, torch) for l in spec]
+    names = [l.name for l in spec]
     out = []
     for M in (1, 16, 256):
         layers = [DecodeLayer(l, copies, dev, bt, torch, packed=p)
                   for l, p in zip(synth.workload("block", M=M), packed)]
-
-        def step(r, layers=layers):
-            for L in layers:
-                L.forward(bt, r)
-
-        for s in range(min(args.warmup, 2 * copies)):
-            step(s % copies)
-        torch.cuda.synchronize()
-        run = graph_runner(step, copies, args.eager, torch)
-        ms, _ = timed(run, args.block_steps, torch)
+        by = dict(zip(names, layers))
+        grouped = [GroupedLayer([by["q"], by["k"], by["v"]], copies, dev, torch), by["o"],
+                   GroupedLayer([by["gate"], by["up"]], copies, dev, torch), by["down"]]
         ops = 2.0 * M * sum(l.N * l.K for l in spec)
-        out.append({"M": M, "us_per_block": round(ms * 1e3, 2),
-                    "packed_GB_s": round(block_bytes / (ms * 1e-3) / 1e9, 1),
-                    "TOPS": round(ops / (ms * 1e-3) / 1e12, 2)})
-        del layers
+        row = {"M": M}
+        for label, units in (("separate", layers), ("grouped", grouped)):
+            def step(r, units=units):
+                for U in units:
+                    U.forward(bt, r)
+
+            for s in range(min(args.warmup, 2 * copies)):
+                step(s % copies)
+            torch.cuda.synchronize()
+            run = graph_runner(step, copies, args.eager, torch)
+            ms, _ = timed(run, args.block_steps, torch)
+            row[label] = {"launch_units": len(units), "us_per_block": round(ms * 1e3, 2),
+                          "packed_GB_s": round(block_bytes / (ms * 1e-3) / 1e9, 1),
+                          "TOPS": round(ops / (ms * 1e-3) / 1e12, 2)}
+        out.append(row)
+        del layers, grouped, by
+        torch.cuda.empty_cache()
     return {"workload": "Llama-3-8B block: q 4096x4096, k/v 4096x1024, o 4096x4096, gate/up "
                         "4096x14336, down 14336x4096; bf16 N(0,1) tokens, RMSNorm + int8 quant "
-                        "before each projection",
+                        "before each projection (grouped: q|k|v and gate|up share one quantisation)",
             "packed_bytes_per_block": block_bytes, "weight_rotation_copies": copies,
             "by_tokens": out}
 

@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
     L.bitnet_linear_forward.restype = i32
     L.bitnet_bitlinear_forward.argtypes = [p, p, f32, p, p, i64, i64, i64, p, p, p, p, p, p]
     L.bitnet_bitlinear_forward.restype = i32
+    L.bitnet_bitlinear_forward_grouped.argtypes = [p, p, f32, p, p, p, i32, i64, i64, p, p, p, p,
+                                                   p, p]
+    L.bitnet_bitlinear_forward_grouped.restype = i32
     L.bitnet_status_string.argtypes = [i32]
     L.bitnet_status_string.restype = ctypes.c_char_p
     L.bitnet_last_error.argtypes = []
@@ -135,6 +138,76 @@ def pack_weights(W, hadamard: bool = False):
                                      _ptr(w_scale), _ptr(workspace), workspace.numel(),
                                      _stream(W.device)))
     return packed, w_scale
+
+
+def pack_weights_grouped(Ws, hadamard: bool = False):
+    """Pack several float32 [N_g][K] matrices that share an input (q|k|v, gate|up)
+    into one stacked buffer for bitlinear_forward_grouped.
+
+    Returns (packed uint8 [sum N_g][K/4], w_scales float32 [G][2], group_rows list).
+    Each group keeps its own absmean scale, exactly as pack_weights gives it.
+    """
+    torch = _torch()
+    if not 1 <= len(Ws) <= 8:
+        raise ValueError("between 1 and 8 weight matrices")
+    K = Ws[0].shape[1]
+    rows = [int(W.shape[0]) for W in Ws]
+    dev = Ws[0].device
+    packed = torch.empty((sum(rows), K // 4), dtype=torch.uint8, device=dev)
+    w_scales = torch.empty((len(Ws), 2), dtype=torch.float32, device=dev)
+    r0 = 0
+    for g, W in enumerate(Ws):
+        _require(W, "W", torch.float32, 2)
+        if W.shape[1] != K:
+            raise ValueError("all grouped matrices need the same K")
+        N = rows[g]
+        ws_bytes = pack_weights_workspace_bytes(N, K, hadamard)
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        _check(lib().bitnet_pack_weights(_ptr(W), N, K, int(bool(hadamard)), _ptr(packed[r0:r0 + N]),
+                                         _ptr(w_scales[g]), _ptr(workspace), workspace.numel(),
+                                         _stream(dev)))
+        r0 += N
+    return packed, w_scales, rows
+
+
+def bitlinear_forward_grouped(x, packed, w_scales, group_rows, gain=None, eps: float = 1e-5,
+                              out=None, codes=None, acc_out=None):
+    """Grouped fused BitLinear forward (bitnet_bitlinear_forward_grouped): x is
+    quantised once and contracted with every group of the stacked ``packed``;
+    y float32 [M][sum(group_rows)].  Arguments otherwise as bitlinear_forward."""
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    _require(packed, "packed", torch.uint8, 2)
+    _require(w_scales, "w_scales", torch.float32, 2)
+    M, K = x.shape
+    rows = [int(r) for r in group_rows]
+    N = sum(rows)
+    if packed.shape[0] != N or packed.shape[1] * 4 != K:
+        raise ValueError(f"packed is {list(packed.shape)}, expected [{N}][{K // 4}]")
+    if tuple(w_scales.shape) != (len(rows), 2):
+        raise ValueError(f"w_scales must be [{len(rows)}][2]")
+    if gain is not None:
+        _require(gain, "gain", torch.float32, 1)
+    if codes is None:
+        codes = (torch.empty((M, K), dtype=torch.int8, device=x.device),
+                 torch.empty(M, dtype=torch.float32, device=x.device),
+                 torch.empty(M, dtype=torch.int32, device=x.device))
+    xq, x_scale, x_qsum = codes
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _require(out, "out", torch.float32, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}][{N}]")
+    if acc_out is not None:
+        _require(acc_out, "acc_out", torch.int32, 2)
+        if tuple(acc_out.shape) != (M, N):
+            raise ValueError(f"acc_out must be [{M}][{N}]")
+    rows_c = (ctypes.c_int64 * len(rows))(*rows)
+    _check(lib().bitnet_bitlinear_forward_grouped(
+        _ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(packed), _ptr(w_scales),
+        ctypes.cast(rows_c, ctypes.c_void_p), len(rows),
+        M, K, _ptr(xq), _ptr(x_scale), _ptr(x_qsum), _ptr(out), _ptr(acc_out), _stream(x.device)))
+    return (out, acc_out) if acc_out is not None else out
 
 
 def _quant(name, x, gain, eps, out):

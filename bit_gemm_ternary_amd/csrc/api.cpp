@@ -167,11 +167,31 @@ int bitnet_linear_forward(const int8_t* xq, const float* x_scale, const int32_t*
         (acc && !aligned(acc, 4)))
         return fail(BITNET_ERR_ALIGN, "%s: scales, sums, y and acc must be 4-byte aligned", fn);
     hipStream_t st = (hipStream_t)stream;
+    const bitnet::RowScales scales = bitnet::single_group(w_scale, N);
     hipError_t e = bitnet::gemv_supported(M, K)
-                       ? bitnet::launch_gemv(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, st)
-                       : bitnet::launch_gemm(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, st);
+                       ? bitnet::launch_gemv(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, st)
+                       : bitnet::launch_gemm(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, st);
     return hip_status(e, fn);
 }
+
+namespace {
+
+// Quantise x once, then contract it with every row group of `packed`.
+int bitlinear_forward_rows(const uint16_t* x, const float* gain, float eps, const uint8_t* packed,
+                           const bitnet::RowScales& scales, int64_t M, int64_t N, int64_t K,
+                           int8_t* xq, float* x_scale, int32_t* x_qsum, float* y, int32_t* acc,
+                           hipStream_t st, const char* fn) {
+    if (bitnet::gemv_supported(M, K))
+        return hip_status(bitnet::launch_fused_decode(x, gain, eps, packed, scales, M, N, K, y, xq,
+                                                      x_scale, x_qsum, acc, st),
+                          fn);
+    hipError_t e = bitnet::launch_quant_act(x, gain, eps, M, K, xq, x_scale, x_qsum, st);
+    if (e == hipSuccess)
+        e = bitnet::launch_gemm(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, st);
+    return hip_status(e, fn);
+}
+
+}  // namespace
 
 int bitnet_bitlinear_forward(const uint16_t* x, const float* gain, float eps,
                              const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
@@ -190,14 +210,42 @@ int bitnet_bitlinear_forward(const uint16_t* x, const float* gain, float eps,
     if (!aligned(packed, 16)) return fail(BITNET_ERR_ALIGN, "%s: packed must be 16-byte aligned", fn);
     if (!aligned(w_scale, 4) || !aligned(y, 4) || (acc && !aligned(acc, 4)))
         return fail(BITNET_ERR_ALIGN, "%s: w_scale, y and acc must be 4-byte aligned", fn);
-    if (bitnet::gemv_supported(M, K))
-        return hip_status(bitnet::launch_fused_decode(x, gain, eps, packed, w_scale, M, N, K, y, xq,
-                                                      x_scale, x_qsum, acc, st),
-                          fn);
-    hipError_t e = bitnet::launch_quant_act(x, gain, eps, M, K, xq, x_scale, x_qsum, st);
-    if (e == hipSuccess)
-        e = bitnet::launch_gemm(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, st);
-    return hip_status(e, fn);
+    return bitlinear_forward_rows(x, gain, eps, packed, bitnet::single_group(w_scale, N), M, N, K,
+                                  xq, x_scale, x_qsum, y, acc, st, fn);
+}
+
+int bitnet_bitlinear_forward_grouped(const uint16_t* x, const float* gain, float eps,
+                                     const uint8_t* packed, const float* w_scales,
+                                     const int64_t* group_rows, int groups, int64_t M, int64_t K,
+                                     int8_t* xq, float* x_scale, int32_t* x_qsum, float* y,
+                                     int32_t* acc, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_bitlinear_forward_grouped";
+    int s = validate_quant(x, gain, eps, M, K, xq, x_scale, x_qsum, false, fn);
+    if (s != BITNET_OK) return s;
+    if (groups < 1 || groups > bitnet::kMaxRowGroups)
+        return fail(BITNET_ERR_SHAPE, "%s: groups=%d must be in [1, %d]", fn, groups,
+                    bitnet::kMaxRowGroups);
+    if (!group_rows) return fail(BITNET_ERR_NULL, "%s: group_rows must not be NULL", fn);
+    bitnet::RowScales scales{};
+    scales.w_scale = w_scales;
+    scales.groups = groups;
+    int64_t N = 0;
+    for (int g = 0; g < groups; ++g) {
+        if (group_rows[g] < 1 || group_rows[g] > kMaxRows - N)
+            return fail(BITNET_ERR_SHAPE, "%s: group %d has %lld rows (each group needs >= 1, total <= 2^31-1)",
+                        fn, g, (long long)group_rows[g]);
+        N += group_rows[g];
+        scales.end[g] = N;
+    }
+    if (M == 0) return BITNET_OK;
+    if (!packed || !w_scales || !y)
+        return fail(BITNET_ERR_NULL, "%s: packed, w_scales and y must not be NULL", fn);
+    if (!aligned(packed, 16)) return fail(BITNET_ERR_ALIGN, "%s: packed must be 16-byte aligned", fn);
+    if (!aligned(w_scales, 4) || !aligned(y, 4) || (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "%s: w_scales, y and acc must be 4-byte aligned", fn);
+    return bitlinear_forward_rows(x, gain, eps, packed, scales, M, N, K, xq, x_scale, x_qsum, y,
+                                  acc, (hipStream_t)stream, fn);
 }
 
 const char* bitnet_status_string(int status) {

@@ -112,7 +112,7 @@ __device__ __forceinline__ void stage_barrier() {
 template <class C>
 __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     const int8_t* __restrict__ X, const uint8_t* __restrict__ P, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ x_qsum, const float* __restrict__ w_scale, int M, int N, int K,
+    const int32_t* __restrict__ x_qsum, const RowScales scales, int M, int N, int K,
     int vec_store, float* __restrict__ y, int32_t* __restrict__ acc_out) {
     __shared__ __align__(16) int8_t lds[C::S][C::X_STAGE + C::W_STAGE];
 
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     // 16 bytes.  Instead each wave dequantises 16 tokens at a time into its own
     // LDS region (row stride TN + 4 floats keeps the 16-byte writes conflict
     // free) and writes them back as whole row segments of TN floats.
-    const float d_w = w_scale[0];
+    const float dw0 = scales.w_scale[0];
     __syncthreads();   // every wave is done with the stage buffers
     float* stage = reinterpret_cast<float*>(&lds[0][0]) + wave * 16 * C::ROW_F;
     constexpr int PPR = C::TN / 4;              // 16-byte pieces per row segment
@@ -270,14 +270,16 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int nl = i * 32 + 8 * q + 4 * fh;   // wave-local output column
+                        const int64_t ng = n0 + wn * C::TN + nl;   // its global column
                         const v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1],
                                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]} -
                                       v4i{qs, qs, qs, qs};
+                        // Columns past N read row N-1's scale; they are never stored.
                         float4 v;
-                        v.x = ((float)a[0] * sx) * d_w;
-                        v.y = ((float)a[1] * sx) * d_w;
-                        v.z = ((float)a[2] * sx) * d_w;
-                        v.w = ((float)a[3] * sx) * d_w;
+                        v.x = ((float)a[0] * sx) * scales.of(min(ng, (int64_t)N - 1), dw0);
+                        v.y = ((float)a[1] * sx) * scales.of(min(ng + 1, (int64_t)N - 1), dw0);
+                        v.z = ((float)a[2] * sx) * scales.of(min(ng + 2, (int64_t)N - 1), dw0);
+                        v.w = ((float)a[3] * sx) * scales.of(min(ng + 3, (int64_t)N - 1), dw0);
                         *reinterpret_cast<float4*>(&stage[(fr % 16) * C::ROW_F + nl]) = v;
                         if (acc_out != nullptr && m < M) {
                             const int64_t nb = n0 + wn * C::TN + nl;
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
 template <int KW>
 __global__ __launch_bounds__(KW * kWave) void skinny_kernel(
     const int8_t* __restrict__ X, const uint8_t* __restrict__ P, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ x_qsum, const float* __restrict__ w_scale, int M, int N, int K,
+    const int32_t* __restrict__ x_qsum, const RowScales scales, int M, int N, int K,
     int vec_store, float* __restrict__ y, int32_t* __restrict__ acc_out) {
     __shared__ v4i part[KW][kWave];
     const int lane = threadIdx.x % kWave;
@@ -386,15 +388,15 @@ __global__ __launch_bounds__(KW * kWave) void skinny_kernel(
     if (m >= M || nb >= N) return;
     const int32_t qs = x_qsum[m];
     const float sx = x_scale[m];
-    const float d_w = w_scale[0];
+    const float dw0 = scales.w_scale[0];
     if (vec_store && nb + 3 < N) {
         const v4i a = acc - v4i{qs, qs, qs, qs};
         if (acc_out != nullptr) *reinterpret_cast<v4i*>(&acc_out[m * N + nb]) = a;
         float4 v;
-        v.x = ((float)a[0] * sx) * d_w;
-        v.y = ((float)a[1] * sx) * d_w;
-        v.z = ((float)a[2] * sx) * d_w;
-        v.w = ((float)a[3] * sx) * d_w;
+        v.x = ((float)a[0] * sx) * scales.of(nb, dw0);
+        v.y = ((float)a[1] * sx) * scales.of(nb + 1, dw0);
+        v.z = ((float)a[2] * sx) * scales.of(nb + 2, dw0);
+        v.w = ((float)a[3] * sx) * scales.of(nb + 3, dw0);
         *reinterpret_cast<float4*>(&y[m * N + nb]) = v;
     } else {
 #pragma unroll
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(KW * kWave) void skinny_kernel(
             if (nb + e < N) {
                 const int a = acc[e] - qs;
                 if (acc_out != nullptr) acc_out[m * N + nb + e] = a;
-                y[m * N + nb + e] = ((float)a * sx) * d_w;
+                y[m * N + nb + e] = ((float)a * sx) * scales.of(nb + e, dw0);
             }
         }
     }
@@ -410,12 +412,12 @@ __global__ __launch_bounds__(KW * kWave) void skinny_kernel(
 
 template <int KW>
 hipError_t launch_skinny(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
-                         const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                         const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                          int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     const int vec_store = (N % 4 == 0) && ((uintptr_t)y % 16 == 0) &&
                           (acc == nullptr || (uintptr_t)acc % 16 == 0);
     return launch_kernel(skinny_kernel<KW>, dim3((unsigned)((N + 15) / 16)), dim3(KW * kWave), 0,
-                         stream, xq, packed, x_scale, x_qsum, w_scale, (int)M, (int)N, (int)K,
+                         stream, xq, packed, x_scale, x_qsum, scales, (int)M, (int)N, (int)K,
                          vec_store, y, acc);
 }
 
@@ -426,12 +428,12 @@ int64_t tiles_of(int64_t M, int64_t N) {
 
 template <class C>
 hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
-                      const uint8_t* packed, const float* w_scale, int64_t M, int64_t N, int64_t K,
+                      const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N, int64_t K,
                       float* y, int32_t* acc, hipStream_t stream) {
     const int vec_store = (N % 4 == 0) && ((uintptr_t)y % 16 == 0) &&
                           (acc == nullptr || (uintptr_t)acc % 16 == 0);
     return launch_kernel(gemm_kernel<C>, dim3((unsigned)tiles_of<C>(M, N)), dim3(C::NT), 0, stream,
-                         xq, packed, x_scale, x_qsum, w_scale, (int)M, (int)N, (int)K, vec_store, y,
+                         xq, packed, x_scale, x_qsum, scales, (int)M, (int)N, (int)K, vec_store, y,
                          acc);
 }
 
@@ -446,24 +448,24 @@ constexpr int64_t kCus = 256;
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
-                       const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                       const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M <= 16) {
         // About 2048 waves in flight: split K eight ways when there are few row blocks.
         if ((N + 15) / 16 < 2 * kCus)
-            return launch_skinny<8>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
-        return launch_skinny<4>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
+            return launch_skinny<8>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+        return launch_skinny<4>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     }
     // The largest tile that still gives every CU enough work: two rounds of the
     // large tile, one of the mid tile.  With fewer tiles the stage loop is bound
     // by load latency, not by the matrix cores, and more, smaller tiles keep
     // more loads in flight (measured on the prefill and Llama-block shapes).
     if (tiles_of<CfgLarge>(M, N) >= 2 * kCus)
-        return launch_cfg<CfgLarge>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
+        return launch_cfg<CfgLarge>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     if (tiles_of<CfgMid>(M, N) >= kCus)
-        return launch_cfg<CfgMid>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
-    return launch_cfg<CfgTiny>(xq, x_scale, x_qsum, packed, w_scale, M, N, K, y, acc, stream);
+        return launch_cfg<CfgMid>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    return launch_cfg<CfgTiny>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
 }
 
 }  // namespace bitnet

@@ -169,12 +169,12 @@ struct GemvCore {
 
     // Epilogue: lane i writes row row0 + i.
     __device__ static __forceinline__ void store(const int (&my_acc)[MT], const float* x_scale,
-                                                 const int32_t* x_qsum, const float* w_scale,
+                                                 const int32_t* x_qsum, const RowScales& scales,
                                                  int64_t N, int64_t row0, int64_t row1, int lane,
                                                  float* y, int32_t* acc_out) {
         const int64_t r = row0 + lane;
         if (r < row1) {
-            const float d_w = w_scale[0];
+            const float d_w = scales.of(r, scales.w_scale[0]);
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 const int a = my_acc[t] - x_qsum[t];
@@ -189,7 +189,7 @@ template <int MT, int CH>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_qsum, const uint8_t* __restrict__ packed,
-    const float* __restrict__ w_scale, int N, int K, int rows_per_wave, float* __restrict__ y,
+    const RowScales scales, int N, int K, int rows_per_wave, float* __restrict__ y,
     int32_t* __restrict__ acc_out) {
     using G = GemvCore<MT, CH>;
     const int lane = threadIdx.x % kWave;
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 #pragma unroll
     for (int t = 0; t < MT; ++t) my_acc[t] = 0;
     G::run(w, xv, packed, row_bytes, nchunk, row0, row1, lane, my_acc);
-    G::store(my_acc, x_scale, x_qsum, w_scale, N, row0, row1, lane, y, acc_out);
+    G::store(my_acc, x_scale, x_qsum, scales, N, row0, row1, lane, y, acc_out);
 }
 
 // Fused RMSNorm + int8 quantisation + GEMV.  Every workgroup quantises the MT
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 template <int MT, int CH, int NT>
 __global__ __launch_bounds__(NT) void fused_decode_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
-    const uint8_t* __restrict__ packed, const float* __restrict__ w_scale, int N, int K,
+    const uint8_t* __restrict__ packed, const RowScales scales, int N, int K,
     int rows_per_wave, float* __restrict__ y, int8_t* __restrict__ xq_out,
     float* __restrict__ x_scale_out, int32_t* __restrict__ x_qsum_out,
     int32_t* __restrict__ acc_out) {
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NT) void fused_decode_kernel(
     float tok_scale[MT];
 #pragma unroll
     for (int tok = 0; tok < MT; ++tok) tok_scale[tok] = dequant_scale(tok);
-    G::store(my_acc, tok_scale, tok_sum, w_scale, N, row0, row1, lane, y, acc_out);
+    G::store(my_acc, tok_scale, tok_sum, scales, N, row0, row1, lane, y, acc_out);
 }
 
 // Rows per wave: spread the rows over about `target_waves` waves (at most 64).
@@ -423,7 +423,7 @@ struct Args {
     const float* gain;
     float eps;
     const uint8_t* packed;
-    const float* w_scale;
+    RowScales scales;
     int64_t N, K;
     float* y;
     int8_t* xq_out;
@@ -439,7 +439,7 @@ struct Standalone {
         const int64_t rpw = rows_per_wave(a.N, 2048);
         const int64_t blocks = ((a.N + rpw - 1) / rpw + kGemvWaves - 1) / kGemvWaves;
         return launch_kernel((gemv_kernel<MT, CH>), dim3((unsigned)blocks), dim3(kGemvThreads), 0,
-                             a.stream, a.xq, a.x_scale, a.x_qsum, a.packed, a.w_scale, (int)a.N,
+                             a.stream, a.xq, a.x_scale, a.x_qsum, a.packed, a.scales, (int)a.N,
                              (int)a.K, (int)rpw, a.y, a.acc);
     }
 };
@@ -454,7 +454,7 @@ struct Fused {
         const int64_t blocks = ((a.N + rpw - 1) / rpw + NT / kWave - 1) / (NT / kWave);
         return launch_kernel((fused_decode_kernel<MT, CH, NT>), dim3((unsigned)blocks),
                              dim3(NT), 0, a.stream, a.x, a.gain, a.eps, a.packed,
-                             a.w_scale, (int)a.N, (int)a.K, (int)rpw, a.y, a.xq_out,
+                             a.scales, (int)a.N, (int)a.K, (int)rpw, a.y, a.xq_out,
                              a.x_scale_out, a.x_qsum_out, a.acc);
     }
 };
@@ -500,21 +500,21 @@ bool gemv_supported(int64_t M, int64_t K) {
 }
 
 hipError_t launch_gemv(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
-                       const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                       const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     if (N == 0) return hipSuccess;
     Args a{};
-    a.xq = xq, a.x_scale = x_scale, a.x_qsum = x_qsum, a.packed = packed, a.w_scale = w_scale;
+    a.xq = xq, a.x_scale = x_scale, a.x_qsum = x_qsum, a.packed = packed, a.scales = scales;
     a.N = N, a.K = K, a.y = y, a.acc = acc, a.stream = stream;
     return dispatch<Standalone>(M, chunks_per_lane(K), a);
 }
 
 hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
-                               const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
-                               int64_t K, float* y, int8_t* xq, float* x_scale, int32_t* x_qsum,
-                               int32_t* acc, hipStream_t stream) {
+                               const uint8_t* packed, const RowScales& scales, int64_t M,
+                               int64_t N, int64_t K, float* y, int8_t* xq, float* x_scale,
+                               int32_t* x_qsum, int32_t* acc, hipStream_t stream) {
     Args a{};
-    a.x = x, a.gain = gain, a.eps = eps, a.packed = packed, a.w_scale = w_scale;
+    a.x = x, a.gain = gain, a.eps = eps, a.packed = packed, a.scales = scales;
     a.N = N, a.K = K, a.y = y, a.xq_out = xq, a.x_scale_out = x_scale, a.x_qsum_out = x_qsum;
     a.acc = acc, a.stream = stream;
     return dispatch<Fused>(M, chunks_per_lane(K), a);

@@ -52,18 +52,48 @@ hipError_t launch_fwht_rows_f32(const float* src, float* dst, int64_t N, int64_t
                                 hipStream_t stream);
 
 // --- contraction (gemv.hip, gemm_mfma.hip) ----------------------------------
+// Dequantisation multipliers of the weight rows: one (d_w, s_w) pair per group
+// of consecutive rows.  A single matrix is one group; projections that share
+// their input (q|k|v, gate|up) are stacked row-wise as several groups and
+// contracted in one launch.
+constexpr int kMaxRowGroups = 8;
+struct RowScales {
+    const float* w_scale;          // device [groups][2]: (d_w, s_w) per group
+    int groups;                    // 1 .. kMaxRowGroups
+    int64_t end[kMaxRowGroups];    // exclusive last row of each group; end[groups-1] = N
+
+    // d_w of weight row n (0 <= n < N); dw0 = w_scale[0], loaded once by the
+    // caller before it stores anything (the outputs may not be assumed apart
+    // from w_scale, so a load here would be repeated after every store).
+    __device__ __forceinline__ float of(int64_t n, float dw0) const {
+        if (groups == 1) return dw0;
+        int g = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxRowGroups - 1; ++i) g += (i < groups - 1 && n >= end[i]) ? 1 : 0;
+        return w_scale[2 * g];
+    }
+};
+
+inline RowScales single_group(const float* w_scale, int64_t N) {
+    RowScales r{};
+    r.w_scale = w_scale;
+    r.groups = 1;
+    r.end[0] = N;
+    return r;
+}
+
 // True if the register-resident GEMV handles this (M, K).
 bool gemv_supported(int64_t M, int64_t K);
 hipError_t launch_gemv(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
-                       const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                       const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream);
 // Fused RMSNorm + int8 quantisation + GEMV (requires gemv_supported(M, K)).
 hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
-                               const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
-                               int64_t K, float* y, int8_t* xq, float* x_scale, int32_t* x_qsum,
-                               int32_t* acc, hipStream_t stream);
+                               const uint8_t* packed, const RowScales& scales, int64_t M,
+                               int64_t N, int64_t K, float* y, int8_t* xq, float* x_scale,
+                               int32_t* x_qsum, int32_t* acc, hipStream_t stream);
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
-                       const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                       const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream);
 
 }  // namespace bitnet

@@ -186,6 +186,36 @@ int bitnet_bitlinear_forward(const uint16_t* x, const float* gain, float eps,
                              int32_t* acc, void* stream);
 
 /*
+ * Grouped BitLinear forward: several projections that read the same input
+ * (q|k|v, gate|up) contracted in one launch after one quantisation of x
+ * ([FT] "양자화 메커니즘", "계산 패러다임"; the activation scale is per token, so
+ * the codes are shared by every projection of the token).
+ *
+ *   x, gain, eps         in   as bitnet_quant_act.
+ *   packed               in   uint8 [N][K/4], N = sum of group_rows: the
+ *                             projections' packed weights (each produced by
+ *                             bitnet_pack_weights) stacked row-wise in group
+ *                             order; 16-byte aligned.
+ *   w_scales             in   float32 [groups][2]: each group's (d_w, s_w) as
+ *                             bitnet_pack_weights wrote it (device, 4-byte aligned).
+ *   group_rows           in   int64 [groups] (host): rows of each group, >= 1.
+ *   groups                    1 .. 8.
+ *   xq, x_scale, x_qsum  out  as bitnet_quant_act.
+ *   y                    out  float32 [M][N]: for n in group g,
+ *                             y[m][n] = acc[m][n] * d_x[m] * d_w[g].
+ *   acc                  out  int32 [M][N], or NULL.
+ * Results are bit-identical to calling bitnet_bitlinear_forward once per
+ * group with that group's rows.  M = 0 is a no-op (after the shape checks);
+ * errors as bitnet_bitlinear_forward, plus BITNET_ERR_SHAPE for a bad group
+ * count or size.
+ */
+int bitnet_bitlinear_forward_grouped(const uint16_t* x, const float* gain, float eps,
+                                     const uint8_t* packed, const float* w_scales,
+                                     const int64_t* group_rows, int groups, int64_t M, int64_t K,
+                                     int8_t* xq, float* x_scale, int32_t* x_qsum, float* y,
+                                     int32_t* acc, void* stream);
+
+/*
  * Profiling hook: arm two hipEvent_t (passed as void*; either may be NULL) for
  * the first kernel the next bitnet_* call on this thread launches (the
  * contraction kernel of bitnet_linear_forward, the quantisation kernel of the

@@ -154,3 +154,34 @@ def test_fused_forward_argument_errors(L):
 
 def test_kernel_events_hook_is_exported(L):
     assert L.bitnet_set_kernel_events(None, None) == 0
+
+
+def _grouped(L, rows=(8, 4), x=A16, gain=None, eps=1e-5, P=A16, ws=A4, M=1, K=256, xq=A16, sx=A4,
+             qs=A4, y=A4, acc=None, groups=None, null_rows=False):
+    rows_c = (ctypes.c_int64 * max(len(rows), 1))(*rows)
+    return L.bitnet_bitlinear_forward_grouped(
+        ctypes.c_void_p(x), None if gain is None else ctypes.c_void_p(gain), ctypes.c_float(eps),
+        ctypes.c_void_p(P), ctypes.c_void_p(ws),
+        None if null_rows else ctypes.cast(rows_c, ctypes.c_void_p),
+        len(rows) if groups is None else groups, M, K, ctypes.c_void_p(xq), ctypes.c_void_p(sx),
+        ctypes.c_void_p(qs), ctypes.c_void_p(y), None if acc is None else ctypes.c_void_p(acc), None)
+
+
+def test_grouped_forward_argument_errors(L):
+    assert _grouped(L, M=-1) == 2
+    assert _grouped(L, K=100) == 2
+    assert _grouped(L, eps=-1.0) == 7
+    assert _grouped(L, groups=0) == 2
+    assert _grouped(L, rows=tuple([4] * 9)) == 2           # more than 8 groups
+    assert _grouped(L, rows=(8, 0, 4)) == 2                # an empty group
+    assert _grouped(L, rows=(2 ** 31 - 1, 1)) == 2         # total rows past 2^31 - 1
+    assert _grouped(L, null_rows=True) == 1
+    assert _grouped(L, x=0) == 1
+    assert _grouped(L, P=0) == 1
+    assert _grouped(L, ws=0) == 1
+    assert _grouped(L, y=0) == 1
+    assert _grouped(L, x=BAD) == 4
+    assert _grouped(L, P=A4) == 4
+    assert _grouped(L, ws=BAD) == 4
+    assert _grouped(L, acc=BAD) == 4
+    assert _grouped(L, M=0, x=0, P=0, y=0) == 0

@@ -341,3 +341,56 @@ def test_bitlinear_forward_graph_replays(orc, dev):
         g.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host(y), eager[i])
+
+
+# ---------------------------------------------------------------------------
+# Grouped forward: projections sharing one input, stacked row-wise, one launch.
+# ---------------------------------------------------------------------------
+
+GROUPED_CASES = [
+    (1, 4096, (4096, 1024, 1024), False),     # Llama-3-8B q|k|v, decode
+    (1, 4096, (14336, 14336), False),         # gate|up, decode
+    (3, 256, (37, 64, 5), True),              # ragged groups, fused path
+    (16, 4096, (4096, 1024, 1024), False),    # skinny path
+    (256, 4096, (1024, 512, 512), False),     # tiled GEMM path
+    (100, 192, (50, 77, 3, 1, 9, 33, 2, 64), True),  # eight groups, ragged
+    (2100, 192, (7000, 6999, 1), False),      # 448 x 128 tiles across group borders
+]
+
+
+@pytest.mark.parametrize("M,K,rows,with_gain", GROUPED_CASES)
+def test_bitlinear_forward_grouped(orc, dev, M, K, rows, with_gain):
+    x = _activation(M, K, seed=1100 + M)
+    gain = np.random.default_rng(M + K).uniform(0.5, 1.5, K).astype(np.float32) if with_gain else None
+    wq, wdx, wqs = orc.quant_act(x, gain=gain)
+    packs, scales, want_acc, want_y = [], [], [], []
+    for g, n in enumerate(rows):
+        W = synth.weights(n, K, seed=1200 + 10 * g + n % 7)
+        packed, d_w, s_w, _ = orc.pack_weights(W)
+        acc_g, y_g = orc.linear_forward(wq, wdx, packed, d_w, K)
+        packs.append(packed)
+        scales.append([d_w, s_w])
+        want_acc.append(acc_g)
+        want_y.append(y_g)
+    N = sum(rows)
+    codes = (torch.empty((M, K), dtype=torch.int8, device=dev), torch.empty(M, device=dev),
+             torch.empty(M, dtype=torch.int32, device=dev))
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+    y, acc = bt.bitlinear_forward_grouped(
+        bf16_to_dev(x, dev), to_dev(np.concatenate(packs), dev),
+        to_dev(np.array(scales, np.float32), dev), rows,
+        None if gain is None else to_dev(gain, dev), 1e-5, codes=codes, acc_out=acc)
+    np.testing.assert_array_equal(host(codes[0]), wq)
+    np.testing.assert_array_equal(host(codes[2]), wqs)
+    np.testing.assert_array_equal(host(acc), np.concatenate(want_acc, axis=1))
+    assert_close_rel(host(y), np.concatenate(want_y, axis=1))
+
+
+def test_pack_weights_grouped_matches_single_packs(orc, dev):
+    K, rows = 512, (96, 32, 160)
+    Ws = [synth.weights(n, K, seed=1300 + g) for g, n in enumerate(rows)]
+    packed, w_scales, got_rows = bt.pack_weights_grouped([to_dev(W, dev) for W in Ws])
+    assert got_rows == list(rows)
+    want = [orc.pack_weights(W) for W in Ws]
+    np.testing.assert_array_equal(host(packed), np.concatenate([p for p, *_ in want]))
+    np.testing.assert_array_equal(host(w_scales), np.array([[d, s] for _, d, s, _ in want], np.float32))
