@@ -17,51 +17,59 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // ---------------------------------------------------------------------------
-// Wavefront reductions (butterfly over the 64 lanes; every lane gets the result).
+// DPP wavefront reductions: four lane moves within each 16-lane row, then the
+// four row results read out to scalars.  No LDS traffic; the combination order
+// is fixed, so floating-point results are deterministic.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
+// Sum of v over the 64 lanes, returned wave-uniform.
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+// Lane-to-lane moves within 16-lane rows (DPP), for 32- and 64-bit values.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_move(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ float read_lane(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double read_lane(double v, int l) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-    return v;
+// Wave-uniform max / sum over the 64 lanes, reduced within each 16-lane row by
+// DPP and then over the four rows; the combination order is fixed, so the
+// double sum is deterministic.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_move<0xB1>(v));
+    v = fmaxf(v, dpp_move<0x4E>(v));
+    v = fmaxf(v, dpp_move<0x141>(v));
+    v = fmaxf(v, dpp_move<0x140>(v));
+    return fmaxf(fmaxf(read_lane(v, 0), read_lane(v, 16)), fmaxf(read_lane(v, 32), read_lane(v, 48)));
 }
-
-// Workgroup reductions over NT threads (NT a multiple of 64, at most 1024).
-// `scratch` must hold NT/64 elements; the call contains two barriers, so every
-// thread of the workgroup must reach it.
-template <int NT, typename T, typename Op>
-__device__ __forceinline__ T block_reduce(T v, T* scratch, Op op) {
-    static_assert(NT % kWave == 0 && NT <= 1024, "block size");
-    constexpr int NW = NT / kWave;
-    const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
-    if (lane == 0) scratch[wave] = v;
-    __syncthreads();
-    T r = scratch[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) r = op(r, scratch[w]);
-    __syncthreads();
-    return r;
+__device__ __forceinline__ double wave_sum_dpp(double v) {
+    v += dpp_move<0xB1>(v);
+    v += dpp_move<0x4E>(v);
+    v += dpp_move<0x141>(v);
+    v += dpp_move<0x140>(v);
+    return (read_lane(v, 0) + read_lane(v, 16)) + (read_lane(v, 32) + read_lane(v, 48));
 }
-
-struct MaxOp {
-    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
-};
-struct SumOp {
-    template <typename T>
-    __device__ T operator()(T a, T b) const { return a + b; }
-};
 
 // Codes of one activation: clamp(rint(v), lo, hi) as an int.  rint rounds half
 // to even (v_rndne_f32).

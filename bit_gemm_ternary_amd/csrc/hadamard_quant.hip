@@ -146,14 +146,27 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
 
     F::template run<0>(v, lds, t);
 
+    // Absmax of the transform and the sum of squares, reduced together: DPP
+    // within each wave, one LDS exchange across waves.  The transform's last
+    // LDS read is behind a barrier, so `lds` is free from here on.
+    constexpr int NW = F::B / kWave;
+    const int lane = t % kWave, wave = t / kWave;
     float amax = 0.f;
 #pragma unroll
     for (int r = 0; r < E; ++r) amax = fmaxf(amax, fabsf(v[r]));
-    amax = block_reduce<F::B>(wave_max(amax), red_f, MaxOp());
-    ss = block_reduce<F::B>(wave_sum(ss), red_d, SumOp());
+    amax = wave_max_dpp(amax);
+    ss = wave_sum_dpp(ss);
+    if (lane == 0) {
+        red_f[wave] = amax;
+        red_d[wave] = ss;
+    }
+    __syncthreads();
+    amax = red_f[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) amax = fmaxf(amax, red_f[w]);
 
-    // Codes go through LDS (as bytes) back to natural order for wide stores.
-    // block_reduce ended with a barrier, so no thread still reads `lds`.
+    // Codes go through LDS (as bytes) back to natural order for wide stores;
+    // each wave's code sum rides along and is added up after the same barrier.
     const bool zero = amax < kTinyAbsmax;
     const float scale = zero ? 0.f : 7.0f / amax;
     int8_t* lds8 = reinterpret_cast<int8_t*>(lds);
@@ -164,6 +177,8 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
         qs += q;
         lds8[F::template index<F::NPH - 1>(t, r)] = (int8_t)q;
     }
+    qs = wave_sum_dpp(qs);
+    if (lane == 0) red_i[wave] = qs;
     __syncthreads();
     int8_t* dst = xq + m * K + (int64_t)t * E;
     if constexpr (E >= 16) {
@@ -175,12 +190,18 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
     } else {
         *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds8 + t * E);
     }
-    qs = block_reduce<F::B>(wave_sum(qs), red_i, SumOp());
 
     if (t == 0) {
-        const double rstd = 1.0 / sqrt(ss / (double)K + (double)eps);
+        double sum_sq = red_d[0];
+        int qsum = red_i[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            sum_sq += red_d[w];
+            qsum += red_i[w];
+        }
+        const double rstd = 1.0 / sqrt(sum_sq / (double)K + (double)eps);
         x_scale[m] = zero ? 0.f : (float)(((double)amax * rstd) / (7.0 * sqrt_k));
-        x_qsum[m] = qs;
+        x_qsum[m] = qsum;
     }
 }
 

@@ -8,7 +8,8 @@
 // One 256-thread workgroup per token.  Each thread owns CH chunks of 16
 // consecutive bf16 values (chunk c = thread + 256*j), kept in registers as raw
 // bf16 between the two passes:
-//   pass 1: u = x * gain, absmax |u| and sum x^2 (float64) -> workgroup reduce;
+//   pass 1: u = x * gain, absmax |u| and sum x^2 (float64) -> workgroup reduce
+//           (DPP within waves, one LDS exchange);
 //   pass 2: codes rint(u * float32(127/absmax)), stored 16 bytes at a time.
 // HBM-bound: 2K bytes read, K bytes written per token.
 #include "common.hpp"
@@ -84,8 +85,20 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
             for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
         }
     }
-    amax = block_reduce<kQuantThreads>(wave_max(amax), red_f, MaxOp());
-    ss = block_reduce<kQuantThreads>(wave_sum(ss), red_d, SumOp());
+    // Absmax and sum of squares reduced together: DPP within each wave, one
+    // LDS exchange across the four waves.
+    constexpr int NW = kQuantThreads / kWave;
+    const int lane = t % kWave, wave = t / kWave;
+    amax = wave_max_dpp(amax);
+    ss = wave_sum_dpp(ss);
+    if (lane == 0) {
+        red_f[wave] = amax;
+        red_d[wave] = ss;
+    }
+    __syncthreads();
+    amax = red_f[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) amax = fmaxf(amax, red_f[w]);
 
     const bool zero = amax < kTinyAbsmax;
     const float scale = zero ? 0.f : 127.0f / amax;
@@ -112,12 +125,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
             *reinterpret_cast<uint4*>(xq + m * K + 16 * c) = make_uint4(word[0], word[1], word[2], word[3]);
         }
     }
-    qs = block_reduce<kQuantThreads>(wave_sum(qs), red_i, SumOp());
+    qs = wave_sum_dpp(qs);
+    if (lane == 0) red_i[wave] = qs;
+    __syncthreads();
 
     if (t == 0) {
-        const double rstd = 1.0 / sqrt(ss / (double)K + (double)eps);
+        double sum_sq = red_d[0];
+        int qsum = red_i[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            sum_sq += red_d[w];
+            qsum += red_i[w];
+        }
+        const double rstd = 1.0 / sqrt(sum_sq / (double)K + (double)eps);
         x_scale[m] = zero ? 0.f : (float)(((double)amax * rstd) / 127.0);
-        x_qsum[m] = qs;
+        x_qsum[m] = qsum;
     }
 }
 
