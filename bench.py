@@ -23,7 +23,9 @@ not Python launch overhead.
                    matrix-core GEMM against the dense int8 peak, and against that
                    peak scaled to the engine clock measured during the kernel
                    (committed counter summary)
-  hadamard         H-BitLinear M=512: FWHT + int4 quantisation GB/s and GEMM TOPS
+  hadamard         H-BitLinear M=512: FWHT + int4 quantisation GB/s and GEMM TOPS,
+                   for int8 codes (int8 matrix core) and for 6-bit E3M2 codes (FP4 x
+                   FP6 matrix core, against the 10.1 PFLOP/s fp6 peak)
   block            the seven BitLinear projections of a Llama-3-8B block at
                    M = 1, 16 and 256 tokens: time per block, packed weight GB/s,
                    int TOPS
@@ -57,6 +59,7 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix-core peak, 5.0 POP/s
 PEAK_CLOCK_GHZ = 2.4        # the engine clock that peak is quoted at
+FP6_PEAK_TOPS = 10100.0     # MI355X dense fp6 / fp4 matrix-core peak, 10.1 PFLOP/s
 ROTATE_BYTES = 1 << 30      # > 4 x the 256 MB Infinity Cache
 METRIC = "BitLinear decode GEMV weight GB/s (%HBM peak); prefill int8 TOPS (%MFMA peak)"
 
@@ -392,21 +395,35 @@ def hadamard_bench(args, dev, bt, torch, synth):
         xs = torch.empty(M, dtype=torch.float32, device=dev)
         qs = torch.empty(M, dtype=torch.int32, device=dev)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        xq6 = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=dev)
         hq = lambda: bt.hadamard_quant_act(x, None, 1e-5, out=(xq, xs, qs))
         gemm = lambda: bt.linear_forward(xq, xs, qs, packed, w_scale, out=y)
+        hq6 = lambda: bt.hadamard_quant_act_f6(x, None, 1e-5, out=(xq6, xs, qs))
+        gemm6 = lambda: bt.linear_forward_f6(xq6, xs, qs, packed, w_scale, out=y)
         for _ in range(5):
             hq()
             gemm()
+            hq6()
+            gemm6()
         torch.cuda.synchronize()
         hq_us = time_launches(hq, args.prefill_iters, bt)
         gemm_us = time_launches(gemm, args.prefill_iters, bt)
+        hq6_us = time_launches(hq6, args.prefill_iters, bt)
+        gemm6_us = time_launches(gemm6, args.prefill_iters, bt)
         hq_bytes = M * K * 2 + M * K + 8 * M
+        hq6_bytes = M * K * 2 + M * K // 4 * 3 + 8 * M
+        ops = 2.0 * M * N * K
         out.append({"M": M, "K": K, "N": N,
                     "fwht_int4_us": round(hq_us, 2),
                     "fwht_int4_GB_s": round(hq_bytes / hq_us / 1e3, 1),
                     "fwht_int4_frac_hbm": round(hq_bytes / hq_us / 1e3 / HBM_PEAK_GBS, 4),
                     "gemm_us": round(gemm_us, 2),
-                    "gemm_TOPS": round(2.0 * M * N * K / (gemm_us * 1e-6) / 1e12, 1)})
+                    "gemm_TOPS": round(ops / (gemm_us * 1e-6) / 1e12, 1),
+                    "f6": {"fwht_e3m2_us": round(hq6_us, 2),
+                           "fwht_e3m2_GB_s": round(hq6_bytes / hq6_us / 1e3, 1),
+                           "gemm_fp4xfp6_us": round(gemm6_us, 2),
+                           "gemm_fp4xfp6_TOPS": round(ops / (gemm6_us * 1e-6) / 1e12, 1),
+                           "gemm_fp4xfp6_frac_fp6_peak": round(ops / (gemm6_us * 1e-6) / 1e12 / FP6_PEAK_TOPS, 4)}})
     return out
 
 

@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
         fn.restype = i32
     L.bitnet_linear_forward.argtypes = [p, p, p, p, p, i64, i64, i64, p, p, p]
     L.bitnet_linear_forward.restype = i32
+    L.bitnet_hadamard_quant_act_f6.argtypes = [p, p, f32, i64, i64, p, p, p, p]
+    L.bitnet_hadamard_quant_act_f6.restype = i32
+    L.bitnet_linear_forward_f6.argtypes = [p, p, p, p, p, i64, i64, i64, p, p, p]
+    L.bitnet_linear_forward_f6.restype = i32
     L.bitnet_bitlinear_forward.argtypes = [p, p, f32, p, p, i64, i64, i64, p, p, p, p, p, p]
     L.bitnet_bitlinear_forward.restype = i32
     L.bitnet_bitlinear_forward_grouped.argtypes = [p, p, f32, p, p, p, i32, i64, i64, p, p, p, p,
@@ -245,6 +249,51 @@ def quant_act(x, gain=None, eps: float = 1e-5, out=None):
 def hadamard_quant_act(x, gain=None, eps: float = 1e-5, out=None):
     """H-BitLinear: bf16 [M][K] (K = 2^p) -> (int4 codes as int8 [M][K], d_x, code sums)."""
     return _quant("bitnet_hadamard_quant_act", x, gain, eps, out)
+
+
+def hadamard_quant_act_f6(x, gain=None, eps: float = 1e-5, out=None):
+    """bf16 [M][K] -> (xq6 uint8 [M][K/4*3] 6-bit E3M2 codes, x_scale float32 [M],
+    x_qsum int32 [M]) (bitnet_hadamard_quant_act_f6)."""
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    M, K = x.shape
+    if gain is not None:
+        _require(gain, "gain", torch.float32, 1)
+    if out is None:
+        out = (torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=x.device),
+               torch.empty(M, dtype=torch.float32, device=x.device),
+               torch.empty(M, dtype=torch.int32, device=x.device))
+    xq6, x_scale, x_qsum = out
+    _require(xq6, "xq6", torch.uint8, 2)
+    if tuple(xq6.shape) != (M, K // 4 * 3):
+        raise ValueError(f"xq6 must be [{M}][{K // 4 * 3}]")
+    _check(lib().bitnet_hadamard_quant_act_f6(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K,
+                                              _ptr(xq6), _ptr(x_scale), _ptr(x_qsum),
+                                              _stream(x.device)))
+    return xq6, x_scale, x_qsum
+
+
+def linear_forward_f6(xq6, x_scale, x_qsum, packed, w_scale, return_acc: bool = False, out=None,
+                      acc_out=None):
+    """FP4 x FP6 contraction + dequantisation (bitnet_linear_forward_f6); returns y
+    float32 [M][N], or (y, acc int32 [M][N]) when return_acc."""
+    torch = _torch()
+    _require(xq6, "xq6", torch.uint8, 2)
+    _require(packed, "packed", torch.uint8, 2)
+    _require(w_scale, "w_scale", torch.float32, 1)
+    M = xq6.shape[0]
+    K = xq6.shape[1] // 3 * 4
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=xq6.device)
+    if return_acc and acc_out is None:
+        acc_out = torch.empty((M, N), dtype=torch.int32, device=xq6.device)
+    _check(lib().bitnet_linear_forward_f6(_ptr(xq6), _ptr(x_scale), _ptr(x_qsum), _ptr(packed),
+                                          _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out),
+                                          _stream(xq6.device)))
+    return (out, acc_out) if acc_out is not None else out
 
 
 def linear_forward(xq, x_scale, x_qsum, packed, w_scale, return_acc: bool = False, out=None,

@@ -149,6 +149,43 @@ int bitnet_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, i
                       fn);
 }
 
+int bitnet_hadamard_quant_act_f6(const uint16_t* x, const float* gain, float eps, int64_t M,
+                                 int64_t K, uint8_t* xq6, float* x_scale, int32_t* x_qsum,
+                                 void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_hadamard_quant_act_f6";
+    int s = validate_quant(x, gain, eps, M, K, reinterpret_cast<int8_t*>(xq6), x_scale, x_qsum,
+                           true, fn);
+    if (s != BITNET_OK || M == 0) return s;
+    return hip_status(bitnet::launch_hadamard_quant_act_f6(x, gain, eps, M, K, std::sqrt((double)K),
+                                                           xq6, x_scale, x_qsum,
+                                                           (hipStream_t)stream),
+                      fn);
+}
+
+int bitnet_linear_forward_f6(const uint8_t* xq6, const float* x_scale, const int32_t* x_qsum,
+                             const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, float* y, int32_t* acc, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_linear_forward_f6";
+    if (M < 0 || M > kMaxRows || N < 0 || N > kMaxRows)
+        return fail(BITNET_ERR_SHAPE, "%s: M=%lld or N=%lld out of range", fn, (long long)M, (long long)N);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!xq6 || !x_scale || !x_qsum || !packed || !w_scale || !y)
+        return fail(BITNET_ERR_NULL, "%s: only acc may be NULL", fn);
+    if (!aligned(xq6, 16) || !aligned(packed, 16))
+        return fail(BITNET_ERR_ALIGN, "%s: xq6 and packed must be 16-byte aligned", fn);
+    if (!aligned(x_scale, 4) || !aligned(x_qsum, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+        (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "%s: scales, sums, y and acc must be 4-byte aligned", fn);
+    return hip_status(bitnet::launch_gemm_f6(xq6, x_scale, x_qsum, packed,
+                                             bitnet::single_group(w_scale, N), M, N, K, y, acc,
+                                             (hipStream_t)stream),
+                      fn);
+}
+
 int bitnet_linear_forward(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                           const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                           int64_t K, float* y, int32_t* acc, void* stream) {

@@ -41,6 +41,8 @@
 // with its own L2); the launch index is remapped so that each XCD works on a
 // contiguous range of tiles, ordered in groups of 8 token tiles per weight
 // tile column, so concurrently running blocks on one XCD share operands in L2.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -57,19 +59,28 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9-family raw buffer descr
 constexpr uint32_t kOutOfRange = 0x80000000u;    // offset past any block's buffer: loads 0
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int BN_, int BM_, int WN_, int WM_, int OCC_, int S_ = 2>
+template <int BN_, int BM_, int WN_, int WM_, int OCC_, int S_ = 2, bool F6_ = false>
 struct GemmCfg {
     static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
     static constexpr int S = S_;                    // LDS stage buffers (S - 1 stages in flight)
+    // Activation format: int8 codes, or 6-bit E3M2 codes (F6: 192 bytes per
+    // row per stage, padded to 208 in LDS so 16-byte reads of 16 consecutive
+    // rows fall in distinct bank groups).
+    static constexpr bool F6 = F6_;
+    static constexpr int X_ROW = F6 ? 208 : kBK;     // LDS bytes per activation row
+    static constexpr int X_ROW_SLOTS = X_ROW / 16;
+    static constexpr int STEPS = F6 ? 4 : 8;         // MFMA K steps per stage (64 or 32 K each)
     static constexpr int OCC = OCC_;                // workgroups per CU the tile is sized for
     static constexpr int NT = WN * WM * kWave;
     static constexpr int TN = BN / WN, TM = BM / WM;
     static constexpr int FN = TN / 32, FM = TM / 32;
-    static constexpr int X_STAGE = BM * kBK;         // bytes
+    static constexpr int X_STAGE = BM * X_ROW;       // bytes
     static constexpr int W_STAGE = BN * (kBK / 4);   // bytes
-    static constexpr int X_SLOTS = BM * 16;          // 16-byte slots per stage
+    static constexpr int X_SLOTS = BM * X_ROW_SLOTS; // 16-byte slots per stage
     static constexpr int W_SLOTS = BN * 4;
     static constexpr int XL = (X_SLOTS + NT - 1) / NT;
     static constexpr int WL = (W_SLOTS + NT - 1) / NT;
@@ -85,6 +96,22 @@ struct GemmCfg {
     static_assert(S >= 2 && (S - 2) * (XL + WL) <= 63, "vmcnt range");
     static_assert(NT <= 1024, "workgroup size");
 };
+
+// Two packed words (32 offset codes c = q + 1, weights 0..15 in w and 16..31
+// in w2) -> 32 FP4 (E2M1) values 2 c / 2 = c, i.e. nibble 2 c: code c of
+// weight 4 d + b of w goes to nibble 2 b of dword d, that of w2 to nibble
+// 2 b + 1.  FP4 holds 0, 1 and 2 exactly.
+__device__ __forceinline__ v8i unpack_fp4(uint32_t w, uint32_t w2) {
+    v8i r = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        r[d] = (int)((((w >> (2 * d)) & 0x03030303u) << 1) | (((w2 >> (2 * d)) & 0x03030303u) << 5));
+    return r;
+}
+
+constexpr int kFmtFp4 = 4;      // MFMA operand format selector: FP4 E2M1
+constexpr int kFmtE3M2 = 3;     // MFMA operand format selector: 6-bit E3M2
+constexpr int kScaleOne = 127;  // E8M0 block scale 2^0
 
 __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
     v4i r;
@@ -109,6 +136,11 @@ __device__ __forceinline__ void stage_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Activation codes as 6-bit E3M2 floats (the f6 format), for the FP4 x FP6
+// matrix core: a 32-value group is 24 bytes; value p of the group (bits 6p ..
+// 6p+5 of its little-endian 192-bit word) is the code at K offset
+// 16 (p % 2) + 4 (p / 8) + (p % 8) / 2, the order in which the packed weights
+// unpack into FP4 nibbles below.
 template <class C>
 __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     const int8_t* __restrict__ X, const uint8_t* __restrict__ P, const float* __restrict__ x_scale,
@@ -141,8 +173,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     // Buffer resources cover only this block's valid rows.
     const int x_rows = (int)min((int64_t)C::BM, (int64_t)M - m0);
     const int w_rows = (int)min((int64_t)C::BN, (int64_t)N - n0);
+    const int x_row_bytes = C::F6 ? K / 4 * 3 : K;   // activation bytes per token in HBM
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(X + m0 * K), (short)0, x_rows * K, (int)kBufferWord3);
+        (void*)(X + m0 * x_row_bytes), (short)0, x_rows * x_row_bytes, (int)kBufferWord3);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(P + n0 * row_bytes), (short)0, w_rows * row_bytes, (int)kBufferWord3);
 
@@ -156,9 +189,17 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
             const int base = idx * C::NT + wave * kWave;   // wave-uniform
             if (base < C::X_SLOTS) {
                 const int p = base + lane;
-                const int r = p >> 4, s = (p & 15) ^ (r & 15);
-                const int k = k0 + 16 * s;
-                const uint32_t off = k < K ? (uint32_t)(r * K + k) : kOutOfRange;
+                uint32_t off;
+                if constexpr (C::F6) {
+                    // 12 data slots and one padding slot per row, in order.
+                    const int r = p / C::X_ROW_SLOTS, s = p % C::X_ROW_SLOTS;
+                    const int b = k0 / 4 * 3 + 16 * s;             // byte in the token's row
+                    off = (s < 12 && b < x_row_bytes) ? (uint32_t)(r * x_row_bytes + b) : kOutOfRange;
+                } else {
+                    const int r = p >> 4, s = (p & 15) ^ (r & 15);
+                    const int k = k0 + 16 * s;
+                    off = k < K ? (uint32_t)(r * K + k) : kOutOfRange;
+                }
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)&lds[buf][base * 16], 16,
                                                          (int)off, 0, 0, 0);
             }
@@ -175,7 +216,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
         }
     };
 
-    v16i acc[C::FN][C::FM];
+    using Acc = typename std::conditional<C::F6, v16f, v16i>::type;
+    Acc acc[C::FN][C::FM];
 #pragma unroll
     for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -202,24 +244,57 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
                     &ws[r * 64 + 16 * ((2 * fh + p) ^ w_swizzle(r))]);
         }
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            v4i b[C::FM];
-#pragma unroll
-            for (int j = 0; j < C::FM; ++j) {
-                const int r = wm * C::TM + j * 32 + fr;
-                b[j] = *reinterpret_cast<const v4i*>(&xs[r * kBK + 16 * ((8 * fh + st) ^ (r & 15))]);
-            }
+        for (int st = 0; st < C::STEPS; ++st) {
+            // Waves on one SIMD are otherwise served oldest first, so within a
+            // stage the youngest wave finishes last while the others wait at
+            // the barrier with the matrix core half idle.  Lowering a wave's
+            // priority as it advances through the stage lets the waves that
+            // are behind catch up (measured: about 4% on the prefill shape).
+            if (st == 0) __builtin_amdgcn_s_setprio(3);
+            if (st == C::STEPS / 4) __builtin_amdgcn_s_setprio(2);
+            if (st == C::STEPS / 2) __builtin_amdgcn_s_setprio(1);
+            if (st == 3 * C::STEPS / 4) __builtin_amdgcn_s_setprio(0);
             if (has_next) {
 #pragma unroll
                 for (int idx = 0; idx < kLoads; ++idx)
-                    if (idx * 4 / kLoads == st) issue_one(nbuf, next_k0, idx);
+                    if (idx * (C::STEPS / 2) / kLoads == st) issue_one(nbuf, next_k0, idx);
             }
+            if constexpr (C::F6) {
+                // K step st of lane half fh: packed words 8 fh + 2 st and 8 fh + 2 st + 1
+                // (64 consecutive K values per step over the two halves) against the
+                // activation group 4 fh + st (24 bytes).
+                v8i b[C::FM];
 #pragma unroll
-            for (int i = 0; i < C::FN; ++i) {
-                const v4i a = unpack_codes(wv[i][st / 4][st % 4]);
+                for (int j = 0; j < C::FM; ++j) {
+                    const int r = wm * C::TM + j * 32 + fr;
+                    const uint2* src = reinterpret_cast<const uint2*>(&xs[r * C::X_ROW + 96 * fh + 24 * st]);
+                    const uint2 q0 = src[0], q1 = src[1], q2 = src[2];
+                    b[j] = v8i{(int)q0.x, (int)q0.y, (int)q1.x, (int)q1.y, (int)q2.x, (int)q2.y, 0, 0};
+                }
 #pragma unroll
-                for (int j = 0; j < C::FM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j], acc[i][j], 0, 0, 0);
+                for (int i = 0; i < C::FN; ++i) {
+                    const uint32_t w = wv[i][st / 2][2 * (st % 2)];
+                    const uint32_t w2 = wv[i][st / 2][2 * (st % 2) + 1];
+                    const v8i a = unpack_fp4(w, w2);
+#pragma unroll
+                    for (int j = 0; j < C::FM; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a, b[j], acc[i][j], kFmtFp4, kFmtE3M2, 0, kScaleOne, 0, kScaleOne);
+                }
+            } else {
+                v4i b[C::FM];
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j) {
+                    const int r = wm * C::TM + j * 32 + fr;
+                    b[j] = *reinterpret_cast<const v4i*>(&xs[r * kBK + 16 * ((8 * fh + st) ^ (r & 15))]);
+                }
+#pragma unroll
+                for (int i = 0; i < C::FN; ++i) {
+                    const v4i a = unpack_codes(wv[i][st / 4][st % 4]);
+#pragma unroll
+                    for (int j = 0; j < C::FM; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b[j], acc[i][j], 0, 0, 0);
+                }
             }
         }
     };
@@ -271,8 +346,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
                     for (int q = 0; q < 4; ++q) {
                         const int nl = i * 32 + 8 * q + 4 * fh;   // wave-local output column
                         const int64_t ng = n0 + wn * C::TN + nl;   // its global column
-                        const v4i a = v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                          acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]} -
+                        // (the FP4 x FP6 sums are exact integers in float32)
+                        const v4i a = v4i{(int)acc[i][j][4 * q], (int)acc[i][j][4 * q + 1],
+                                          (int)acc[i][j][4 * q + 2], (int)acc[i][j][4 * q + 3]} -
                                       v4i{qs, qs, qs, qs};
                         // Columns past N read row N-1's scale; they are never stored.
                         float4 v;
@@ -442,6 +518,10 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_q
 using CfgLarge = GemmCfg<448, 128, 7, 2, 1>;   // 14 waves, wave tile 64 x 64, 120 KiB LDS
 using CfgMid = GemmCfg<256, 128, 4, 2, 1>;     // 8 waves, wave tile 64 x 64, 96 KiB LDS
 using CfgTiny = GemmCfg<64, 64, 2, 2, 2>;      // 4 waves, wave tile 32 x 32, 40 KiB LDS
+// The same tiles with 6-bit activations (FP4 x FP6 matrix core).
+using CfgLargeF6 = GemmCfg<448, 128, 7, 2, 1, 2, true>;
+using CfgMidF6 = GemmCfg<256, 128, 4, 2, 1, 2, true>;
+using CfgTinyF6 = GemmCfg<64, 64, 2, 2, 2, 2, true>;
 
 constexpr int64_t kCus = 256;
 
@@ -466,6 +546,18 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_
     if (tiles_of<CfgMid>(M, N) >= kCus)
         return launch_cfg<CfgMid>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     return launch_cfg<CfgTiny>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+}
+
+hipError_t launch_gemm_f6(const uint8_t* xq6, const float* x_scale, const int32_t* x_qsum,
+                          const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    const int8_t* x = reinterpret_cast<const int8_t*>(xq6);
+    if (tiles_of<CfgLargeF6>(M, N) >= 2 * kCus)
+        return launch_cfg<CfgLargeF6>(x, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    if (tiles_of<CfgMidF6>(M, N) >= kCus)
+        return launch_cfg<CfgMidF6>(x, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    return launch_cfg<CfgTinyF6>(x, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
 }
 
 }  // namespace bitnet

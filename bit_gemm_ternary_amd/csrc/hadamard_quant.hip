@@ -113,7 +113,21 @@ __device__ __forceinline__ void load_bf16(const uint16_t* p, float (&v)[E]) {
     }
 }
 
-template <int P, int E>
+// int4 code v in [-8, 7] as a 6-bit E3M2 float (sign, 3 exponent bits with
+// bias 3, 2 mantissa bits), exact for every such integer.
+__device__ __forceinline__ uint32_t e3m2_of_int(int v) {
+    const uint32_t a = (uint32_t)(v < 0 ? -v : v);
+    if (a == 0) return 0;
+    const int l = 31 - __clz(a);                       // floor(log2 a): 0 .. 3
+    const uint32_t m = ((a << 2) >> l) & 3u;
+    return (v < 0 ? 0x20u : 0u) | ((uint32_t)(l + 3) << 2) | m;
+}
+
+// F6 = false: int8 codes, xq [M][K].  F6 = true: 6-bit E3M2 codes, xq
+// [M][K/4*3] bytes, 32 values per 24-byte group; value p of a group is the
+// code at K offset 16 (p % 2) + 4 (p / 8) + (p % 8) / 2 (the order in which the
+// FP4 x FP6 contraction unpacks the weights).
+template <int P, int E, bool F6>
 __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps, double sqrt_k,
     int8_t* __restrict__ xq, float* __restrict__ x_scale, int32_t* __restrict__ x_qsum) {
@@ -180,6 +194,26 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
     qs = wave_sum_dpp(qs);
     if (lane == 0) red_i[wave] = qs;
     __syncthreads();
+    if constexpr (F6) {
+        uint2* row = reinterpret_cast<uint2*>(xq + m * (K / 4 * 3));
+        for (int g = t; g < K / 32; g += F::B) {
+            const uint4 c0 = reinterpret_cast<const uint4*>(lds8 + 32 * g)[0];
+            const uint4 c1 = reinterpret_cast<const uint4*>(lds8 + 32 * g)[1];
+            const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            uint32_t out[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int p = 0; p < 32; ++p) {
+                const int k = 16 * (p % 2) + 4 * (p / 8) + (p % 8) / 2;
+                const int v = (int)(int8_t)(cw[k / 4] >> (8 * (k % 4)));
+                const uint64_t f = (uint64_t)e3m2_of_int(v) << ((6 * p) % 32);
+                out[(6 * p) / 32] |= (uint32_t)f;
+                if ((6 * p) % 32 > 26) out[(6 * p) / 32 + 1] |= (uint32_t)(f >> 32);
+            }
+            row[3 * g] = make_uint2(out[0], out[1]);
+            row[3 * g + 1] = make_uint2(out[2], out[3]);
+            row[3 * g + 2] = make_uint2(out[4], out[5]);
+        }
+    } else {
     int8_t* dst = xq + m * K + (int64_t)t * E;
     if constexpr (E >= 16) {
 #pragma unroll
@@ -189,6 +223,7 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
         *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(lds8 + t * E);
     } else {
         *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds8 + t * E);
+    }
     }
 
     if (t == 0) {
@@ -243,12 +278,36 @@ constexpr int elems_per_thread() {
     return P >= 13 ? 32 : (P >= 10 ? 16 : (1 << P) / 64);
 }
 
-template <int P>
+int log2_exact(int64_t k) {
+    int p = 0;
+    while ((int64_t{1} << p) < k) ++p;
+    return p;
+}
+
+template <int P, bool F6>
 hipError_t launch_hq(const uint16_t* x, const float* gain, float eps, int64_t M, double sqrt_k,
                      int8_t* xq, float* x_scale, int32_t* x_qsum, hipStream_t stream) {
     constexpr int E = elems_per_thread<P>();
-    return launch_kernel((hadamard_quant_kernel<P, E>), dim3((unsigned)M), dim3(Fwht<P, E>::B), 0,
-                       stream, x, gain, eps, sqrt_k, xq, x_scale, x_qsum);
+    return launch_kernel((hadamard_quant_kernel<P, E, F6>), dim3((unsigned)M),
+                         dim3(Fwht<P, E>::B), 0, stream, x, gain, eps, sqrt_k, xq, x_scale, x_qsum);
+}
+
+template <bool F6>
+hipError_t launch_hq_k(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
+                       double sqrt_k, int8_t* xq, float* x_scale, int32_t* x_qsum,
+                       hipStream_t stream) {
+    if (M == 0) return hipSuccess;
+    switch (log2_exact(K)) {
+        case 8: return launch_hq<8, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 9: return launch_hq<9, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 10: return launch_hq<10, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 11: return launch_hq<11, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 12: return launch_hq<12, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 13: return launch_hq<13, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 14: return launch_hq<14, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 15: return launch_hq<15, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int P>
@@ -258,29 +317,20 @@ hipError_t launch_rows(const float* src, float* dst, int64_t N, hipStream_t stre
                        src, dst);
 }
 
-int log2_exact(int64_t k) {
-    int p = 0;
-    while ((int64_t{1} << p) < k) ++p;
-    return p;
-}
 
 }  // namespace
 
 hipError_t launch_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
                                      int64_t K, double sqrt_k, int8_t* xq, float* x_scale,
                                      int32_t* x_qsum, hipStream_t stream) {
-    if (M == 0) return hipSuccess;
-    switch (log2_exact(K)) {
-        case 8: return launch_hq<8>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 9: return launch_hq<9>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 10: return launch_hq<10>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 11: return launch_hq<11>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 12: return launch_hq<12>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 13: return launch_hq<13>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 14: return launch_hq<14>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 15: return launch_hq<15>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_hq_k<false>(x, gain, eps, M, K, sqrt_k, xq, x_scale, x_qsum, stream);
+}
+
+hipError_t launch_hadamard_quant_act_f6(const uint16_t* x, const float* gain, float eps,
+                                        int64_t M, int64_t K, double sqrt_k, uint8_t* xq6,
+                                        float* x_scale, int32_t* x_qsum, hipStream_t stream) {
+    return launch_hq_k<true>(x, gain, eps, M, K, sqrt_k, reinterpret_cast<int8_t*>(xq6), x_scale,
+                             x_qsum, stream);
 }
 
 hipError_t launch_fwht_rows_f32(const float* src, float* dst, int64_t N, int64_t K,

@@ -46,6 +46,11 @@ hipError_t launch_quant_act(const uint16_t* x, const float* gain, float eps, int
 hipError_t launch_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
                                      int64_t K, double sqrt_k, int8_t* xq, float* x_scale,
                                      int32_t* x_qsum, hipStream_t stream);
+// The same codes written as 6-bit E3M2 floats, 24 bytes per 32 values
+// (xq6: [M][K / 4 * 3] bytes), in the order the FP4 x FP6 contraction reads.
+hipError_t launch_hadamard_quant_act_f6(const uint16_t* x, const float* gain, float eps,
+                                        int64_t M, int64_t K, double sqrt_k, uint8_t* xq6,
+                                        float* x_scale, int32_t* x_qsum, hipStream_t stream);
 // Row-wise unnormalised Walsh-Hadamard transform of float32 [N][K] (K = 2^p,
 // 256 <= K <= 32768), used for the weight pre-rotation.
 hipError_t launch_fwht_rows_f32(const float* src, float* dst, int64_t N, int64_t K,
@@ -95,5 +100,10 @@ hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                        const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream);
+// The contraction with 6-bit E3M2 activation codes (bitnet_hadamard_quant_act_f6
+// layout) on the FP4 x FP6 matrix core; any M.
+hipError_t launch_gemm_f6(const uint8_t* xq6, const float* x_scale, const int32_t* x_qsum,
+                          const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc, hipStream_t stream);
 
 }  // namespace bitnet

@@ -149,6 +149,24 @@ int bitnet_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, i
                               void* stream);
 
 /*
+ * H-BitLinear activations as true 4-bit-range floats ([V2] "방법론": 4-bit
+ * activations for hardware with low-bit arithmetic).  Same computation and
+ * codes as bitnet_hadamard_quant_act, written as 6-bit E3M2 floats (sign,
+ * 3 exponent bits with bias 3, 2 mantissa bits), which hold every integer in
+ * [-8, 8] exactly:
+ *
+ *   xq6   out  uint8 [M][K/4*3], 16-byte aligned (x_scale, x_qsum as before).
+ *              Each group of 32 consecutive K values takes 24 bytes; value p of
+ *              the group (bits 6p .. 6p+5 of its little-endian 192-bit word) is
+ *              the code at K offset 16 (p % 2) + 4 (p / 8) + (p % 8) / 2.
+ *
+ * Consumed by bitnet_linear_forward_f6.  K a power of two in [256, 32768].
+ */
+int bitnet_hadamard_quant_act_f6(const uint16_t* x, const float* gain, float eps, int64_t M,
+                                 int64_t K, uint8_t* xq6, float* x_scale, int32_t* x_qsum,
+                                 void* stream);
+
+/*
  * Ternary integer contraction + dequantisation ([FT] "계산 패러다임",
  * "추론 최적화 및 커스텀 커널", "양자화 메커니즘" rescale; [QP] dequantise).
  *
@@ -166,6 +184,21 @@ int bitnet_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, i
 int bitnet_linear_forward(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                           const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                           int64_t K, float* y, int32_t* acc, void* stream);
+
+/*
+ * Contraction + dequantisation with 6-bit activation codes (the xq6 layout of
+ * bitnet_hadamard_quant_act_f6) on the FP4 x FP6 matrix cores ([V2] "방법론";
+ * [FT] "계산 패러다임").  The offset weight codes q + 1 (0, 1, 2) are exact in
+ * FP4 E2M1, the activation codes in E3M2, and every partial sum is an integer
+ * below 2^24 in magnitude, so the float32 accumulation is exact: acc and y are
+ * bit-identical to bitnet_linear_forward on the int8 codes.
+ *
+ *   xq6, x_scale, x_qsum  in  outputs of bitnet_hadamard_quant_act_f6.
+ *   other arguments           as bitnet_linear_forward (K a multiple of 64).
+ */
+int bitnet_linear_forward_f6(const uint8_t* xq6, const float* x_scale, const int32_t* x_qsum,
+                             const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, float* y, int32_t* acc, void* stream);
 
 /*
  * Fused BitLinear forward: bitnet_quant_act followed by bitnet_linear_forward

@@ -185,3 +185,23 @@ def test_grouped_forward_argument_errors(L):
     assert _grouped(L, ws=BAD) == 4
     assert _grouped(L, acc=BAD) == 4
     assert _grouped(L, M=0, x=0, P=0, y=0) == 0
+
+
+def test_f6_argument_errors(L):
+    q = lambda **kw: _quant(L, "bitnet_hadamard_quant_act_f6", **kw)
+    assert q(K=384) == 3          # not a power of two
+    assert q(M=-1) == 2
+    assert q(x=0) == 1
+    assert q(xq=BAD) == 4
+
+    def fwd(xq=A16, sx=A4, qs=A4, P=A16, ws=A4, M=4, N=8, K=256, y=A4, acc=None):
+        return L.bitnet_linear_forward_f6(ctypes.c_void_p(xq), ctypes.c_void_p(sx),
+                                          ctypes.c_void_p(qs), ctypes.c_void_p(P),
+                                          ctypes.c_void_p(ws), M, N, K, ctypes.c_void_p(y),
+                                          None if acc is None else ctypes.c_void_p(acc), None)
+    assert fwd(K=100) == 2
+    assert fwd(M=-1) == 2
+    assert fwd(xq=0) == 1
+    assert fwd(xq=A4) == 4
+    assert fwd(acc=BAD) == 4
+    assert fwd(M=0, xq=0) == 0

@@ -394,3 +394,73 @@ def test_pack_weights_grouped_matches_single_packs(orc, dev):
     want = [orc.pack_weights(W) for W in Ws]
     np.testing.assert_array_equal(host(packed), np.concatenate([p for p, *_ in want]))
     np.testing.assert_array_equal(host(w_scales), np.array([[d, s] for _, d, s, _ in want], np.float32))
+
+
+# ---------------------------------------------------------------------------
+# True 4-bit H path: 6-bit E3M2 activation codes, FP4 x FP6 matrix cores.
+# ---------------------------------------------------------------------------
+
+import f6_layout  # noqa: E402  (host encoder/decoder of the xq6 layout)
+
+
+@pytest.mark.parametrize("M,K,with_gain", [(1, 256, False), (7, 4096, True), (512, 4096, False),
+                                            (33, 16384, False), (2, 32768, True)])
+def test_hadamard_quant_act_f6(orc, dev, M, K, with_gain):
+    x = _activation(M, K, seed=1400 + M, dist="student_t")
+    gain = np.random.default_rng(K).uniform(0.5, 1.5, K).astype(np.float32) if with_gain else None
+    wq, wdx, wqs = orc.hadamard_quant_act(x, gain=gain)
+    xq6, xs, qs = bt.hadamard_quant_act_f6(bf16_to_dev(x, dev),
+                                           None if gain is None else to_dev(gain, dev))
+    got = f6_layout.decode(host(xq6), K)
+    # the GPU keeps the transform's float order, so the codes match exactly
+    np.testing.assert_array_equal(got, wq)
+    np.testing.assert_array_equal(host(qs), wqs)
+    assert_close_rel(host(xs), wdx)
+
+
+F6_FORWARD_CASES = [
+    (1, 100, 256), (3, 77, 4096), (64, 333, 1024), (200, 900, 2048), (100, 250, 320),
+    (2100, 14000, 256),   # 448 x 128 tiles
+    (2000, 4100, 192),    # 256 x 128 tiles, K not a multiple of the 256-deep stage
+    (512, 4096, 64),
+]
+
+
+@pytest.mark.parametrize("M,N,K", F6_FORWARD_CASES)
+def test_linear_forward_f6(orc, dev, M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    codes = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    codes[0, :] = 0                                   # an all-zero token
+    if M > 2:
+        codes[1, :] = -8                              # extreme codes
+    W = synth.weights(N, K, seed=1500 + N % 97)
+    packed, d_w, _, _ = orc.pack_weights(W)
+    d_x = rng.uniform(1e-3, 1e-2, M).astype(np.float32)
+    qsum = codes.astype(np.int64).sum(axis=1).astype(np.int32)
+    want_acc, want_y = orc.linear_forward(codes, d_x, packed, d_w, K)
+    y, acc = bt.linear_forward_f6(to_dev(f6_layout.encode(codes), dev), to_dev(d_x, dev),
+                                  to_dev(qsum, dev), to_dev(packed, dev),
+                                  to_dev(np.array([d_w, 0], np.float32), dev), return_acc=True)
+    np.testing.assert_array_equal(host(acc), want_acc)
+    assert_close_rel(host(y), want_y)
+
+
+def test_h_bitlinear_f6_matches_int8_path(orc, dev):
+    """Full H-BitLinear at the benchmark shape: the f6 path gives the int8 path's
+    accumulators and outputs bit for bit, and both match the oracle on samples."""
+    M, N, K = 512, 4096, 4096
+    W = synth.weights(N, K, 1600)
+    x_bits = _activation(M, K, 1601, dist="student_t")
+    x = bf16_to_dev(x_bits, dev)
+    packed, w_scale = bt.pack_weights(to_dev(W, dev), hadamard=True)
+    xq, xs, qs = bt.hadamard_quant_act(x)
+    y8, acc8 = bt.linear_forward(xq, xs, qs, packed, w_scale, return_acc=True)
+    xq6, xs6, qs6 = bt.hadamard_quant_act_f6(x)
+    y6, acc6 = bt.linear_forward_f6(xq6, xs6, qs6, packed, w_scale, return_acc=True)
+    np.testing.assert_array_equal(host(acc6), host(acc8))
+    np.testing.assert_array_equal(host(y6), host(y8))
+    wq, _, _ = orc.hadamard_quant_act(x_bits)
+    rng = np.random.default_rng(3)
+    rows, cols = rng.integers(0, M, 2000), rng.integers(0, N, 2000)
+    want = orc.int_gemm_sampled(wq, host(packed), K, rows, cols)
+    np.testing.assert_array_equal(host(acc6)[rows, cols], want)
