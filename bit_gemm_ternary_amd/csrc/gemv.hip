@@ -8,412 +8,499 @@
 // registers (section 추론 최적화 및 커스텀 커널: weights unpacked on the fly
 // inside the matmul).
 //
-// Mapping: a wavefront owns up to 64 consecutive output rows, processed in
-// batches of RB rows whose loads are all issued before any of them is used.
-// Lane l owns the 16-byte packed chunks l, l+64, ... of every row (64 weights
-// per chunk), so a wave reads 1 KiB of a row per load instruction, fully
-// coalesced.  The matching 64 activation bytes per chunk stay in registers.
+// Mapping: wave g of the W waves in the grid owns the weight rows g, g + W,
+// g + 2W, ...  (interleaved, so the waves of the whole chip stream one
+// contiguous stretch of the matrix at a time).  A wave's rows are processed in
+// batches of RB rows whose loads are all in flight together: one batch when the
+// wave owns at most RB rows, else two register sets that alternate (the loads of
+// the next batch are issued before the current one is used).  Lane l owns the
+// 16-byte chunks l, l + 64, ... of every row (64 weights per chunk), so one load
+// instruction reads 1 KiB of a row, fully coalesced; the matching activation
+// codes stay in registers for all rows.
 //
 // Unpack: a packed word holds weights 16g..16g+15; with the field of weight
 // 16g+4i+b at bits 8b+2i, (word & (3 << 2i) per byte) gives the four codes
 // (q+1) of weights 16g+4i..16g+4i+3 times 4^i, in byte order, which
 // v_dot4_i32_i8 multiplies with the activation dword 4g+i.  Slots i = 0, 1, 2
 // need only the mask (codes times 1, 4, 16 fit a signed byte); slot 3 is shifted
-// down first.  The four slot sums are combined exactly as s0 + s1/4 + s2/16 + s3.
-// The offset code q + 1 is corrected at the end: sum q x = sum (q+1) x - sum x.
+// down first.  Slots 0 and 3 share an accumulator; the three sums are combined
+// exactly as s03 + s1/4 + s2/16.  The offset code q + 1 is corrected at the end:
+// sum q x = sum (q+1) x - sum x.
 //
-// Fused variant: each 256-thread workgroup first quantises the (<= 4) tokens
-// itself (RMSNorm + absmax int8, the same arithmetic as quant_act.hip) from the
-// bf16 input, which every workgroup reads from L2, and shares the codes through
-// LDS; the weight loads of the first batch are issued right after the
-// activation loads and stay in flight through that prologue.  This removes the
-// separate quantisation launch from the decode critical path.
+// Row totals: after a batch every lane holds one partial sum per (row, token),
+// NV = RB * MT values.  A transposing butterfly over the lane-index bits
+// (v_permlane32_swap, v_permlane16_swap, then DPP moves inside 16-lane rows)
+// halves the number of values per lane at each step while adding pairs, so all
+// NV totals cost about 2 NV + 12 lane operations rather than NV separate wave
+// reductions; lane L then holds the total of value L >> (6 - log2 NV).
+//
+// Loads use buffer resources: an out-of-range offset returns zeros, so the tail
+// rows and chunks need no branches and the compiler counts the loads of a batch
+// exactly when it waits for the first of them.  The wave index is made
+// wave-uniform explicitly, so the row bookkeeping lives in scalar registers.
+//
+// Fused variant: each workgroup first quantises the (<= 4) tokens itself
+// (RMSNorm + absmax int8, the arithmetic of quant_act.hip) from the bf16 input,
+// which every workgroup reads from L2, and shares the codes through LDS.  The
+// activation (and gain) loads are issued first and the first weight batch right
+// after them, so the weight stream is in flight through that prologue.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace bitnet {
 namespace {
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvWaves = kGemvThreads / kWave;
-constexpr int kMaxXRegsChunks = 8;
-// Fused decode launch shape: 256-thread workgroups, about 1024 waves in all
-// (measured on the decode projections against 512- and 1024-thread
-// workgroups and 2048 or 4096 waves).
-constexpr int kFusedThreads = 256;
-constexpr int kFusedWaves = 1024;  // MT * CH limit: 16 * MT * CH activation VGPRs
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
+constexpr uint32_t kOutOfRange = 0x80000000u;   // offset past every buffer used here: loads 0
+constexpr int kMaxRecords = 0x7fffffff;         // buffer size used for the weight batches
+constexpr int kMaxXRegsChunks = 8;              // MT * CH limit: 16 * MT * CH code VGPRs
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-// Rows per batch: all loads of a batch are in flight together (4*RB*CH VGPRs).
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t res, uint32_t off) {
+    const v4i q = __builtin_amdgcn_raw_buffer_load_b128(res, off, 0, 0);
+    return make_uint4((uint32_t)q[0], (uint32_t)q[1], (uint32_t)q[2], (uint32_t)q[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Transposing wave reduction.  tstep<M>(a, b): lanes with lane bit M clear keep
+// a, lanes with it set keep b, and each adds the copy of the kept value held by
+// a partner lane whose bit M differs (and whose higher bits agree).
+// ---------------------------------------------------------------------------
+template <int M>
+__device__ __forceinline__ int tstep(int a, int b, int lane) {
+    if constexpr (M == 32) {  // lanes 0-31 get (a, a of lane + 32), lanes 32-63 (b of lane - 32, b)
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        return (int)r[0] + (int)r[1];
+    } else if constexpr (M == 16) {  // the same between 16-lane rows 0|1 and 2|3
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        return (int)r[0] + (int)r[1];
+    } else if constexpr (M == 8) {  // row_ror:8 pairs lane ^ 8; banks 2, 3 are the lanes with bit 3
+        const int x = __builtin_amdgcn_update_dpp(a, b, 0x128, 0xF, 0xC, false);
+        const int y = __builtin_amdgcn_update_dpp(b, a, 0x128, 0xF, 0x3, false);
+        return x + y;
+    } else if constexpr (M == 4) {  // row_half_mirror pairs lane ^ 7; banks 1, 3 have bit 2
+        const int x = __builtin_amdgcn_update_dpp(a, b, 0x141, 0xF, 0xA, false);
+        const int y = __builtin_amdgcn_update_dpp(b, a, 0x141, 0xF, 0x5, false);
+        return x + y;
+    } else {  // quad_perm lane ^ 2 or lane ^ 1
+        constexpr int ctrl = M == 2 ? 0x4E : 0xB1;
+        const bool hi = (lane & M) != 0;
+        return (hi ? b : a) + __builtin_amdgcn_update_dpp(0, hi ? a : b, ctrl, 0xF, 0xF, false);
+    }
+}
+// Plain butterfly step: v plus the partner's v.
+template <int M>
+__device__ __forceinline__ int pstep(int v) {
+    if constexpr (M == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (int)r[0] + (int)r[1];
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (int)r[0] + (int)r[1];
+    } else {
+        constexpr int ctrl = M == 8 ? 0x128 : (M == 4 ? 0x141 : (M == 2 ? 0x4E : 0xB1));
+        return v + __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+    }
+}
+template <int M, int NV>
+__device__ __forceinline__ void xstage(int (&p)[NV], int& n, int lane) {
+    if (n > 1) {
+        const int h = n / 2;
+#pragma unroll
+        for (int i = 0; i < NV / 2; ++i)
+            if (i < h) p[i] = tstep<M>(p[i], p[i + h], lane);
+        n = h;
+    } else {
+        p[0] = pstep<M>(p[0]);
+    }
+}
+// Sums each of the NV values (a power of 2, <= 64) over the 64 lanes; afterwards
+// p[0] of lane L is the total of value L >> (6 - log2 NV).  The masks are taken
+// from the top lane bit down, so the transposing steps consume the high bits and
+// the plain steps pair lanes that hold the same value.
+template <int NV>
+__device__ __forceinline__ void xreduce(int (&p)[NV], int lane) {
+    int n = NV;
+    xstage<32>(p, n, lane);
+    xstage<16>(p, n, lane);
+    xstage<8>(p, n, lane);
+    xstage<4>(p, n, lane);
+    xstage<2>(p, n, lane);
+    xstage<1>(p, n, lane);
+}
+
+constexpr int log2_of(int v) { return v <= 1 ? 0 : 1 + log2_of(v / 2); }
+
+// Largest batch (rows in flight per register set) for CH chunks per lane.
 template <int CH>
-constexpr int rows_per_batch() {
+constexpr int max_batch() {
     return CH == 1 ? 16 : (CH == 2 ? 8 : (CH <= 4 ? 4 : 2));
 }
 
-// MT tokens, CH 16-byte chunks per lane per row (K <= CH * 4096).
-template <int MT, int CH>
-struct GemvCore {
-    static constexpr int RB = rows_per_batch<CH>();
-
-    // Loads of rows [r, r + RB) (zero beyond row1 or past the last chunk).
-    __device__ static __forceinline__ void load(uint4 (&w)[RB][CH], const uint8_t* packed,
-                                                int64_t row_bytes, int nchunk, int64_t r,
-                                                int64_t row1, int lane) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const int c = lane + kWave * j;
-                w[rb][j] = make_uint4(0, 0, 0, 0);
-                if (r + rb < row1 && c < nchunk)
-                    w[rb][j] = *reinterpret_cast<const uint4*>(packed + (r + rb) * row_bytes +
-                                                               16 * (int64_t)c);
-            }
-        }
-    }
-
-    // Dot products of one batch; the wave total of row r + rb lands in lane
-    // (r + rb - row0) of my_acc.
-    __device__ static __forceinline__ void compute(const uint4 (&w)[RB][CH],
-                                                   const uint32_t (&xv)[MT][CH][16], int64_t r,
-                                                   int64_t row0, int64_t row1, int lane,
-                                                   int (&my_acc)[MT]) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            if (r + rb >= row1) break;  // wave-uniform: the batch's last rows may be past row1
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-#pragma unroll
-                for (int j = 0; j < CH; ++j) {
-                    const uint32_t ws[4] = {w[rb][j].x, w[rb][j].y, w[rb][j].z, w[rb][j].w};
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const uint32_t word = ws[d];
-                        s0 = dot4(word & 0x03030303u, xv[t][j][4 * d + 0], s0);
-                        s1 = dot4(word & 0x0C0C0C0Cu, xv[t][j][4 * d + 1], s1);
-                        s2 = dot4(word & 0x30303030u, xv[t][j][4 * d + 2], s2);
-                        s3 = dot4((word >> 6) & 0x03030303u, xv[t][j][4 * d + 3], s3);
-                    }
-                }
-                const int total = wave_sum_dpp(s0 + (s1 >> 2) + (s2 >> 4) + s3);
-                if (lane == (int)(r + rb - row0)) my_acc[t] = total;
-            }
-        }
-    }
-
-    // Process rows [row0, row1) of this wave, the first batch already loaded in w.
-    __device__ static __forceinline__ void run(uint4 (&w)[RB][CH], const uint32_t (&xv)[MT][CH][16],
-                                               const uint8_t* packed, int64_t row_bytes,
-                                               int nchunk, int64_t row0, int64_t row1, int lane,
-                                               int (&my_acc)[MT]) {
-        for (int64_t r = row0; r < row1; r += RB) {
-            if (r != row0) load(w, packed, row_bytes, nchunk, r, row1, lane);
-            compute(w, xv, r, row0, row1, lane, my_acc);
-        }
-    }
-
-    // Epilogue: lane i writes row row0 + i.
-    __device__ static __forceinline__ void store(const int (&my_acc)[MT], const float* x_scale,
-                                                 const int32_t* x_qsum, const RowScales& scales,
-                                                 int64_t N, int64_t row0, int64_t row1, int lane,
-                                                 float* y, int32_t* acc_out) {
-        const int64_t r = row0 + lane;
-        if (r < row1) {
-            const float d_w = scales.of(r, scales.w_scale[0]);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int a = my_acc[t] - x_qsum[t];
-                if (acc_out != nullptr) acc_out[(int64_t)t * N + r] = a;
-                y[(int64_t)t * N + r] = ((float)a * x_scale[t]) * d_w;
-            }
-        }
-    }
+struct Args {
+    const uint16_t* x;       // fused: bf16 tokens [MT][K]
+    const float* gain;       // fused: [K] or NULL
+    float eps;
+    const int8_t* xq;        // standalone: codes [MT][K]
+    const float* x_scale;    // standalone: d_x [MT]
+    const int32_t* x_qsum;   // standalone: sum of codes [MT]
+    const uint8_t* packed;   // [N][K/4]
+    RowScales scales;
+    int N, K;
+    float* y;                // [MT][N]
+    int8_t* xq_out;          // fused: codes, scales and sums written by workgroup 0
+    float* x_scale_out;
+    int32_t* x_qsum_out;
+    int32_t* acc;            // [MT][N] or NULL
 };
 
-template <int MT, int CH>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
-    const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
-    const int32_t* __restrict__ x_qsum, const uint8_t* __restrict__ packed,
-    const RowScales scales, int N, int K, int rows_per_wave, float* __restrict__ y,
-    int32_t* __restrict__ acc_out) {
-    using G = GemvCore<MT, CH>;
-    const int lane = threadIdx.x % kWave;
-    const int wave = (int)((blockIdx.x * (int64_t)kGemvThreads + threadIdx.x) / kWave);
-    const int64_t row0 = (int64_t)wave * rows_per_wave;
-    if (row0 >= N) return;  // wave-uniform; no workgroup barrier in this kernel
-    const int64_t row1 = min((int64_t)N, row0 + rows_per_wave);
-    const int nchunk = K / 64;
-    const int64_t row_bytes = K / 4;
-
-    uint4 w[G::RB][CH];
-    G::load(w, packed, row_bytes, nchunk, row0, row1, lane);
-
-    // Activation bytes of my chunks: chunk c covers x[64c .. 64c+63].
-    uint32_t xv[MT][CH][16];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int c = lane + kWave * j;
-            const uint4* p = reinterpret_cast<const uint4*>(xq + (int64_t)t * K + 64 * (int64_t)c);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint4 a = make_uint4(0, 0, 0, 0);
-                if (c < nchunk) a = p[q];
-                xv[t][j][4 * q] = a.x;
-                xv[t][j][4 * q + 1] = a.y;
-                xv[t][j][4 * q + 2] = a.z;
-                xv[t][j][4 * q + 3] = a.w;
-            }
-        }
-    }
-
-    int my_acc[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) my_acc[t] = 0;
-    G::run(w, xv, packed, row_bytes, nchunk, row0, row1, lane, my_acc);
-    G::store(my_acc, x_scale, x_qsum, scales, N, row0, row1, lane, y, acc_out);
-}
-
-// Fused RMSNorm + int8 quantisation + GEMV.  Every workgroup quantises the MT
-// tokens (K <= CH * 4096) into LDS; workgroup 0 also writes the codes, scales
-// and sums to global memory.
-//
-// Order matters for latency: the bf16 activations are loaded first and the
-// weights second, so the prologue (which waits for its own loads, and loads
-// complete in issue order) does not wait for the weights; the weight loads
-// stay in flight through the prologue.  The prologue needs one workgroup
-// reduction (absmax and sum of squares of every token together); each wave
-// then sums the codes it reads back from LDS itself.
-template <int MT, int CH, int NT>
-__global__ __launch_bounds__(NT) void fused_decode_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
-    const uint8_t* __restrict__ packed, const RowScales scales, int N, int K,
-    int rows_per_wave, float* __restrict__ y, int8_t* __restrict__ xq_out,
-    float* __restrict__ x_scale_out, int32_t* __restrict__ x_qsum_out,
-    int32_t* __restrict__ acc_out) {
-    using G = GemvCore<MT, CH>;
+// MT tokens, CH 16-byte chunks per lane per row (K <= CH * 4096), NT threads,
+// RB rows per batch, MULTI: more than RB rows per wave.
+template <int MT, int CH, int NT, int RB, bool MULTI, bool FUSED>
+__global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     constexpr int NW = NT / kWave;
-    constexpr int XV = (CH * 512 + NT - 1) / NT;  // 8-value bf16 vectors per thread per token (K <= CH*4096)
-    __shared__ __align__(16) int8_t codes[MT][CH * 4096];
+    constexpr int MTP = MT == 3 ? 4 : MT;  // tokens per row in the reduction (a power of 2)
+    constexpr int NV = MTP * RB;
+    constexpr int LV = log2_of(NV);
+    constexpr int XV = (CH * 512 + NT - 1) / NT;  // 8-value bf16 vectors per thread per token
+    static_assert(NV <= kWave && (NV & (NV - 1)) == 0, "values per batch: a power of 2, <= 64");
+    __shared__ __align__(16) int8_t codes[MT][FUSED ? CH * 4096 : 16];
     __shared__ float red_f[MT][NW];
     __shared__ double red_d[MT][NW];
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
-    const int wave_id = t / kWave;
-    const int64_t row0 = ((int64_t)blockIdx.x * NW + wave_id) * rows_per_wave;
-    const int64_t row1 = min((int64_t)N, row0 + rows_per_wave);
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int g = (int)blockIdx.x * NW + wave;
+    const int W = (int)gridDim.x * NW;
+    const int N = a.N, K = a.K;
     const int nchunk = K / 64;
-    const int64_t row_bytes = K / 4;
-    const int nvec = K / 8;
+    const int row_bytes = K / 4;
+    const int nrows = g < N ? (int)(((int64_t)N - g + W - 1) / W) : 0;  // rows g + i W, i < nrows
+    const float dw0 = a.scales.w_scale[0];              // before any store (see RowScales::of)
 
-    // 1. Activation loads, then weight loads (in flight through the prologue).
-    uint4 raw[MT][XV];
+    // Weight loads of rows i0 .. i0 + RB - 1 of this wave (zeros past the last).
+    auto load = [&](uint4 (&w)[RB][CH], int i0) {
+        const int64_t r0 = i0 < nrows ? (int64_t)g + (int64_t)i0 * W : 0;
+        const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.packed + r0 * row_bytes), (short)0, kMaxRecords, (int)kBufferWord3);
 #pragma unroll
-    for (int tok = 0; tok < MT; ++tok) {
-        const uint4* xr = reinterpret_cast<const uint4*>(x + (int64_t)tok * K);
+        for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int i = 0; i < XV; ++i) {
-            const int v = t + NT * i;
-            raw[tok][i] = v < nvec ? xr[v] : make_uint4(0, 0, 0, 0);
-        }
-    }
-    uint4 w[G::RB][CH];
-    G::load(w, packed, row_bytes, nchunk, row0, row1, lane);
-
-    auto values = [&](int tok, int i, int v, float (&u)[8], bool with_gain) {
-        const uint32_t ws[4] = {raw[tok][i].x, raw[tok][i].y, raw[tok][i].z, raw[tok][i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            u[2 * e] = bf16_lo(ws[e]);
-            u[2 * e + 1] = bf16_hi(ws[e]);
-        }
-        if (with_gain && gain != nullptr) {
-            const float4 g0 = reinterpret_cast<const float4*>(gain)[2 * v];
-            const float4 g1 = reinterpret_cast<const float4*>(gain)[2 * v + 1];
-            u[0] *= g0.x; u[1] *= g0.y; u[2] *= g0.z; u[3] *= g0.w;
-            u[4] *= g1.x; u[5] *= g1.y; u[6] *= g1.z; u[7] *= g1.w;
+            for (int j = 0; j < CH; ++j) {
+                const int c = lane + kWave * j;
+                const uint32_t off = (i0 + rb < nrows && c < nchunk)
+                                         ? (uint32_t)(rb * W * row_bytes + 16 * c)
+                                         : kOutOfRange;
+                w[rb][j] = load16(res, off);
+            }
         }
     };
 
-    // 2. Per-token absmax of x*gain and sum of x^2: one workgroup reduction.
-#pragma unroll
-    for (int tok = 0; tok < MT; ++tok) {
-        float amax = 0.f;
-        double ss = 0.0;
-#pragma unroll
-        for (int i = 0; i < XV; ++i) {
-            const int v = t + NT * i;
-            if (v < nvec) {
-                float u[8];
-                values(tok, i, v, u, false);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss += (double)u[e] * (double)u[e];
-                values(tok, i, v, u, true);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(u[e]));
-            }
-        }
-        amax = wave_max_dpp(amax);
-        ss = wave_sum_dpp(ss);
-        if (lane == 0) {
-            red_f[tok][wave_id] = amax;
-            red_d[tok][wave_id] = ss;
-        }
-    }
-    __syncthreads();
-
-    // 3. Codes into LDS; every thread derives the same scales.  The dequant
-    // factor (which needs a double square root and division) is only computed
-    // in the epilogue, off the path to the contraction.
-    float tok_amax[MT];
-#pragma unroll
-    for (int tok = 0; tok < MT; ++tok) {
-        float amax = red_f[tok][0];
-#pragma unroll
-        for (int wv = 1; wv < NW; ++wv) amax = fmaxf(amax, red_f[tok][wv]);
-        tok_amax[tok] = amax;
-        const bool zero = amax < kTinyAbsmax;
-        const float scale = zero ? 0.f : 127.0f / amax;
-#pragma unroll
-        for (int i = 0; i < XV; ++i) {
-            const int v = t + NT * i;
-            if (v < nvec) {
-                float u[8];
-                values(tok, i, v, u, true);
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int q0 = zero ? 0 : round_clamp(u[e] * scale, -128.f, 127.f);
-                    const int q1 = zero ? 0 : round_clamp(u[4 + e] * scale, -128.f, 127.f);
-                    lo |= (uint32_t)(q0 & 0xff) << (8 * e);
-                    hi |= (uint32_t)(q1 & 0xff) << (8 * e);
-                }
-                *reinterpret_cast<uint2*>(&codes[tok][8 * v]) = make_uint2(lo, hi);
-            }
-        }
-    }
-    __syncthreads();
-
-    // 4. Codes of my chunks into registers; the wave sums them itself.
-    uint32_t xv[MT][CH][16];
+    uint32_t xv[MT][CH][16];  // codes of my chunks: chunk c covers x[64c .. 64c+63]
     int tok_sum[MT];
-#pragma unroll
-    for (int tok = 0; tok < MT; ++tok) {
-        int part = 0;
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int c = lane + kWave * j;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint4 a = make_uint4(0, 0, 0, 0);
-                if (c < nchunk) a = reinterpret_cast<const uint4*>(&codes[tok][64 * c])[q];
-                xv[tok][j][4 * q] = a.x;
-                xv[tok][j][4 * q + 1] = a.y;
-                xv[tok][j][4 * q + 2] = a.z;
-                xv[tok][j][4 * q + 3] = a.w;
-                part = dot4(a.x, 0x01010101u, part);
-                part = dot4(a.y, 0x01010101u, part);
-                part = dot4(a.z, 0x01010101u, part);
-                part = dot4(a.w, 0x01010101u, part);
-            }
-        }
-        tok_sum[tok] = wave_sum_dpp(part);
-    }
-
-    auto dequant_scale = [&](int tok) {
-        double ss = red_d[tok][0];
-#pragma unroll
-        for (int wv = 1; wv < NW; ++wv) ss += red_d[tok][wv];
-        const double rstd = 1.0 / sqrt(ss / (double)K + (double)eps);
-        return tok_amax[tok] < kTinyAbsmax ? 0.f : (float)(((double)tok_amax[tok] * rstd) / 127.0);
-    };
-    if (blockIdx.x == 0) {
-        for (int tok = 0; tok < MT; ++tok) {
-            for (int v = t; v < K / 16; v += NT)
-                reinterpret_cast<uint4*>(xq_out + (int64_t)tok * K)[v] =
-                    reinterpret_cast<const uint4*>(codes[tok])[v];
-            if (t == 0) {
-                x_scale_out[tok] = dequant_scale(tok);
-                x_qsum_out[tok] = tok_sum[tok];
-            }
-        }
-    }
-    if (row0 >= N) return;  // after the last barrier: wave-uniform exit
-
-    int my_acc[MT];
-#pragma unroll
-    for (int tok = 0; tok < MT; ++tok) my_acc[tok] = 0;
-    G::run(w, xv, packed, row_bytes, nchunk, row0, row1, lane, my_acc);
     float tok_scale[MT];
+    uint4 w0[RB][CH], w1[RB][CH];
+
+    if constexpr (FUSED) {
+        // 1. Activation (and gain) loads, then the first weight batch, which
+        // stays in flight through the prologue.
+        const int nvec = K / 8;
+        const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)a.x, (short)0, MT * K * 2, (int)kBufferWord3);
+        uint4 raw[MT][XV];
 #pragma unroll
-    for (int tok = 0; tok < MT; ++tok) tok_scale[tok] = dequant_scale(tok);
-    G::store(my_acc, tok_scale, tok_sum, scales, N, row0, row1, lane, y, acc_out);
+        for (int tok = 0; tok < MT; ++tok)
+#pragma unroll
+            for (int i = 0; i < XV; ++i) {
+                const int v = t + NT * i;
+                raw[tok][i] = load16(xres, v < nvec ? (uint32_t)(tok * K * 2 + 16 * v) : kOutOfRange);
+            }
+        float gv[XV][8];
+        const bool has_gain = a.gain != nullptr;
+        if (has_gain) {
+            const __amdgpu_buffer_rsrc_t gres = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)a.gain, (short)0, K * 4, (int)kBufferWord3);
+#pragma unroll
+            for (int i = 0; i < XV; ++i) {
+                const int v = t + NT * i;
+                const uint4 g0 = load16(gres, v < nvec ? (uint32_t)(32 * v) : kOutOfRange);
+                const uint4 g1 = load16(gres, v < nvec ? (uint32_t)(32 * v + 16) : kOutOfRange);
+                gv[i][0] = __uint_as_float(g0.x); gv[i][1] = __uint_as_float(g0.y);
+                gv[i][2] = __uint_as_float(g0.z); gv[i][3] = __uint_as_float(g0.w);
+                gv[i][4] = __uint_as_float(g1.x); gv[i][5] = __uint_as_float(g1.y);
+                gv[i][6] = __uint_as_float(g1.z); gv[i][7] = __uint_as_float(g1.w);
+            }
+        }
+        load(w0, 0);
+        if constexpr (MULTI) load(w1, RB);
+
+        auto values = [&](int tok, int i, float (&u)[8], bool with_gain) {
+            const uint32_t ws[4] = {raw[tok][i].x, raw[tok][i].y, raw[tok][i].z, raw[tok][i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u[2 * e] = bf16_lo(ws[e]);
+                u[2 * e + 1] = bf16_hi(ws[e]);
+            }
+            if (with_gain && has_gain) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] *= gv[i][e];
+            }
+        };
+
+        // 2. Per-token absmax of x*gain and sum of x^2 (four independent f64
+        // chains per thread): one workgroup reduction.
+#pragma unroll
+        for (int tok = 0; tok < MT; ++tok) {
+            float amax = 0.f;
+            double ss[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int i = 0; i < XV; ++i) {
+                if (t + NT * i < nvec) {
+                    float u[8];
+                    values(tok, i, u, false);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ss[e % 4] += (double)u[e] * (double)u[e];
+                    values(tok, i, u, true);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(u[e]));
+                }
+            }
+            amax = wave_max_dpp(amax);
+            const double s = wave_sum_dpp((ss[0] + ss[1]) + (ss[2] + ss[3]));
+            if (lane == 0) {
+                red_f[tok][wave] = amax;
+                red_d[tok][wave] = s;
+            }
+        }
+        __syncthreads();
+
+        // 3. Codes into LDS.  For |v| <= 127.00002, v + 1.5 * 2^23 rounds v to
+        // an integer (ties to even, the rint of the definition) and leaves it,
+        // two's complement, in the low byte of the float's bit pattern.  The
+        // clamp to [-128, 127] never acts: |x * gain| <= amax, so
+        // |x * gain * rn(127 / amax)| < 127.5.
+        float tok_amax[MT];
+#pragma unroll
+        for (int tok = 0; tok < MT; ++tok) {
+            float amax = red_f[tok][0];
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv) amax = fmaxf(amax, red_f[tok][wv]);
+            tok_amax[tok] = amax;
+            const float scale = amax < kTinyAbsmax ? 0.f : 127.0f / amax;
+#pragma unroll
+            for (int i = 0; i < XV; ++i) {
+                const int v = t + NT * i;
+                if (v < nvec) {
+                    float u[8];
+                    values(tok, i, u, true);
+                    uint32_t b[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        b[e] = __float_as_uint(__fadd_rn(__fmul_rn(u[e], scale), 12582912.0f));
+                    const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                              __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u),
+                                                              0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                                              __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
+                                                              0x05040100u);
+                    *reinterpret_cast<uint2*>(&codes[tok][8 * v]) = make_uint2(lo, hi);
+                }
+            }
+        }
+        __syncthreads();
+
+        // 4. Codes of my chunks into registers; each wave sums them itself.
+#pragma unroll
+        for (int tok = 0; tok < MT; ++tok) {
+            int part = 0;
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int c = lane + kWave * j;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (c < nchunk) v = reinterpret_cast<const uint4*>(&codes[tok][64 * c])[q];
+                    xv[tok][j][4 * q] = v.x;
+                    xv[tok][j][4 * q + 1] = v.y;
+                    xv[tok][j][4 * q + 2] = v.z;
+                    xv[tok][j][4 * q + 3] = v.w;
+                    part = dot4(v.x, 0x01010101u, part);
+                    part = dot4(v.y, 0x01010101u, part);
+                    part = dot4(v.z, 0x01010101u, part);
+                    part = dot4(v.w, 0x01010101u, part);
+                }
+            }
+            tok_sum[tok] = wave_sum_dpp(part);
+            double ss = red_d[tok][0];
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv) ss += red_d[tok][wv];
+            const double rstd = 1.0 / sqrt(ss / (double)K + (double)a.eps);
+            tok_scale[tok] = tok_amax[tok] < kTinyAbsmax ? 0.f
+                                                         : (float)(((double)tok_amax[tok] * rstd) / 127.0);
+        }
+        if (blockIdx.x == 0) {
+            for (int tok = 0; tok < MT; ++tok)
+                for (int v = t; v < K / 16; v += NT)
+                    reinterpret_cast<uint4*>(a.xq_out + (int64_t)tok * K)[v] =
+                        reinterpret_cast<const uint4*>(codes[tok])[v];
+            if (t == 0) {
+#pragma unroll
+                for (int tok = 0; tok < MT; ++tok) {
+                    a.x_scale_out[tok] = tok_scale[tok];
+                    a.x_qsum_out[tok] = tok_sum[tok];
+                }
+            }
+        }
+    } else {
+        // Codes of my chunks straight from memory, ahead of the weights.
+        const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)a.xq, (short)0, MT * K, (int)kBufferWord3);
+#pragma unroll
+        for (int tok = 0; tok < MT; ++tok)
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int c = lane + kWave * j;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint4 v = load16(qres, c < nchunk ? (uint32_t)(tok * K + 64 * c + 16 * q) : kOutOfRange);
+                    xv[tok][j][4 * q] = v.x;
+                    xv[tok][j][4 * q + 1] = v.y;
+                    xv[tok][j][4 * q + 2] = v.z;
+                    xv[tok][j][4 * q + 3] = v.w;
+                }
+            }
+#pragma unroll
+        for (int tok = 0; tok < MT; ++tok) {
+            tok_sum[tok] = a.x_qsum[tok];
+            tok_scale[tok] = a.x_scale[tok];
+        }
+        load(w0, 0);
+        if constexpr (MULTI) load(w1, RB);
+    }
+    if (nrows == 0) return;  // after the last barrier: wave-uniform exit
+
+    // 5. Contraction and epilogue, one batch at a time.
+    auto batch = [&](const uint4 (&w)[RB][CH], int i0) {
+        int p[NV];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int tok = 0; tok < MTP; ++tok) p[rb * MTP + tok] = 0;
+            if (i0 + rb < nrows) {  // wave-uniform
+#pragma unroll
+                for (int tok = 0; tok < MT; ++tok) {
+                    int s03 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+                    for (int j = 0; j < CH; ++j) {
+                        const uint32_t ws[4] = {w[rb][j].x, w[rb][j].y, w[rb][j].z, w[rb][j].w};
+#pragma unroll
+                        for (int d = 0; d < 4; ++d) {
+                            const uint32_t word = ws[d];
+                            s03 = dot4(word & 0x03030303u, xv[tok][j][4 * d + 0], s03);
+                            s1 = dot4(word & 0x0C0C0C0Cu, xv[tok][j][4 * d + 1], s1);
+                            s2 = dot4(word & 0x30303030u, xv[tok][j][4 * d + 2], s2);
+                            s03 = dot4((word >> 6) & 0x03030303u, xv[tok][j][4 * d + 3], s03);
+                        }
+                    }
+                    p[rb * MTP + tok] = s03 + (s1 >> 2) + (s2 >> 4);
+                }
+            }
+        }
+        xreduce<NV>(p, lane);
+        const int idx = lane >> (6 - LV);
+        const int rb = idx / MTP, tok = idx % MTP;
+        if ((lane & ((kWave >> LV) - 1)) == 0 && i0 + rb < nrows && tok < MT) {
+            const int64_t r = (int64_t)g + (int64_t)(i0 + rb) * W;
+            int qs = tok_sum[0];
+            float ts = tok_scale[0];
+#pragma unroll
+            for (int k = 1; k < MT; ++k) {  // selects: register arrays take no runtime index
+                qs = tok == k ? tok_sum[k] : qs;
+                ts = tok == k ? tok_scale[k] : ts;
+            }
+            const int acc = p[0] - qs;
+            if (a.acc != nullptr) a.acc[(int64_t)tok * N + r] = acc;
+            a.y[(int64_t)tok * N + r] = ((float)acc * ts) * a.scales.of(r, dw0);
+        }
+    };
+    if constexpr (!MULTI) {
+        batch(w0, 0);
+    } else {
+        const int nb = (nrows + RB - 1) / RB;
+        for (int b = 0; b < nb; b += 2) {
+            batch(w0, b * RB);
+            if (b + 2 < nb) load(w0, (b + 2) * RB);
+            if (b + 1 < nb) {
+                batch(w1, (b + 1) * RB);
+                if (b + 3 < nb) load(w1, (b + 3) * RB);
+            }
+        }
+    }
 }
 
-// Rows per wave: spread the rows over about `target_waves` waves (at most 64).
-int64_t rows_per_wave(int64_t N, int64_t target_waves) {
-    int64_t rpw = (N + target_waves - 1) / target_waves;
-    if (rpw < 1) rpw = 1;
-    if (rpw > kWave) rpw = kWave;
-    return rpw;
+// ---------------------------------------------------------------------------
+// Launch shape.  A wave's rows stay in registers, so the grid decides how much
+// of the matrix is in flight: about 1024 waves of 256-thread workgroups, or
+// 2048 waves of 512-thread workgroups for matrices with more than 4096 rows of
+// one chunk per lane (one workgroup per CU either way, since every workgroup
+// repeats the quantisation).  Measured on the decode projections of a 7B
+// model; oversized batches (loads and butterfly steps for absent rows) cost
+// more than they save, so RB is the smallest power of two that holds a wave's
+// rows.
+// ---------------------------------------------------------------------------
+int chunks_per_lane(int64_t K) { return (int)((K / 64 + kWave - 1) / kWave); }
+
+// The chunk counts instantiated: 1, 2, 3, 4, 6, 8 (larger counts are not supported).
+int rounded_ch(int ch) { return ch <= 4 ? ch : (ch <= 6 ? 6 : (ch <= 8 ? 8 : ch)); }
+
+template <int MT, int CH, int NT, int RB, bool MULTI, bool FUSED>
+hipError_t launch_shape(const Args& a, int64_t waves, hipStream_t stream) {
+    constexpr int NW = NT / kWave;
+    const int64_t blocks = (waves + NW - 1) / NW;
+    return launch_kernel((decode_kernel<MT, CH, NT, RB, MULTI, FUSED>), dim3((unsigned)blocks),
+                         dim3(NT), 0, stream, a);
 }
 
-struct Args {
-    const int8_t* xq;
-    const float* x_scale;
-    const int32_t* x_qsum;
-    const uint16_t* x;
-    const float* gain;
-    float eps;
-    const uint8_t* packed;
-    RowScales scales;
-    int64_t N, K;
-    float* y;
-    int8_t* xq_out;
-    float* x_scale_out;
-    int32_t* x_qsum_out;
-    int32_t* acc;
-    hipStream_t stream;
-};
+// Pick RB (and MULTI) for a wave owning up to rpw rows.
+template <int MT, int CH, int NT, bool FUSED>
+hipError_t launch_rb(const Args& a, int64_t rpw, int64_t waves, hipStream_t stream) {
+    constexpr int CAP = max_batch<CH>();
+    constexpr int MTP = MT == 3 ? 4 : MT;
+    constexpr int CAP_MT = MTP * CAP <= kWave ? CAP : kWave / MTP;
+    if (rpw <= 2 && CAP_MT >= 2) return launch_shape<MT, CH, NT, 2, false, FUSED>(a, waves, stream);
+    if constexpr (CAP_MT >= 4)
+        if (rpw <= 4) return launch_shape<MT, CH, NT, 4, false, FUSED>(a, waves, stream);
+    if constexpr (CAP_MT >= 8)
+        if (rpw <= 8) return launch_shape<MT, CH, NT, 8, false, FUSED>(a, waves, stream);
+    if constexpr (CAP_MT >= 16)
+        if (rpw <= 16) return launch_shape<MT, CH, NT, 16, false, FUSED>(a, waves, stream);
+    return launch_shape<MT, CH, NT, CAP_MT, true, FUSED>(a, waves, stream);
+}
 
-template <int MT, int CH>
-struct Standalone {
-    static hipError_t run(const Args& a) {
-        const int64_t rpw = rows_per_wave(a.N, 2048);
-        const int64_t blocks = ((a.N + rpw - 1) / rpw + kGemvWaves - 1) / kGemvWaves;
-        return launch_kernel((gemv_kernel<MT, CH>), dim3((unsigned)blocks), dim3(kGemvThreads), 0,
-                             a.stream, a.xq, a.x_scale, a.x_qsum, a.packed, a.scales, (int)a.N,
-                             (int)a.K, (int)rpw, a.y, a.acc);
+template <int MT, int CH, bool FUSED>
+hipError_t launch_ch(const Args& a, hipStream_t stream) {
+    const int64_t N = a.N;
+    // 512-thread workgroups for many rows of a single chunk (M = 1 only).
+    if constexpr (MT == 1 && CH == 1) {
+        if (N > 4096) {
+            const int64_t rpw = (N + 2047) / 2048;
+            return launch_rb<MT, CH, 512, FUSED>(a, rpw, (N + rpw - 1) / rpw, stream);
+        }
     }
-};
+    const int64_t rpw = (N + 1023) / 1024;
+    return launch_rb<MT, CH, 256, FUSED>(a, rpw, (N + rpw - 1) / rpw, stream);
+}
 
-template <int MT, int CH>
-struct Fused {
-    static constexpr int NT = kFusedThreads;
-    static hipError_t run(const Args& a) {
-        // Every workgroup repeats the quantisation, so about one workgroup
-        // per CU; its prologue is split over NT threads.
-        const int64_t rpw = rows_per_wave(a.N, kFusedWaves);
-        const int64_t blocks = ((a.N + rpw - 1) / rpw + NT / kWave - 1) / (NT / kWave);
-        return launch_kernel((fused_decode_kernel<MT, CH, NT>), dim3((unsigned)blocks),
-                             dim3(NT), 0, a.stream, a.x, a.gain, a.eps, a.packed,
-                             a.scales, (int)a.N, (int)a.K, (int)rpw, a.y, a.xq_out,
-                             a.x_scale_out, a.x_qsum_out, a.acc);
-    }
-};
-
-template <template <int, int> class L, int MT>
-hipError_t dispatch_ch(int ch, const Args& a) {
-#define BITNET_GEMV_CH(C)                                                  \
-    if (ch <= C) {                                                         \
-        if constexpr (MT * C <= kMaxXRegsChunks) return L<MT, C>::run(a); \
-        return hipErrorInvalidValue;                                       \
+template <int MT, bool FUSED>
+hipError_t dispatch_ch(int ch, const Args& a, hipStream_t stream) {
+#define BITNET_GEMV_CH(C)                                                          \
+    if (ch <= C) {                                                                 \
+        if constexpr (MT * C <= kMaxXRegsChunks) return launch_ch<MT, C, FUSED>(a, stream); \
+        return hipErrorInvalidValue;                                               \
     }
     BITNET_GEMV_CH(1)
     BITNET_GEMV_CH(2)
@@ -425,21 +512,17 @@ hipError_t dispatch_ch(int ch, const Args& a) {
     return hipErrorInvalidValue;
 }
 
-template <template <int, int> class L>
-hipError_t dispatch(int64_t M, int ch, const Args& a) {
+template <bool FUSED>
+hipError_t dispatch(int64_t M, const Args& a, hipStream_t stream) {
+    const int ch = chunks_per_lane(a.K);
     switch (M) {
-        case 1: return dispatch_ch<L, 1>(ch, a);
-        case 2: return dispatch_ch<L, 2>(ch, a);
-        case 3: return dispatch_ch<L, 3>(ch, a);
-        case 4: return dispatch_ch<L, 4>(ch, a);
+        case 1: return dispatch_ch<1, FUSED>(ch, a, stream);
+        case 2: return dispatch_ch<2, FUSED>(ch, a, stream);
+        case 3: return dispatch_ch<3, FUSED>(ch, a, stream);
+        case 4: return dispatch_ch<4, FUSED>(ch, a, stream);
         default: return hipErrorInvalidValue;
     }
 }
-
-int chunks_per_lane(int64_t K) { return (int)((K / 64 + kWave - 1) / kWave); }
-
-// The chunk counts instantiated: 1, 2, 3, 4, 6, 8 (larger counts are not supported).
-int rounded_ch(int ch) { return ch <= 4 ? ch : (ch <= 6 ? 6 : (ch <= 8 ? 8 : ch)); }
 
 }  // namespace
 
@@ -454,8 +537,8 @@ hipError_t launch_gemv(const int8_t* xq, const float* x_scale, const int32_t* x_
     if (N == 0) return hipSuccess;
     Args a{};
     a.xq = xq, a.x_scale = x_scale, a.x_qsum = x_qsum, a.packed = packed, a.scales = scales;
-    a.N = N, a.K = K, a.y = y, a.acc = acc, a.stream = stream;
-    return dispatch<Standalone>(M, chunks_per_lane(K), a);
+    a.N = (int)N, a.K = (int)K, a.y = y, a.acc = acc;
+    return dispatch<false>(M, a, stream);
 }
 
 hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
@@ -464,9 +547,9 @@ hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
                                int32_t* x_qsum, int32_t* acc, hipStream_t stream) {
     Args a{};
     a.x = x, a.gain = gain, a.eps = eps, a.packed = packed, a.scales = scales;
-    a.N = N, a.K = K, a.y = y, a.xq_out = xq, a.x_scale_out = x_scale, a.x_qsum_out = x_qsum;
-    a.acc = acc, a.stream = stream;
-    return dispatch<Fused>(M, chunks_per_lane(K), a);
+    a.N = (int)N, a.K = (int)K, a.y = y, a.xq_out = xq, a.x_scale_out = x_scale;
+    a.x_qsum_out = x_qsum, a.acc = acc;
+    return dispatch<true>(M, a, stream);
 }
 
 }  // namespace bitnet
