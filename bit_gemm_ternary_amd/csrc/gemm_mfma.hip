@@ -150,7 +150,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
-    const int wave = t / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform, in an SGPR
     const int wn = wave % C::WN, wm = wave / C::WN;
 
     // Launch index -> tile: contiguous ranges per XCD, grouped order.
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(KW * kWave) void skinny_kernel(
     int vec_store, float* __restrict__ y, int32_t* __restrict__ acc_out) {
     __shared__ v4i part[KW][kWave];
     const int lane = threadIdx.x % kWave;
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int fr = lane % 16, fg = lane / 16;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int row_bytes = K / 4;
