@@ -179,12 +179,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     const int N = a.N, K = a.K;
     const int nchunk = K / 64;
     const int row_bytes = K / 4;
-    const int nrows = g < N ? (int)(((int64_t)N - g + W - 1) / W) : 0;  // rows g + i W, i < nrows
+    // Row i of this wave is g + i W; it exists while that is below N.
+    auto has_row = [&](int i) { return (int64_t)g + (int64_t)i * W < N; };
     const float dw0 = a.scales.w_scale[0];              // before any store (see RowScales::of)
 
     // Weight loads of rows i0 .. i0 + RB - 1 of this wave (zeros past the last).
     auto load = [&](uint4 (&w)[RB][CH], int i0) {
-        const int64_t r0 = i0 < nrows ? (int64_t)g + (int64_t)i0 * W : 0;
+        const int64_t r0 = has_row(i0) ? (int64_t)g + (int64_t)i0 * W : 0;
         const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.packed + r0 * row_bytes), (short)0, kMaxRecords, (int)kBufferWord3);
 #pragma unroll
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 const int c = lane + kWave * j;
-                const uint32_t off = (i0 + rb < nrows && c < nchunk)
+                const uint32_t off = (has_row(i0 + rb) && c < nchunk)
                                          ? (uint32_t)(rb * W * row_bytes + 16 * c)
                                          : kOutOfRange;
                 w[rb][j] = load16(res, off);
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
                     float u[8];
                     values(tok, i, u, false);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) ss[e % 4] += (double)u[e] * (double)u[e];
+                    for (int e = 0; e < 8; ++e) ss[e % 4] = __fma_rn((double)u[e], (double)u[e], ss[e % 4]);
                     values(tok, i, u, true);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(u[e]));
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
         load(w0, 0);
         if constexpr (MULTI) load(w1, RB);
     }
-    if (nrows == 0) return;  // after the last barrier: wave-uniform exit
+    if (g >= N) return;  // after the last barrier: wave-uniform exit
 
     // 5. Contraction and epilogue, one batch at a time.
     auto batch = [&](const uint4 (&w)[RB][CH], int i0) {
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
         for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
             for (int tok = 0; tok < MTP; ++tok) p[rb * MTP + tok] = 0;
-            if (i0 + rb < nrows) {  // wave-uniform
+            if (has_row(i0 + rb)) {  // wave-uniform
 #pragma unroll
                 for (int tok = 0; tok < MT; ++tok) {
                     int s03 = 0, s1 = 0, s2 = 0;
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
         xreduce<NV>(p, lane);
         const int idx = lane >> (6 - LV);
         const int rb = idx / MTP, tok = idx % MTP;
-        if ((lane & ((kWave >> LV) - 1)) == 0 && i0 + rb < nrows && tok < MT) {
+        if ((lane & ((kWave >> LV) - 1)) == 0 && has_row(i0 + rb) && tok < MT) {
             const int64_t r = (int64_t)g + (int64_t)(i0 + rb) * W;
             int qs = tok_sum[0];
             float ts = tok_scale[0];
@@ -430,13 +431,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     if constexpr (!MULTI) {
         batch(w0, 0);
     } else {
-        const int nb = (nrows + RB - 1) / RB;
-        for (int b = 0; b < nb; b += 2) {
-            batch(w0, b * RB);
-            if (b + 2 < nb) load(w0, (b + 2) * RB);
-            if (b + 1 < nb) {
-                batch(w1, (b + 1) * RB);
-                if (b + 3 < nb) load(w1, (b + 3) * RB);
+        for (int i0 = 0; has_row(i0); i0 += 2 * RB) {
+            batch(w0, i0);
+            if (has_row(i0 + 2 * RB)) load(w0, i0 + 2 * RB);
+            if (has_row(i0 + RB)) {
+                batch(w1, i0 + RB);
+                if (has_row(i0 + 3 * RB)) load(w1, i0 + 3 * RB);
             }
         }
     }
@@ -445,12 +445,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
 // ---------------------------------------------------------------------------
 // Launch shape.  A wave's rows stay in registers, so the grid decides how much
 // of the matrix is in flight: about 1024 waves of 256-thread workgroups, or
-// 2048 waves of 512-thread workgroups for matrices with more than 4096 rows of
-// one chunk per lane (one workgroup per CU either way, since every workgroup
-// repeats the quantisation).  Measured on the decode projections of a 7B
-// model; oversized batches (loads and butterfly steps for absent rows) cost
-// more than they save, so RB is the smallest power of two that holds a wave's
-// rows.
+// 2048 waves of 512-thread workgroups for one token and matrices larger than
+// 4096 x 4096 (one workgroup per CU either way, since every workgroup repeats
+// the quantisation; the larger workgroup splits that work over more threads).
+// Measured on the decode projections of a 7B model.  Oversized batches (loads
+// and butterfly steps for absent rows) cost more than they save, so RB is the
+// smallest power of two that holds a wave's rows.
 // ---------------------------------------------------------------------------
 int chunks_per_lane(int64_t K) { return (int)((K / 64 + kWave - 1) / kWave); }
 
@@ -484,9 +484,10 @@ hipError_t launch_rb(const Args& a, int64_t rpw, int64_t waves, hipStream_t stre
 template <int MT, int CH, bool FUSED>
 hipError_t launch_ch(const Args& a, hipStream_t stream) {
     const int64_t N = a.N;
-    // 512-thread workgroups for many rows of a single chunk (M = 1 only).
-    if constexpr (MT == 1 && CH == 1) {
-        if (N > 4096) {
+    // 512-thread workgroups (2048 waves) for single tokens and matrices larger
+    // than 4096 x 4096: they halve each thread's share of the quantisation.
+    if constexpr (MT == 1) {
+        if (N >= 4096 && (N > 4096 || a.K > 4096)) {
             const int64_t rpw = (N + 2047) / 2048;
             return launch_rb<MT, CH, 512, FUSED>(a, rpw, (N + rpw - 1) / rpw, stream);
         }
