@@ -92,7 +92,7 @@ def parse_args():
 COPY_BYTES = 256 << 20
 READ_REF_BYTES = 2 << 30
 CSRC = os.path.join(ROOT, "bit_gemm_ternary_amd", "csrc")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_decode_kernel.decode_M1.hbm_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_kernel.decode_M1.hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("gemv.hip", "common.hpp")]
 GEMM_SUMMARY = os.path.join(ROOT, "profiles", "gemm_kernel.prefill_M2048_K4096_N14336.counters.md")
 GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "common.hpp")]
@@ -298,7 +298,7 @@ def decode_bench(args, dev, bt, torch, synth):
     ms_per_step, wall_s = timed(run_steps, args.steps, torch)
     # Warm reference: the same steps on one weight copy, which then stays
     # resident in the 256 MB Infinity Cache (and partly in L2).
-    warm_run = graph_runner(lambda r: step(0), 1, args.eager, torch)
+    warm_run = graph_runner(lambda r: step(0), copies, args.eager, torch)
     warm_ms, _ = timed(warm_run, min(args.steps, 500), torch)
 
     # Per-kernel durations: the same steps again, launched eagerly with the
@@ -625,7 +625,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else traffic["hbm_bytes_per_step"],
             "traffic_per_launch": None if traffic is None else traffic["hbm_bytes_per_launch"],
-            "kernel": "fused_decode_kernel (3 launches per step)",
+            "kernel": "decode_kernel, fused (3 launches per step)",
             "bytes_per_step": dec["kernel_bytes"],
             "us_per_step": round(dec["kernel_us"], 3),
             "per_launch": dec["per_layer"],
