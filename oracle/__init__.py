@@ -58,6 +58,14 @@ def load(path: str):
     lib.oracle_int_gemm_sampled.restype = i32
     lib.oracle_dequant.argtypes = [p, p, f32, i64, i64, p]
     lib.oracle_dequant.restype = None
+    lib.oracle_transpose_packed.argtypes = [p, i64, i64, p]
+    lib.oracle_transpose_packed.restype = i32
+    lib.oracle_linear_backward_input.argtypes = [p, p, f32, i64, i64, i64, p]
+    lib.oracle_linear_backward_input.restype = i32
+    lib.oracle_linear_backward_weight.argtypes = [p, p, p, i64, i64, i64, p]
+    lib.oracle_linear_backward_weight.restype = i32
+    lib.oracle_rmsnorm_backward.argtypes = [p, p, f32, p, i64, i64, p, p]
+    lib.oracle_rmsnorm_backward.restype = i32
     return lib
 
 
@@ -167,6 +175,56 @@ class Oracle:
         """Full contraction + dequantisation: returns (acc int32 [M][N], y float64 [M][N])."""
         acc = self.int_gemm(xq, packed, K)
         return acc, self.dequant(acc, d_x, d_w)
+
+    # --- backward under the straight-through estimator -------------------
+
+    def transpose_packed(self, packed: np.ndarray, K: int) -> np.ndarray:
+        """packed uint8 [N][K/4] -> packed_t uint8 [K][N/4] (same layout along rows)."""
+        packed = _c(packed, np.uint8)
+        N = packed.shape[0]
+        out = np.empty((K, N // 4), np.uint8)
+        if self.lib.oracle_transpose_packed(_ptr(packed), N, K, _ptr(out)) != 0:
+            raise ValueError(f"oracle_transpose_packed rejected N={N} K={K}")
+        return out
+
+    def linear_backward_input(self, grad_y_bits, packed, d_w, K: int) -> np.ndarray:
+        """grad_n float64 [M][K] = d_w * grad_y (bf16 bits [M][N]) @ q_w."""
+        g = _c(grad_y_bits, np.uint16)
+        packed = _c(packed, np.uint8)
+        M, N = g.shape
+        out = np.empty((M, K), np.float64)
+        rc = self.lib.oracle_linear_backward_input(_ptr(g), _ptr(packed), ctypes.c_float(d_w),
+                                                   M, N, K, _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_linear_backward_input rejected its arguments")
+        return out
+
+    def linear_backward_weight(self, grad_y_bits, xq, d_x) -> np.ndarray:
+        """grad_w float64 [N][K] = sum_m grad_y[m][n] d_x[m] q_x[m][k]."""
+        g = _c(grad_y_bits, np.uint16)
+        xq = _c(xq, np.int8)
+        d_x = _c(d_x, np.float32)
+        M, N = g.shape
+        K = xq.shape[1]
+        out = np.empty((N, K), np.float64)
+        rc = self.lib.oracle_linear_backward_weight(_ptr(g), _ptr(xq), _ptr(d_x), M, N, K, _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_linear_backward_weight rejected its arguments")
+        return out
+
+    def rmsnorm_backward(self, x_bits, grad_n, gain=None, eps: float = 1e-5, with_gain_grad=False):
+        """(grad_x float64 [M][K], grad_gain float64 [K] or None) of n = x * gain * r."""
+        x_bits = _c(x_bits, np.uint16)
+        gn = _c(grad_n, np.float32)
+        M, K = x_bits.shape
+        g = None if gain is None else _c(gain, np.float32)
+        gx = np.empty((M, K), np.float64)
+        gg = np.empty(K, np.float64) if with_gain_grad else None
+        rc = self.lib.oracle_rmsnorm_backward(_ptr(x_bits), _ptr(g), ctypes.c_float(eps), _ptr(gn),
+                                              M, K, _ptr(gx), _ptr(gg))
+        if rc != 0:
+            raise ValueError("oracle_rmsnorm_backward rejected its arguments")
+        return gx, gg
 
 
 _DEFAULT = None

@@ -21,6 +21,9 @@
  *   [2B]  "AI 혁신의 선두: 마이크로소프트의 1비트 LLM, BitNet b1.58 2B4T",
  *         sections "주요 아키텍처 혁신" (architecture) and
  *         "훈련 안정성 및 효율성 향상" (normalisation before quantisation).
+ *   [FT]  also sections "Straight-Through Estimator (STE)를 이용한 학습"
+ *         (training through round() with the gradient taken as 1) and
+ *         "동적 워밍업 양자화" (the lambda warm-up blend).
  *   [QP]  endplan.ai quantization primer "양자화(quantization) 1.58bit",
  *         sections "그러면 크기를 더 못줄이나요?" (absmax example) and
  *         "1.58비트는 어디서 나온거에요?" (three weight values).
@@ -52,7 +55,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_VERSION 1
+#define ORACLE_VERSION 2
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -366,4 +369,127 @@ void oracle_dequant(const int32_t* acc, const float* d_x, float d_w, int64_t M, 
     for (int64_t m = 0; m < M; m++)
         for (int64_t n = 0; n < N; n++)
             y[m * N + n] = (double)acc[m * N + n] * (double)d_x[m] * (double)d_w;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Backward pass under the straight-through estimator ([FT] "Straight-      */
+/* Through Estimator (STE)를 이용한 학습": round() is given gradient 1, so    */
+/* the quantisers pass the gradient through unchanged).                      */
+/*                                                                           */
+/* Seen by the estimator, the forward is y = n~ W~^T with the dequantised    */
+/* operands n~[m][k] = d_x[m] q_x[m][k] (which stands for the normalised     */
+/* activation n = x * gain * r, r = 1 / sqrt(mean(x^2) + eps)) and           */
+/* W~[n][k] = d_w q_w[n][k] (which stands for W).  So                        */
+/*   dL/dn = dL/dy W~,   dL/dW = (dL/dy)^T n~,                               */
+/* and dL/dx follows from the RMSNorm that produced n.                       */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * The packed weights with the roles of N and K exchanged: packed [N][K/4] ->
+ * packed_t [K][N/4], in the same layout along the new row (row k, word g holds
+ * weights n = 16g .. 16g+15, weight 16g + 4i + b in bits 2i..2i+1 of byte b).
+ * N and K must be multiples of 16.  The field values (q + 1) are copied as is.
+ */
+int oracle_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed_t) {
+    if (N < 16 || K < 16 || N % 16 != 0 || K % 16 != 0) return -1;
+    const int64_t row_bytes = K / 4, row_bytes_t = N / 4;
+    memset(packed_t, 0, (size_t)K * (size_t)row_bytes_t);
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            int field = (packed[n * row_bytes + packed_byte_of(k)] >> packed_shift_of(k)) & 3;
+            packed_t[k * row_bytes_t + packed_byte_of(n)] |= (uint8_t)(field << packed_shift_of(n));
+        }
+    }
+    return 0;
+}
+
+/*
+ * Gradient with respect to the normalised activations:
+ * grad_n[m][k] = d_w * sum_n grad_y[m][n] * q_w[n][k], in float64 (the sum
+ * runs over n in order).  grad_y is bf16 [M][N]; packed is the forward's
+ * [N][K/4] matrix.
+ */
+int oracle_linear_backward_input(const uint16_t* grad_y, const uint8_t* packed, float d_w,
+                                 int64_t M, int64_t N, int64_t K, double* grad_n) {
+    if (M < 0 || N < 1 || K < 16 || K % 16 != 0) return -1;
+    int8_t* qw = (int8_t*)malloc((size_t)N * (size_t)K);
+    if (!qw) return -1;
+    oracle_unpack_weights(packed, N, K, qw);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; m++) {
+        for (int64_t k = 0; k < K; k++) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; n++)
+                s += (double)bf16_bits_to_float(grad_y[m * N + n]) * (double)qw[n * K + k];
+            grad_n[m * K + k] = s * (double)d_w;
+        }
+    }
+    free(qw);
+    return 0;
+}
+
+/*
+ * Gradient with respect to the latent weights:
+ * grad_w[n][k] = sum_m grad_y[m][n] * d_x[m] * q_x[m][k], in float64 (the sum
+ * runs over m in order).  grad_y bf16 [M][N], q_x int8 [M][K], d_x float32 [M].
+ */
+int oracle_linear_backward_weight(const uint16_t* grad_y, const int8_t* xq, const float* d_x,
+                                  int64_t M, int64_t N, int64_t K, double* grad_w) {
+    if (M < 0 || N < 1 || K < 1) return -1;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; m++)
+                s += (double)bf16_bits_to_float(grad_y[m * N + n]) * (double)d_x[m] *
+                     (double)xq[m * K + k];
+            grad_w[n * K + k] = s;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Backward of the RMSNorm that feeds the quantiser ([FT] "양자화 메커니즘":
+ * the activations are normalised before quantisation): n[m][k] = x[m][k] * g[k] * r[m]
+ * with r[m] = 1 / sqrt(sum_k x[m][k]^2 / K + eps) and g = gain (1 if NULL).
+ * Given grad_n (float32 [M][K]) it returns, in float64,
+ *   grad_x[m][j] = g[j] r grad_n[m][j] - x[m][j] r^3 / K * sum_k grad_n[m][k] x[m][k] g[k]
+ *   grad_gain[k] = sum_m grad_n[m][k] x[m][k] r[m]          (if grad_gain != NULL)
+ * which is the derivative of n written out.
+ */
+int oracle_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, const float* grad_n,
+                            int64_t M, int64_t K, double* grad_x, double* grad_gain) {
+    if (M < 0 || K < 1) return -1;
+    double* r = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1));
+    if (!r) return -1;
+    for (int64_t m = 0; m < M; m++) {
+        double ss = 0.0, dot = 0.0;
+        for (int64_t k = 0; k < K; k++) {
+            const double xv = (double)bf16_bits_to_float(x[m * K + k]);
+            ss += xv * xv;
+        }
+        r[m] = 1.0 / sqrt(ss / (double)K + (double)eps);
+        for (int64_t k = 0; k < K; k++) {
+            const double xv = (double)bf16_bits_to_float(x[m * K + k]);
+            const double g = gain ? (double)gain[k] : 1.0;
+            dot += (double)grad_n[m * K + k] * xv * g;
+        }
+        const double r3 = r[m] * r[m] * r[m];
+        for (int64_t k = 0; k < K; k++) {
+            const double xv = (double)bf16_bits_to_float(x[m * K + k]);
+            const double g = gain ? (double)gain[k] : 1.0;
+            grad_x[m * K + k] = g * r[m] * (double)grad_n[m * K + k] - xv * r3 / (double)K * dot;
+        }
+    }
+    if (grad_gain) {
+        for (int64_t k = 0; k < K; k++) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; m++)
+                s += (double)grad_n[m * K + k] * (double)bf16_bits_to_float(x[m * K + k]) * r[m];
+            grad_gain[k] = s;
+        }
+    }
+    free(r);
+    return 0;
 }

@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 from oracle import build as oracle_build
+import test_oracle_backward_pins as bpins
 import test_oracle_pins as pins
 
 MUTANTS = {
@@ -50,6 +51,22 @@ MUTANTS = {
     "contraction: sampled path ignores the offset": ("s += (int64_t)xq[m * K + k] * (int64_t)(field - 1);",
                                                      "s += (int64_t)xq[m * K + k] * (int64_t)(field);"),
     "dequant: weight scale dropped": ("* (double)d_x[m] * (double)d_w;", "* (double)d_x[m];"),
+    "transpose: shift of the old column": ("(uint8_t)(field << packed_shift_of(n));",
+                                           "(uint8_t)(field << packed_shift_of(k));"),
+    "backward input: transposed weight index": ("* (double)qw[n * K + k];", "* (double)qw[k * N + n];"),
+    "backward input: weight scale dropped": ("grad_n[m * K + k] = s * (double)d_w;", "grad_n[m * K + k] = s;"),
+    "backward weight: activation scale dropped": ("(double)bf16_bits_to_float(grad_y[m * N + n]) * (double)d_x[m] *",
+                                                  "(double)bf16_bits_to_float(grad_y[m * N + n]) *"),
+    "backward weight: codes of the wrong token": ("(double)xq[m * K + k];", "(double)xq[k];"),
+    "rmsnorm backward: r^2 in the projection": ("const double r3 = r[m] * r[m] * r[m];",
+                                                "const double r3 = r[m] * r[m];"),
+    "rmsnorm backward: gain missing from the direct term": ("grad_x[m * K + k] = g * r[m] * (double)grad_n",
+                                                            "grad_x[m * K + k] = r[m] * (double)grad_n"),
+    "rmsnorm backward: projection not divided by K": ("- xv * r3 / (double)K * dot;", "- xv * r3 * dot;"),
+    "rmsnorm backward: gain gradient without r": ("(double)bf16_bits_to_float(x[m * K + k]) * r[m];",
+                                                  "(double)bf16_bits_to_float(x[m * K + k]);"),
+    "rmsnorm backward: eps dropped": ("r[m] = 1.0 / sqrt(ss / (double)K + (double)eps);",
+                                      "r[m] = 1.0 / sqrt(ss / (double)K);"),
 }
 
 # Pins run against every mutant (the parametrised ones at a representative size).
@@ -78,6 +95,13 @@ PIN_CALLS = [
     (pins.test_dequant_closed_form, {}),
     (pins.test_int8_path_end_to_end_scale, {}),
     (pins.test_hadamard_path_end_to_end_scale, {}),
+    (bpins.test_transpose_packed_moves_every_field, {}),
+    (bpins.test_backward_input_is_the_adjoint_of_the_forward, {}),
+    (bpins.test_backward_input_closed_forms, {}),
+    (bpins.test_backward_weight_is_the_adjoint_of_the_forward, {}),
+    (bpins.test_backward_weight_single_token_is_an_outer_product, {}),
+    (bpins.test_rmsnorm_backward_matches_finite_differences, {}),
+    (bpins.test_rmsnorm_backward_is_orthogonal_to_x_without_eps, {}),
 ]
 
 
