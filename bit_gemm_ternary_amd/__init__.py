@@ -75,6 +75,18 @@ def lib() -> ctypes.CDLL:
     L.bitnet_bitlinear_forward_grouped.argtypes = [p, p, f32, p, p, p, i32, i64, i64, p, p, p, p,
                                                    p, p]
     L.bitnet_bitlinear_forward_grouped.restype = i32
+    L.bitnet_transpose_packed.argtypes = [p, i64, i64, p, p]
+    L.bitnet_transpose_packed.restype = i32
+    L.bitnet_linear_backward_input.argtypes = [p, p, p, i64, i64, i64, p, p]
+    L.bitnet_linear_backward_input.restype = i32
+    L.bitnet_linear_backward_weight_workspace_bytes.argtypes = [i64, i64, i64]
+    L.bitnet_linear_backward_weight_workspace_bytes.restype = sz
+    L.bitnet_linear_backward_weight.argtypes = [p, p, p, i64, i64, i64, p, p, sz, p]
+    L.bitnet_linear_backward_weight.restype = i32
+    L.bitnet_rmsnorm_backward_workspace_bytes.argtypes = [i64, i64]
+    L.bitnet_rmsnorm_backward_workspace_bytes.restype = sz
+    L.bitnet_rmsnorm_backward.argtypes = [p, p, f32, p, i64, i64, p, p, p, sz, p]
+    L.bitnet_rmsnorm_backward.restype = i32
     L.bitnet_status_string.argtypes = [i32]
     L.bitnet_status_string.restype = ctypes.c_char_p
     L.bitnet_last_error.argtypes = []
@@ -376,6 +388,81 @@ def bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5, out=None
                                           _ptr(x_qsum), _ptr(out), _ptr(acc_out),
                                           _stream(x.device)))
     return (out, acc_out) if acc_out is not None else out
+
+
+# --- backward under the straight-through estimator ------------------------
+
+def transpose_packed(packed, K: int, out=None):
+    """packed uint8 [N][K/4] -> packed_t uint8 [K][N/4] (bitnet_transpose_packed)."""
+    torch = _torch()
+    _require(packed, "packed", torch.uint8, 2)
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}]")
+    if out is None:
+        out = torch.empty((K, N // 4), dtype=torch.uint8, device=packed.device)
+    _check(lib().bitnet_transpose_packed(_ptr(packed), N, K, _ptr(out), _stream(packed.device)))
+    return out
+
+
+def linear_backward_input(grad_y, packed_t, w_scale, out=None):
+    """grad_n float32 [M][K] = d_w * grad_y (bf16 [M][N]) @ q_w, from packed_t [K][N/4]."""
+    torch = _torch()
+    _require(grad_y, "grad_y", torch.bfloat16, 2)
+    _require(packed_t, "packed_t", torch.uint8, 2)
+    _require(w_scale, "w_scale", torch.float32, 1)
+    M, N = grad_y.shape
+    K = packed_t.shape[0]
+    if packed_t.shape[1] * 4 != N:
+        raise ValueError(f"packed_t is [{K}][{packed_t.shape[1]}], expected [{K}][{N // 4}]")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=grad_y.device)
+    _check(lib().bitnet_linear_backward_input(_ptr(grad_y), _ptr(packed_t), _ptr(w_scale), M, N, K,
+                                              _ptr(out), _stream(grad_y.device)))
+    return out
+
+
+def linear_backward_weight(grad_y, xq, x_scale, out=None, workspace=None):
+    """grad_w float32 [N][K] = sum_m grad_y[m][n] d_x[m] q_x[m][k] (bitnet_linear_backward_weight)."""
+    torch = _torch()
+    _require(grad_y, "grad_y", torch.bfloat16, 2)
+    _require(xq, "xq", torch.int8, 2)
+    _require(x_scale, "x_scale", torch.float32, 1)
+    M, N = grad_y.shape
+    K = xq.shape[1]
+    if xq.shape[0] != M or x_scale.shape[0] != M:
+        raise ValueError("xq and x_scale must have M rows")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=grad_y.device)
+    need = int(lib().bitnet_linear_backward_weight_workspace_bytes(M, N, K))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=grad_y.device)
+    _check(lib().bitnet_linear_backward_weight(_ptr(grad_y), _ptr(xq), _ptr(x_scale), M, N, K,
+                                               _ptr(out), _ptr(workspace), workspace.numel(),
+                                               _stream(grad_y.device)))
+    return out
+
+
+def rmsnorm_backward(x, grad_n, gain=None, eps: float = 1e-5, with_gain_grad: bool = False):
+    """(grad_x float32 [M][K], grad_gain float32 [K] or None) of n = x * gain * r."""
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    _require(grad_n, "grad_n", torch.float32, 2)
+    M, K = x.shape
+    if tuple(grad_n.shape) != (M, K):
+        raise ValueError("grad_n must have the shape of x")
+    if gain is not None:
+        _require(gain, "gain", torch.float32, 1)
+    grad_x = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    grad_gain = torch.empty(K, dtype=torch.float32, device=x.device) if with_gain_grad else None
+    ws, ws_bytes = None, 0
+    if with_gain_grad:
+        ws_bytes = int(lib().bitnet_rmsnorm_backward_workspace_bytes(M, K))
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().bitnet_rmsnorm_backward(_ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(grad_n), M, K,
+                                         _ptr(grad_x), _ptr(grad_gain), _ptr(ws), ws_bytes,
+                                         _stream(x.device)))
+    return grad_x, grad_gain
 
 
 def bitlinear(x, packed, w_scale, hadamard: bool = False, gain=None, eps: float = 1e-5):

@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitnet_hip.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "pack.hip", "quant_act.hip", "hadamard_quant.hip", "gemv.hip", "gemm_mfma.hip"]
+SOURCES = ["api.cpp", "pack.hip", "quant_act.hip", "hadamard_quant.hip", "gemv.hip", "gemm_mfma.hip",
+           "backward.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -285,6 +285,121 @@ int bitnet_bitlinear_forward_grouped(const uint16_t* x, const float* gain, float
                                   acc, (hipStream_t)stream, fn);
 }
 
+namespace {
+
+// Backward shapes: N and K multiples of 64 (whole 64 x 64 transpose tiles and
+// 64-value reduction stages), M any token count.
+int check_backward_nk(int64_t N, int64_t K, const char* fn) {
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (N < 64 || N > kMaxK || N % 64 != 0)
+        return fail(BITNET_ERR_SHAPE, "%s: N=%lld must be a multiple of 64 in [64, 65536]", fn,
+                    (long long)N);
+    return BITNET_OK;
+}
+
+}  // namespace
+
+int bitnet_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed_t,
+                            void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_transpose_packed";
+    int s = check_backward_nk(N, K, fn);
+    if (s != BITNET_OK) return s;
+    if (!packed || !packed_t) return fail(BITNET_ERR_NULL, "%s: packed and packed_t must not be NULL", fn);
+    if (!aligned(packed, 16) || !aligned(packed_t, 16))
+        return fail(BITNET_ERR_ALIGN, "%s: packed and packed_t must be 16-byte aligned", fn);
+    return hip_status(bitnet::launch_transpose_packed(packed, N, K, packed_t, (hipStream_t)stream), fn);
+}
+
+int bitnet_linear_backward_input(const uint16_t* grad_y, const uint8_t* packed_t, const float* w_scale,
+                                 int64_t M, int64_t N, int64_t K, float* grad_n, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_linear_backward_input";
+    if (M < 0 || M > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
+    int s = check_backward_nk(N, K, fn);
+    if (s != BITNET_OK) return s;
+    if (M == 0) return BITNET_OK;
+    if (!grad_y || !packed_t || !w_scale || !grad_n)
+        return fail(BITNET_ERR_NULL, "%s: no pointer may be NULL", fn);
+    if (!aligned(grad_y, 16) || !aligned(packed_t, 16))
+        return fail(BITNET_ERR_ALIGN, "%s: grad_y and packed_t must be 16-byte aligned", fn);
+    if (!aligned(w_scale, 4) || !aligned(grad_n, 4))
+        return fail(BITNET_ERR_ALIGN, "%s: w_scale and grad_n must be 4-byte aligned", fn);
+    return hip_status(bitnet::launch_backward_input(grad_y, packed_t, w_scale, M, N, K, grad_n,
+                                                    (hipStream_t)stream),
+                      fn);
+}
+
+size_t bitnet_linear_backward_weight_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > kMaxRows || N < 64 || N > kMaxK || N % 64 != 0 || K < kMinK || K > kMaxK ||
+        K % 64 != 0)
+        return 0;
+    return bitnet::backward_weight_workspace_bytes(M, N, K);
+}
+
+int bitnet_linear_backward_weight(const uint16_t* grad_y, const int8_t* xq, const float* x_scale,
+                                  int64_t M, int64_t N, int64_t K, float* grad_w, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_linear_backward_weight";
+    if (M < 0 || M > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
+    int s = check_backward_nk(N, K, fn);
+    if (s != BITNET_OK) return s;
+    if (!grad_w) return fail(BITNET_ERR_NULL, "%s: grad_w must not be NULL", fn);
+    if (!aligned(grad_w, 4)) return fail(BITNET_ERR_ALIGN, "%s: grad_w must be 4-byte aligned", fn);
+    if (M == 0) {  // an empty sum: zero gradient
+        return hip_status(bitnet::launch_zero_f32(grad_w, N * K, (hipStream_t)stream), fn);
+    }
+    if (!grad_y || !xq || !x_scale) return fail(BITNET_ERR_NULL, "%s: no input pointer may be NULL", fn);
+    if (!aligned(grad_y, 16) || !aligned(xq, 16))
+        return fail(BITNET_ERR_ALIGN, "%s: grad_y and xq must be 16-byte aligned", fn);
+    if (!aligned(x_scale, 4)) return fail(BITNET_ERR_ALIGN, "%s: x_scale must be 4-byte aligned", fn);
+    const size_t need = bitnet::backward_weight_workspace_bytes(M, N, K);
+    if (!workspace || workspace_bytes < need)
+        return fail(BITNET_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(BITNET_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+    return hip_status(bitnet::launch_backward_weight(grad_y, xq, x_scale, M, N, K, grad_w, workspace,
+                                                     (hipStream_t)stream),
+                      fn);
+}
+
+size_t bitnet_rmsnorm_backward_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 1 || M > kMaxRows || K < kMinK || K > kMaxK || K % 64 != 0) return 0;
+    return bitnet::rmsnorm_backward_workspace_bytes(M, K);
+}
+
+int bitnet_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, const float* grad_n,
+                            int64_t M, int64_t K, float* grad_x, float* grad_gain, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_rmsnorm_backward";
+    if (M < 0 || M > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if ((s = check_eps(eps, fn)) != BITNET_OK) return s;
+    if (M == 0) {
+        if (grad_gain)
+            return hip_status(bitnet::launch_zero_f32(grad_gain, K, (hipStream_t)stream), fn);
+        return BITNET_OK;
+    }
+    if (!x || !grad_n || !grad_x) return fail(BITNET_ERR_NULL, "%s: x, grad_n and grad_x must not be NULL", fn);
+    if (!aligned(x, 4) || !aligned(grad_n, 4) || !aligned(grad_x, 4) || (gain && !aligned(gain, 4)) ||
+        (grad_gain && !aligned(grad_gain, 4)))
+        return fail(BITNET_ERR_ALIGN, "%s: arrays must be 4-byte aligned", fn);
+    if (grad_gain) {
+        const size_t need = bitnet::rmsnorm_backward_workspace_bytes(M, K);
+        if (!workspace || workspace_bytes < need)
+            return fail(BITNET_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 16)) return fail(BITNET_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+    }
+    return hip_status(bitnet::launch_rmsnorm_backward(x, gain, eps, grad_n, M, K, grad_x, grad_gain,
+                                                      workspace, (hipStream_t)stream),
+                      fn);
+}
+
 const char* bitnet_status_string(int status) {
     switch (status) {
         case BITNET_OK: return "ok";

@@ -1,0 +1,468 @@
+// backward.hip - BitLinear backward under the straight-through estimator.
+//
+// The estimator gives round() the gradient 1 (Hugging Face 1.58-bit write-up,
+// section "Straight-Through Estimator (STE)를 이용한 학습"), so both quantisers
+// pass gradients through unchanged.  Seen by it, the forward is y = n~ W~^T
+// with the dequantised operands n~ = d_x q_x (standing for the normalised
+// activation n = x * gain * r) and W~ = d_w q_w (standing for W), hence
+//   dL/dn = dL/dy W~        (bf16 x ternary contraction over the N outputs)
+//   dL/dW = (dL/dy)^T n~    (contraction over the M tokens)
+// and dL/dx follows from the RMSNorm in front of the quantiser (section
+// "양자화 메커니즘": the activations are normalised before quantisation).
+//
+// Both contractions run on v_mfma_f32_32x32x16_bf16 in one "NT" GEMM kernel,
+// C[r][c] = sum_j A[r][j] B[c][j], with both operands contiguous along j and
+// staged into LDS by the buffer-load-to-LDS path.  For dL/dn, B is the packed
+// ternary matrix transposed once to [K][N/4] (pack once, like the forward):
+// its tile stays 2-bit in LDS and each lane turns 8 codes into 8 bf16 values
+// in {-1, 0, 1} with two byte permutes per pair (the codes index a four-entry
+// table of bf16 bytes), so the products grad_y * q are exact and only the
+// float32 accumulation rounds.  For dL/dW the activation codes (exact in
+// bf16) are transposed to [K][M] and grad_y * d_x is transposed to [N][M] as a
+// bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi), |p - hi - lo| <= 2^-16 |p|);
+// each step multiplies both halves with the same codes.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace bitnet {
+namespace {
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
+constexpr uint32_t kOutOfRange = 0x80000000u;   // offset past every buffer here: loads 0
+constexpr int kBJ = 64;                          // reduction values per LDS stage
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {  // finite inputs
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// packed [N][K/4] -> packed_t [K][N/4], both in the forward's layout along
+// their rows (word g holds values 16g..16g+15; value 16g + 4i + b at bits
+// 2i..2i+1 of byte b).  One 64 x 64 tile per workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void transpose_packed_kernel(const uint8_t* __restrict__ packed,
+                                                                   int N, int K,
+                                                                   uint8_t* __restrict__ packed_t) {
+    __shared__ uint32_t tile[64][5];  // [n][word of k], padded
+    const int n0 = (int)blockIdx.y * 64, k0 = (int)blockIdx.x * 64;
+    const int t = threadIdx.x;
+    {
+        const int r = t / 4, w = t % 4;
+        tile[r][w] = *reinterpret_cast<const uint32_t*>(packed + (int64_t)(n0 + r) * (K / 4) + k0 / 4 + 4 * w);
+    }
+    __syncthreads();
+    const int kr = t / 4, wn = t % 4;  // output row k0 + kr, word wn (n = n0 + 16 wn ..)
+    const int kw = kr / 16, kshift = 8 * (kr % 4) + 2 * ((kr % 16) / 4);
+    uint32_t out = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t field = (tile[16 * wn + 4 * i + b][kw] >> kshift) & 3u;
+            out |= field << (8 * b + 2 * i);
+        }
+    *reinterpret_cast<uint32_t*>(packed_t + (int64_t)(k0 + kr) * (N / 4) + n0 / 4 + 4 * wn) = out;
+}
+
+// ---------------------------------------------------------------------------
+// NT GEMM on the bf16 matrix cores.  Workgroup tile BR x 128 (BR = 64 WR),
+// 2 x 2 waves, a wave WR/2 x 2 blocks of 32 x 32; K steps of 16 inside LDS
+// stages of 64.  TERN: B is 2-bit codes q+1 ([C][J/4] bytes), else bf16.
+// HILO: a second A operand (the low halves) multiplies the same B.
+// ---------------------------------------------------------------------------
+template <int WR, bool TERN, bool HILO>
+struct BwdCfg {
+    static constexpr int BR = 64 * WR;                       // rows per workgroup
+    static constexpr int BC = 128;                           // columns per workgroup
+    static constexpr int A_BYTES = BR * kBJ * 2;             // one A stage
+    static constexpr int B_BYTES = TERN ? BC * kBJ / 4 : BC * kBJ * 2;
+    static constexpr int STAGE = A_BYTES * (HILO ? 2 : 1) + B_BYTES;
+    static constexpr int A_SLOTS = A_BYTES / 16;              // 16-byte load slots
+    static constexpr int B_SLOTS = B_BYTES / 16;
+    static_assert(A_SLOTS % kThreads == 0, "whole A loads per thread");
+    static_assert(TERN ? B_SLOTS % kWave == 0 : B_SLOTS % kThreads == 0, "whole B loads per wave");
+    static_assert(2 * STAGE <= 160 * 1024, "LDS");
+};
+
+// Two bf16 values (-1, 0 or +1) from the codes (0, 1, 2) in bytes b and b + 1
+// of d: the codes select bytes of a table (low bytes 80 00 80, high bytes
+// BF 00 3F), so code c becomes the bf16 pattern of c - 1.
+template <int B>
+__device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t d) {
+    constexpr uint32_t dup = B == 0 ? 0x01010000u : 0x03030202u;
+    const uint32_t sel = __builtin_amdgcn_perm(d, d, dup) + 0x04000400u;
+    return __builtin_amdgcn_perm(0x003F00BFu, 0x00800080u, sel);
+}
+
+template <class C, bool TERN, bool HILO>
+__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2, const uint8_t* __restrict__ B,
+    int R, int Cn, int J, const float* __restrict__ scale_ptr, float* __restrict__ out) {
+    constexpr int WR = C::BR / 64;
+    __shared__ __align__(16) uint8_t lds[2][C::STAGE];
+    const int t = threadIdx.x, lane = t % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int wr = wave / 2, wc = wave % 2;
+    const int64_t r0 = (int64_t)blockIdx.y * C::BR;
+    const int64_t c0 = (int64_t)blockIdx.x * C::BC;
+    const float scale = scale_ptr != nullptr ? scale_ptr[0] : 1.0f;
+    const int a_rows = (int)min((int64_t)C::BR, (int64_t)R - r0);
+    const int b_rows = (int)min((int64_t)C::BC, (int64_t)Cn - c0);
+    const int b_row_bytes = TERN ? J / 4 : J * 2;
+    const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(A + r0 * J), (short)0, a_rows * J * 2, (int)kBufferWord3);
+    const __amdgpu_buffer_rsrc_t a2res = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(HILO ? A2 + r0 * J : A), (short)0, HILO ? a_rows * J * 2 : 0, (int)kBufferWord3);
+    const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(B + c0 * b_row_bytes), (short)0, b_rows * b_row_bytes, (int)kBufferWord3);
+
+    // A (and B when bf16) tiles: row r of 64 values = 8 granules of 16 bytes,
+    // granule g stored at position g ^ (r & 7) so that the 32 rows a fragment
+    // read touches spread over all banks.  Slot p of the tile is filled by a
+    // load of row p / 8, granule (p % 8) ^ (row & 7).
+    auto load_stage = [&](int buf, int j0) {
+#pragma unroll
+        for (int i = 0; i < C::A_SLOTS / kThreads; ++i) {
+            const int base = i * kThreads + wave * kWave;  // wave-uniform
+            const int p = base + lane, r = p / 8, g = (p % 8) ^ (r & 7);
+            const int j = j0 + 8 * g;
+            const uint32_t off = (r < a_rows && j < J) ? (uint32_t)((r * J + j) * 2) : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)&lds[buf][base * 16], 16, (int)off, 0, 0, 0);
+            if constexpr (HILO)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(a2res, (lds_void*)&lds[buf][C::A_BYTES + base * 16],
+                                                         16, (int)off, 0, 0, 0);
+        }
+        constexpr int BOFF = C::A_BYTES * (HILO ? 2 : 1);
+        if constexpr (TERN) {
+            // row c: 16 bytes (64 codes) per stage, slot c
+            const int base = wave * kWave;
+            if (base < C::B_SLOTS) {
+                const int c = base + lane;
+                const uint32_t off = c < b_rows ? (uint32_t)(c * b_row_bytes + j0 / 4) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (lds_void*)&lds[buf][BOFF + base * 16], 16, (int)off, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::B_SLOTS / kThreads; ++i) {
+                const int base = i * kThreads + wave * kWave;
+                const int p = base + lane, r = p / 8, g = (p % 8) ^ (r & 7);
+                const int j = j0 + 8 * g;
+                const uint32_t off = (r < b_rows && j < J) ? (uint32_t)((r * J + j) * 2) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (lds_void*)&lds[buf][BOFF + base * 16], 16, (int)off, 0, 0, 0);
+            }
+        }
+    };
+
+    v16f acc[WR][2], acc2[HILO ? WR : 1][2];
+#pragma unroll
+    for (int i = 0; i < WR; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            acc[i][j] = v16f{};
+            if constexpr (HILO) acc2[i][j] = v16f{};
+        }
+
+    const int h = lane / 32, l32 = lane % 32;
+    auto frag = [&](const uint8_t* tile, int row, int g) {
+        return *reinterpret_cast<const uint4*>(tile + (row * 8 + (g ^ (row & 7))) * 16);
+    };
+    auto compute = [&](int buf) {
+        const uint8_t* at = lds[buf];
+        const uint8_t* bt = lds[buf] + C::A_BYTES * (HILO ? 2 : 1);
+        uint4 bq[2];
+        if constexpr (TERN) {
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+                bq[cb] = *reinterpret_cast<const uint4*>(bt + (wc * 64 + cb * 32 + l32) * 16);
+        }
+#pragma unroll
+        for (int s = 0; s < kBJ / 16; ++s) {
+            uint4 bf[2];
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                if constexpr (TERN) {
+                    const uint32_t w = s == 0 ? bq[cb].x : (s == 1 ? bq[cb].y : (s == 2 ? bq[cb].z : bq[cb].w));
+                    const uint32_t d0 = (w >> (4 * h)) & 0x03030303u;      // values 8h .. 8h+3 of the step
+                    const uint32_t d1 = (w >> (4 * h + 2)) & 0x03030303u;  // values 8h+4 .. 8h+7
+                    bf[cb] = make_uint4(codes_to_bf16x2<0>(d0), codes_to_bf16x2<2>(d0),
+                                        codes_to_bf16x2<0>(d1), codes_to_bf16x2<2>(d1));
+                } else {
+                    bf[cb] = frag(bt, wc * 64 + cb * 32 + l32, 2 * s + h);
+                }
+            }
+#pragma unroll
+            for (int rb = 0; rb < WR; ++rb) {
+                const int row = wr * (32 * WR) + rb * 32 + l32;
+                const uint4 af = frag(at, row, 2 * s + h);
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(v8bf, af), __builtin_bit_cast(v8bf, bf[cb]), acc[rb][cb], 0, 0, 0);
+                if constexpr (HILO) {
+                    const uint4 af2 = frag(at + C::A_BYTES, row, 2 * s + h);
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        acc2[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(v8bf, af2), __builtin_bit_cast(v8bf, bf[cb]), acc2[rb][cb], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    const int nj = (J + kBJ - 1) / kBJ;
+    load_stage(0, 0);
+    for (int js = 0; js < nj; ++js) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // stage js landed for every wave; stage js - 1 fully read
+        if (js + 1 < nj) load_stage((js + 1) % 2, (js + 1) * kBJ);
+        compute(js % 2);
+    }
+
+    // D[i][j] of a 32 x 32 block: lane j + 32 ((i / 4) % 2), element 4 (i / 8) + i % 4.
+#pragma unroll
+    for (int rb = 0; rb < WR; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = r0 + wr * (32 * WR) + rb * 32 + 8 * (e / 4) + 4 * h + e % 4;
+                const int64_t col = c0 + wc * 64 + cb * 32 + l32;
+                float v = acc[rb][cb][e];
+                if constexpr (HILO) v += acc2[rb][cb][e];
+                if (row < R && col < Cn) out[row * Cn + col] = v * scale;
+            }
+}
+
+// ---------------------------------------------------------------------------
+// Operands of dL/dW: p = grad_y[m][n] * d_x[m] transposed to [N][Mp] as
+// bf16 hi and lo, and the codes transposed to [K][Mp] as bf16; columns
+// m >= M are zero (Mp = M rounded up to 64).  One 64 x 64 tile per workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void prep_grad_kernel(const uint16_t* __restrict__ g,
+                                                             const float* __restrict__ d_x, int M,
+                                                             int N, int Mp, uint16_t* __restrict__ hi,
+                                                             uint16_t* __restrict__ lo) {
+    __shared__ float tile[64][65];  // [m][n]
+    const int m0 = (int)blockIdx.x * 64, n0 = (int)blockIdx.y * 64;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // 64 rows x 8 granules of 8 bf16
+        const int p = t + kThreads * i, r = p / 8, gr = p % 8;
+        const int m = m0 + r;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        float s = 0.f;
+        if (m < M) {
+            v = *reinterpret_cast<const uint4*>(g + (int64_t)m * N + n0 + 8 * gr);
+            s = d_x[m];
+        }
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tile[r][8 * gr + 2 * e] = bf16_lo(w[e]) * s;
+            tile[r][8 * gr + 2 * e + 1] = bf16_hi(w[e]) * s;
+        }
+    }
+    __syncthreads();
+    const int nr = t / 4, mc = (t % 4) * 16;  // output row n0 + nr, m = m0 + mc .. +15
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float p0 = tile[mc + 2 * e][nr], p1 = tile[mc + 2 * e + 1][nr];
+        const uint16_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
+        const uint16_t l0 = bf16_rne(p0 - __uint_as_float((uint32_t)h0 << 16));
+        const uint16_t l1 = bf16_rne(p1 - __uint_as_float((uint32_t)h1 << 16));
+        hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    uint4* ho = reinterpret_cast<uint4*>(hi + (int64_t)(n0 + nr) * Mp + m0 + mc);
+    uint4* lo4 = reinterpret_cast<uint4*>(lo + (int64_t)(n0 + nr) * Mp + m0 + mc);
+    ho[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    ho[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
+    lo4[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    lo4[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+}
+
+__global__ __launch_bounds__(kThreads) void prep_codes_kernel(const int8_t* __restrict__ xq, int M,
+                                                              int K, int Mp, uint16_t* __restrict__ xt) {
+    __shared__ int tile[64][65];  // [m][k]
+    const int m0 = (int)blockIdx.x * 64, k0 = (int)blockIdx.y * 64;
+    const int t = threadIdx.x;
+    {
+        const int r = t / 4, gr = t % 4;  // 64 rows x 4 granules of 16 codes
+        const int m = m0 + r;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (m < M) v = *reinterpret_cast<const uint4*>(xq + (int64_t)m * K + k0 + 16 * gr);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tile[r][16 * gr + e] = (int)(int8_t)(w[e / 4] >> (8 * (e % 4)));
+    }
+    __syncthreads();
+    const int kr = t / 4, mc = (t % 4) * 16;
+    uint32_t o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {  // a code is exact in bf16: the top half of its float
+        const uint32_t b0 = __float_as_uint((float)tile[mc + 2 * e][kr]) >> 16;
+        const uint32_t b1 = __float_as_uint((float)tile[mc + 2 * e + 1][kr]) >> 16;
+        o[e] = b0 | (b1 << 16);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(xt + (int64_t)(k0 + kr) * Mp + m0 + mc);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm backward, one workgroup per token: float64 sums of x^2 and of
+// grad_n * x * gain, then grad_x = gain r grad_n - x r^3 dot / K in float32.
+// r goes to the workspace for the gain gradient.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void rmsnorm_bwd_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps,
+    const float* __restrict__ grad_n, int K, float* __restrict__ grad_x, double* __restrict__ r_out) {
+    __shared__ double red[2][kThreads / kWave];
+    const int64_t m = blockIdx.x;
+    const int t = threadIdx.x, lane = t % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const uint16_t* xr = x + m * K;
+    const float* gr = grad_n + m * K;
+    double ss = 0.0, dot = 0.0;
+    for (int k = t; k < K; k += kThreads) {
+        const double xv = (double)__uint_as_float((uint32_t)xr[k] << 16);
+        const double g = gain != nullptr ? (double)gain[k] : 1.0;
+        ss = __fma_rn(xv, xv, ss);
+        dot = __fma_rn((double)gr[k] * xv, g, dot);
+    }
+    ss = wave_sum_dpp(ss);
+    dot = wave_sum_dpp(dot);
+    if (lane == 0) {
+        red[0][wave] = ss;
+        red[1][wave] = dot;
+    }
+    __syncthreads();
+    ss = 0.0;
+    dot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+        ss += red[0][w];
+        dot += red[1][w];
+    }
+    const double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+    const double coef = r * r * r * dot / (double)K;
+    for (int k = t; k < K; k += kThreads) {
+        const double xv = (double)__uint_as_float((uint32_t)xr[k] << 16);
+        const double g = gain != nullptr ? (double)gain[k] : 1.0;
+        grad_x[m * K + k] = (float)(g * r * (double)gr[k] - xv * coef);
+    }
+    if (t == 0 && r_out != nullptr) r_out[m] = r;
+}
+
+// grad_gain[k] = sum_m grad_n[m][k] x[m][k] r[m]: partial sums over token
+// chunks (float64), then the chunks in order.
+constexpr int kGainChunk = 64;
+__global__ __launch_bounds__(kThreads) void gain_partial_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ grad_n, const double* __restrict__ r,
+    int M, int K, double* __restrict__ part) {
+    const int k = (int)blockIdx.x * kThreads + threadIdx.x;
+    const int mc = (int)blockIdx.y;
+    if (k >= K) return;
+    double s = 0.0;
+    const int m1 = min(M, (mc + 1) * kGainChunk);
+    for (int m = mc * kGainChunk; m < m1; ++m) {
+        const double xv = (double)__uint_as_float((uint32_t)x[(int64_t)m * K + k] << 16);
+        s = __fma_rn((double)grad_n[(int64_t)m * K + k] * xv, r[m], s);
+    }
+    part[(int64_t)mc * K + k] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void gain_final_kernel(const double* __restrict__ part, int chunks,
+                                                              int K, float* __restrict__ grad_gain) {
+    const int k = (int)blockIdx.x * kThreads + threadIdx.x;
+    if (k >= K) return;
+    double s = 0.0;
+    for (int c = 0; c < chunks; ++c) s += part[(int64_t)c * K + k];
+    grad_gain[k] = (float)s;
+}
+
+__global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ p, int64_t count) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < count; i += (int64_t)gridDim.x * kThreads)
+        p[i] = 0.f;
+}
+
+using CfgIn = BwdCfg<4, true, false>;   // dL/dn: 256 x 128 tiles, 2-bit B
+using CfgW = BwdCfg<2, false, true>;    // dL/dW: 128 x 128 tiles, bf16 B, hi + lo A
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+}  // namespace
+
+hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t stream) {
+    if (count <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((count + kThreads - 1) / kThreads, 4096);
+    return launch_kernel(zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, count);
+}
+
+hipError_t launch_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed_t,
+                                   hipStream_t stream) {
+    return launch_kernel(transpose_packed_kernel, dim3((unsigned)(K / 64), (unsigned)(N / 64)), dim3(kThreads),
+                         0, stream, packed, (int)N, (int)K, packed_t);
+}
+
+hipError_t launch_backward_input(const uint16_t* grad_y, const uint8_t* packed_t, const float* w_scale,
+                                 int64_t M, int64_t N, int64_t K, float* grad_n, hipStream_t stream) {
+    const dim3 grid((unsigned)((K + CfgIn::BC - 1) / CfgIn::BC), (unsigned)((M + CfgIn::BR - 1) / CfgIn::BR));
+    return launch_kernel((bwd_gemm_kernel<CfgIn, true, false>), grid, dim3(kThreads), 0, stream, grad_y,
+                         (const uint16_t*)nullptr, packed_t, (int)M, (int)K, (int)N, w_scale, grad_n);
+}
+
+size_t backward_weight_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int64_t Mp = round_up(M, 64);
+    return (size_t)((2 * N + K) * Mp * 2);
+}
+
+hipError_t launch_backward_weight(const uint16_t* grad_y, const int8_t* xq, const float* x_scale,
+                                  int64_t M, int64_t N, int64_t K, float* grad_w, void* workspace,
+                                  hipStream_t stream) {
+    const int64_t Mp = round_up(M, 64);
+    uint16_t* hi = static_cast<uint16_t*>(workspace);
+    uint16_t* lo = hi + N * Mp;
+    uint16_t* xt = lo + N * Mp;
+    hipError_t e = launch_kernel(prep_grad_kernel, dim3((unsigned)(Mp / 64), (unsigned)(N / 64)), dim3(kThreads),
+                                 0, stream, grad_y, x_scale, (int)M, (int)N, (int)Mp, hi, lo);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(prep_codes_kernel, dim3((unsigned)(Mp / 64), (unsigned)(K / 64)), dim3(kThreads), 0, stream,
+                      xq, (int)M, (int)K, (int)Mp, xt);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)((K + CfgW::BC - 1) / CfgW::BC), (unsigned)((N + CfgW::BR - 1) / CfgW::BR));
+    return launch_kernel((bwd_gemm_kernel<CfgW, false, true>), grid, dim3(kThreads), 0, stream,
+                         (const uint16_t*)hi, (const uint16_t*)lo, reinterpret_cast<const uint8_t*>(xt), (int)N,
+                         (int)K, (int)Mp, (const float*)nullptr, grad_w);
+}
+
+size_t rmsnorm_backward_workspace_bytes(int64_t M, int64_t K) {
+    const int64_t chunks = (M + kGainChunk - 1) / kGainChunk;
+    return (size_t)(round_up(M, 32) * 8 + chunks * K * 8);
+}
+
+hipError_t launch_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, const float* grad_n,
+                                   int64_t M, int64_t K, float* grad_x, float* grad_gain, void* workspace,
+                                   hipStream_t stream) {
+    double* r = static_cast<double*>(workspace);
+    hipError_t e = launch_kernel(rmsnorm_bwd_kernel, dim3((unsigned)M), dim3(kThreads), 0, stream, x, gain, eps,
+                                 grad_n, (int)K, grad_x, grad_gain != nullptr ? r : (double*)nullptr);
+    if (e != hipSuccess || grad_gain == nullptr) return e;
+    const int chunks = (int)((M + kGainChunk - 1) / kGainChunk);
+    double* part = r + round_up(M, 32);
+    const unsigned kb = (unsigned)((K + kThreads - 1) / kThreads);
+    e = launch_kernel(gain_partial_kernel, dim3(kb, (unsigned)chunks), dim3(kThreads), 0, stream, x, grad_n,
+                      (const double*)r, (int)M, (int)K, part);
+    if (e != hipSuccess) return e;
+    return launch_kernel(gain_final_kernel, dim3(kb), dim3(kThreads), 0, stream, (const double*)part, chunks,
+                         (int)K, grad_gain);
+}
+
+}  // namespace bitnet

@@ -106,4 +106,26 @@ hipError_t launch_gemm_f6(const uint8_t* xq6, const float* x_scale, const int32_
                           const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                           int64_t K, float* y, int32_t* acc, hipStream_t stream);
 
+// --- backward under the straight-through estimator (backward.hip) --------
+// p[0 .. count) = 0 by a kernel (no memset node if the caller captures a graph).
+hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t stream);
+// packed [N][K/4] -> packed_t [K][N/4] (N, K multiples of 64).
+hipError_t launch_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed_t,
+                                   hipStream_t stream);
+// grad_n [M][K] = d_w * grad_y (bf16 [M][N]) @ q_w, with q_w read from packed_t.
+hipError_t launch_backward_input(const uint16_t* grad_y, const uint8_t* packed_t, const float* w_scale,
+                                 int64_t M, int64_t N, int64_t K, float* grad_n, hipStream_t stream);
+// grad_w [N][K] = sum_m grad_y[m][n] d_x[m] q_x[m][k]; workspace of
+// backward_weight_workspace_bytes(M, N, K) bytes, 16-byte aligned.
+size_t backward_weight_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_backward_weight(const uint16_t* grad_y, const int8_t* xq, const float* x_scale,
+                                  int64_t M, int64_t N, int64_t K, float* grad_w, void* workspace,
+                                  hipStream_t stream);
+// RMSNorm backward: grad_x [M][K], optional grad_gain [K] (workspace of
+// rmsnorm_backward_workspace_bytes(M, K) bytes when grad_gain is requested).
+size_t rmsnorm_backward_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, const float* grad_n,
+                                   int64_t M, int64_t K, float* grad_x, float* grad_gain, void* workspace,
+                                   hipStream_t stream);
+
 }  // namespace bitnet

@@ -1,5 +1,6 @@
 /*
- * bitnet.h - C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear forward pass.
+ * bitnet.h - C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear forward pass
+ * and of its straight-through-estimator backward.
  *
  * A BitLinear layer replaces a bias-free linear layer y = W x.  Its weights are
  * quantised once to the three values {-1, 0, +1} with one per-tensor scale and
@@ -64,7 +65,7 @@ typedef enum {
     BITNET_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement
                                     (Hadamard with K not a power of two in [256, 32768]) */
     BITNET_ERR_ALIGN = 4,        /* a device pointer is not aligned as documented */
-    BITNET_ERR_WORKSPACE = 5,    /* pack workspace missing or too small */
+    BITNET_ERR_WORKSPACE = 5,    /* a workspace is missing or too small */
     BITNET_ERR_HIP = 6,          /* a HIP launch or runtime call failed */
     BITNET_ERR_VALUE = 7         /* a scalar argument is invalid (eps < 0 or not finite,
                                     hadamard not 0 or 1) */
@@ -247,6 +248,87 @@ int bitnet_bitlinear_forward_grouped(const uint16_t* x, const float* gain, float
                                      const int64_t* group_rows, int groups, int64_t M, int64_t K,
                                      int8_t* xq, float* x_scale, int32_t* x_qsum, float* y,
                                      int32_t* acc, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Backward pass under the straight-through estimator ([FT] "Straight-Through
+ * Estimator (STE)를 이용한 학습": round() is given the gradient 1, so both
+ * quantisers pass the gradient through).  Seen by the estimator the forward is
+ * y = n~ W~^T with n~[m][k] = d_x[m] q_x[m][k] (standing for the normalised
+ * activation n = x * gain * r, r = 1 / sqrt(mean(x^2) + eps), [FT]
+ * "양자화 메커니즘": normalisation before quantisation) and W~ = d_w q_w
+ * (standing for the latent weights W).  These calls compute, for a loss L,
+ *   dL/dn = dL/dy W~,   dL/dW = (dL/dy)^T n~,   dL/dx, dL/dgain from dL/dn.
+ * They cover the end of the [FT] "동적 워밍업 양자화" schedule (lambda = 1, fully
+ * quantised); with lambda < 1 the forward operands are blends of the
+ * full-precision and quantised values, which is a dense float contraction and
+ * not a ternary one.  Gradients are bf16 [M][N] (uint16 bit patterns); shapes
+ * need N and K multiples of 64 in [64, 65536] and 0 <= M <= 2^31 - 1.
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * The packed weights with the roles of N and K exchanged, for dL/dn:
+ *   packed    in  uint8 [N][K/4] (bitnet_pack_weights), 16-byte aligned;
+ *   packed_t  out uint8 [K][N/4], 16-byte aligned, in the packed layout along
+ *                 its rows (row k, word g holds the fields of n = 16g ..
+ *                 16g+15, n = 16g + 4i + b in bits 2i..2i+1 of byte b).
+ * Pack once per weight update, like the forward's packing.
+ */
+int bitnet_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed_t,
+                            void* stream);
+
+/*
+ * Gradient with respect to the normalised activations (the STE input side):
+ *   grad_y    in  bf16 [M][N], 16-byte aligned;
+ *   packed_t  in  bitnet_transpose_packed output [K][N/4], 16-byte aligned;
+ *   w_scale   in  float32 [2] from bitnet_pack_weights (d_w is w_scale[0]);
+ *   grad_n    out float32 [M][K]:  grad_n[m][k] = d_w * sum_n grad_y[m][n] q_w[n][k].
+ * The products grad_y * q_w (q_w in {-1, 0, 1}) are exact; the sum is
+ * accumulated in float32 on the bf16 matrix cores.  M = 0 is a no-op.
+ */
+int bitnet_linear_backward_input(const uint16_t* grad_y, const uint8_t* packed_t,
+                                 const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                 float* grad_n, void* stream);
+
+/* Workspace bytes of bitnet_linear_backward_weight (0 for an invalid shape or M = 0). */
+size_t bitnet_linear_backward_weight_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Gradient with respect to the latent weights (the STE weight side):
+ *   grad_y     in  bf16 [M][N], 16-byte aligned;
+ *   xq         in  int8 codes [M][K] of the forward (bitnet_quant_act), 16-byte aligned;
+ *   x_scale    in  float32 [M], d_x of the forward;
+ *   grad_w     out float32 [N][K]:  grad_w[n][k] = sum_m grad_y[m][n] d_x[m] q_x[m][k];
+ *   workspace  caller-owned device scratch of
+ *              bitnet_linear_backward_weight_workspace_bytes(M, N, K) bytes,
+ *              16-byte aligned (transposed operands; contents undefined after).
+ * grad_y * d_x is rounded once to float32 and carried as two bf16 halves
+ * (relative error <= 2^-16 per term); the codes are exact; the sum over m is
+ * accumulated in float32 on the bf16 matrix cores.  M = 0 writes zeros.
+ */
+int bitnet_linear_backward_weight(const uint16_t* grad_y, const int8_t* xq, const float* x_scale,
+                                  int64_t M, int64_t N, int64_t K, float* grad_w,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of bitnet_rmsnorm_backward with a gain gradient (0 if invalid or M = 0). */
+size_t bitnet_rmsnorm_backward_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * Backward of the RMSNorm in front of the quantiser, n = x * gain * r:
+ *   x          in  bf16 [M][K] (the forward's input), gain in float32 [K] or NULL (1);
+ *   grad_n     in  float32 [M][K] (bitnet_linear_backward_input);
+ *   grad_x     out float32 [M][K]:
+ *              grad_x[m][j] = gain[j] r grad_n[m][j] - x[m][j] r^3 / K * sum_k grad_n[m][k] x[m][k] gain[k];
+ *   grad_gain  out float32 [K] or NULL:  grad_gain[k] = sum_m grad_n[m][k] x[m][k] r[m];
+ *   workspace  needed only with grad_gain: bitnet_rmsnorm_backward_workspace_bytes(M, K)
+ *              bytes, 16-byte aligned.
+ * r and both sums in float64, results rounded to float32.  Arrays 4-byte aligned.
+ * M = 0 writes zeros to grad_gain (if given).
+ */
+int bitnet_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, const float* grad_n,
+                            int64_t M, int64_t K, float* grad_x, float* grad_gain, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Profiling hook: arm two hipEvent_t (passed as void*; either may be NULL) for

@@ -205,3 +205,49 @@ def test_f6_argument_errors(L):
     assert fwd(xq=A4) == 4
     assert fwd(acc=BAD) == 4
     assert fwd(M=0, xq=0) == 0
+
+
+def test_backward_argument_errors(L):
+    p = ctypes.c_void_p
+    # transpose: N and K multiples of 64, pointers 16-byte aligned
+    assert L.bitnet_transpose_packed(p(A16), 100, 256, p(A16), None) == 2
+    assert L.bitnet_transpose_packed(p(A16), 128, 96, p(A16), None) == 2
+    assert L.bitnet_transpose_packed(None, 128, 256, p(A16), None) == 1
+    assert L.bitnet_transpose_packed(p(A16), 128, 256, p(A4), None) == 4
+    # grad_n
+    bi = lambda gy=A16, pt=A16, ws=A4, M=8, N=128, K=256, out=A4: L.bitnet_linear_backward_input(
+        p(gy), p(pt), p(ws), M, N, K, p(out), None)
+    assert bi(M=-1) == 2
+    assert bi(N=96) == 2
+    assert bi(K=32) == 2
+    assert bi(gy=0) == 1
+    assert bi(out=0) == 1
+    assert bi(gy=A4) == 4
+    assert bi(pt=BAD) == 4
+    assert bi(M=0, gy=0, pt=0) == 0   # empty batch: nothing enqueued
+    # grad_w: workspace size and alignment
+    need = L.bitnet_linear_backward_weight_workspace_bytes(8, 128, 256)
+    assert need == (2 * 128 + 256) * 64 * 2
+    assert L.bitnet_linear_backward_weight_workspace_bytes(0, 128, 256) == 0
+    assert L.bitnet_linear_backward_weight_workspace_bytes(8, 100, 256) == 0
+    bw = lambda gy=A16, xq=A16, sx=A4, M=8, N=128, K=256, out=A4, ws=A16, wsb=need: \
+        L.bitnet_linear_backward_weight(p(gy), p(xq), p(sx), M, N, K, p(out), p(ws), wsb, None)
+    assert bw(N=64 + 32) == 2
+    assert bw(out=0) == 1
+    assert bw(gy=0) == 1
+    assert bw(xq=A4) == 4
+    assert bw(ws=0) == 5
+    assert bw(wsb=need - 1) == 5
+    assert bw(ws=A4) == 4
+    # RMSNorm backward: the workspace is needed only with a gain gradient
+    rb = lambda x=A16, g=None, eps=1e-5, gn=A4, M=8, K=256, gx=A4, gg=None, ws=None, wsb=0: \
+        L.bitnet_rmsnorm_backward(p(x), None if g is None else p(g), ctypes.c_float(eps), p(gn), M, K,
+                                  p(gx), None if gg is None else p(gg), None if ws is None else p(ws),
+                                  wsb, None)
+    assert rb(K=100) == 2
+    assert rb(eps=-1.0) == 7
+    assert rb(x=0) == 1
+    assert rb(gx=BAD) == 4
+    assert rb(gg=A4) == 5
+    assert rb(gg=A4, ws=A4, wsb=L.bitnet_rmsnorm_backward_workspace_bytes(8, 256)) == 4
+    assert L.bitnet_rmsnorm_backward_workspace_bytes(8, 256) == 32 * 8 + 1 * 256 * 8
