@@ -60,6 +60,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix-core peak, 5.0 POP/s
 PEAK_CLOCK_GHZ = 2.4        # the engine clock that peak is quoted at
 FP6_PEAK_TOPS = 10100.0     # MI355X dense fp6 / fp4 matrix-core peak, 10.1 PFLOP/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, 2.5 PFLOP/s
 ROTATE_BYTES = 1 << 30      # > 4 x the 256 MB Infinity Cache
 METRIC = "BitLinear decode GEMV weight GB/s (%HBM peak); prefill int8 TOPS (%MFMA peak)"
 
@@ -82,7 +83,7 @@ def parse_args():
     ap.add_argument("--block-steps", type=int, default=200, help="timed steps per token count of the block leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES, ten times (HBM counter calibration)")
-    ap.add_argument("--legs", default="decode,prefill,hadamard,block",
+    ap.add_argument("--legs", default="decode,prefill,hadamard,block,backward",
                     help="comma-separated legs to run (the headline needs decode)")
     ap.add_argument("--cpu-one-core-seconds", type=float, default=5.0,
                     help="wall time budget of the one-core CPU-oracle sample")
@@ -427,6 +428,53 @@ def hadamard_bench(args, dev, bt, torch, synth):
     return out
 
 
+def backward_bench(args, dev, bt, torch, synth):
+    """STE backward of the prefill layer (M 2048 tokens, K 4096 -> N 14336)."""
+    layer = synth.workload("prefill")[0]
+    M, K, N = layer.M, layer.K, layer.N
+    packed, w_scale = bt.pack_weights(torch.from_numpy(layer.weights()).to(dev))
+    packed_t = bt.transpose_packed(packed, K)
+    x = torch.from_numpy(layer.activations().view(np.int16)).to(dev).view(torch.bfloat16)
+    xq, xs, _ = bt.quant_act(x, None, 1e-5)
+    rng = np.random.default_rng(7001)
+    gy = torch.from_numpy(synth.bf16_bits(rng.standard_normal((M, N)).astype(np.float32) * 1e-2)
+                          .view(np.int16)).to(dev).view(torch.bfloat16)
+    gn = torch.empty((M, K), dtype=torch.float32, device=dev)
+    gw = torch.empty((N, K), dtype=torch.float32, device=dev)
+    ws = torch.empty(bt.lib().bitnet_linear_backward_weight_workspace_bytes(M, N, K), dtype=torch.uint8,
+                     device=dev)
+    pt = torch.empty_like(packed_t)
+    tr = lambda: bt.transpose_packed(packed, K, out=pt)
+    bin_ = lambda: bt.linear_backward_input(gy, packed_t, w_scale, out=gn)
+    bw = lambda: bt.linear_backward_weight(gy, xq, xs, out=gw, workspace=ws)
+    rb = lambda: bt.rmsnorm_backward(x, gn, None, 1e-5)
+    for _ in range(3):
+        tr(); bin_(); bw(); rb()
+    torch.cuda.synchronize()
+    iters = max(5, args.prefill_iters // 2)
+    tr_us = time_launches(tr, iters, bt)
+    in_us = time_launches(bin_, iters, bt)
+    rb_us = time_launches(rb, iters, bt)
+    w_ms, _ = timed(lambda n: [bw() for _ in range(n)], iters, torch)  # three kernels per call
+    flops = 2.0 * M * N * K
+    w_us = w_ms * 1e3
+    rb_bytes = M * K * (2 + 4 + 4) + 8 * M
+    return {
+        "workload": f"STE backward of the prefill layer: grad_y bf16 [{M}][{N}], ternary W [{N}][{K}], "
+                    "int8 codes of x; grad_n, grad_w, RMSNorm backward",
+        "grad_n_us": round(in_us, 2),
+        "grad_n_TFLOPs": round(flops / (in_us * 1e-6) / 1e12, 1),
+        "grad_n_frac_bf16_peak": round(flops / (in_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "grad_w_us": round(w_us, 2),
+        "grad_w_TFLOPs": round(flops / (w_us * 1e-6) / 1e12, 1),
+        "grad_w_note": "three kernels per call (operand transposes + GEMM); the GEMM runs the hi and "
+                       "lo halves, 2x the algorithmic 2 M N K flops counted here",
+        "rmsnorm_bwd_us": round(rb_us, 2),
+        "rmsnorm_bwd_GB_s": round(rb_bytes / rb_us / 1e3, 1),
+        "transpose_packed_us": round(tr_us, 2),
+    }
+
+
 class GroupedLayer:
     """Projections sharing one input (q|k|v or gate|up) stacked row-wise, run
     with one bitnet_bitlinear_forward_grouped call per step."""
@@ -564,7 +612,7 @@ def main():
     if "decode" not in legs:
         # Secondary legs only (used for per-kernel counter runs); no headline line.
         for name, fn in (("prefill", prefill_bench), ("hadamard", hadamard_bench),
-                         ("block", block_bench)):
+                         ("block", block_bench), ("backward", backward_bench)):
             if name in legs:
                 secondary[name] = fn(args, dev, bt, torch, synth)
                 torch.cuda.empty_cache()
@@ -580,7 +628,7 @@ def main():
 
     if not args.no_secondary:
         for name, fn in (("prefill", prefill_bench), ("hadamard", hadamard_bench),
-                         ("block", block_bench)):
+                         ("block", block_bench), ("backward", backward_bench)):
             if name in legs:
                 secondary[name] = fn(args, dev, bt, torch, synth)
                 log(f"{name}: {secondary[name]}")

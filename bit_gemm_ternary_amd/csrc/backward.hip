@@ -17,10 +17,15 @@
 // its tile stays 2-bit in LDS and each lane turns 8 codes into 8 bf16 values
 // in {-1, 0, 1} with two byte permutes per pair (the codes index a four-entry
 // table of bf16 bytes), so the products grad_y * q are exact and only the
-// float32 accumulation rounds.  For dL/dW the activation codes (exact in
-// bf16) are transposed to [K][M] and grad_y * d_x is transposed to [N][M] as a
-// bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi), |p - hi - lo| <= 2^-16 |p|);
-// each step multiplies both halves with the same codes.
+// float32 accumulation rounds.  For dL/dW, p = grad_y * d_x is carried as a
+// bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi), |p - hi - lo| <= 2^-16 |p|)
+// and the activation codes (exact in bf16) are repeated: the operands are
+// A = [hi | lo] ([N][2 Mp]) and B = [codes | codes] ([K][2 Mp]), transposed so
+// that the token index m runs along the rows, and the same kernel sums the
+// 2 Mp products.  Tiles are 128 x 128 with four waves of 64 x 64: small enough
+// for two workgroups per CU, which measured faster than one workgroup with
+// larger tiles (less operand reuse, but the second workgroup hides the LDS and
+// barrier latencies).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -71,22 +76,23 @@ __global__ __launch_bounds__(kThreads) void transpose_packed_kernel(const uint8_
 }
 
 // ---------------------------------------------------------------------------
-// NT GEMM on the bf16 matrix cores.  Workgroup tile BR x 128 (BR = 64 WR),
-// 2 x 2 waves, a wave WR/2 x 2 blocks of 32 x 32; K steps of 16 inside LDS
+// NT GEMM on the bf16 matrix cores.  Workgroup tile BR x BC = 64 WR x 64 WC,
+// 2 x 2 waves, a wave WR x WC blocks of 32 x 32; K steps of 16 inside LDS
 // stages of 64.  TERN: B is 2-bit codes q+1 ([C][J/4] bytes), else bf16.
-// HILO: a second A operand (the low halves) multiplies the same B.
 // ---------------------------------------------------------------------------
-template <int WR, bool TERN, bool HILO>
+template <int WR_, int WC_, bool TERN>
 struct BwdCfg {
+    static constexpr int WR = WR_, WC = WC_;                 // 32 x 32 blocks per wave
     static constexpr int BR = 64 * WR;                       // rows per workgroup
-    static constexpr int BC = 128;                           // columns per workgroup
+    static constexpr int BC = 64 * WC;                       // columns per workgroup
     static constexpr int A_BYTES = BR * kBJ * 2;             // one A stage
     static constexpr int B_BYTES = TERN ? BC * kBJ / 4 : BC * kBJ * 2;
-    static constexpr int STAGE = A_BYTES * (HILO ? 2 : 1) + B_BYTES;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_SLOTS = A_BYTES / 16;              // 16-byte load slots
     static constexpr int B_SLOTS = B_BYTES / 16;
     static_assert(A_SLOTS % kThreads == 0, "whole A loads per thread");
-    static_assert(TERN ? B_SLOTS % kWave == 0 : B_SLOTS % kThreads == 0, "whole B loads per wave");
+    static_assert(TERN ? (B_SLOTS % kWave == 0 && B_SLOTS <= kThreads) : B_SLOTS % kThreads == 0,
+                  "whole B loads per wave");
     static_assert(2 * STAGE <= 160 * 1024, "LDS");
 };
 
@@ -100,11 +106,11 @@ __device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t d) {
     return __builtin_amdgcn_perm(0x003F00BFu, 0x00800080u, sel);
 }
 
-template <class C, bool TERN, bool HILO>
+template <class C, bool TERN>
 __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ A2, const uint8_t* __restrict__ B,
-    int R, int Cn, int J, const float* __restrict__ scale_ptr, float* __restrict__ out) {
-    constexpr int WR = C::BR / 64;
+    const uint16_t* __restrict__ A, const uint8_t* __restrict__ B, int R, int Cn, int J,
+    const float* __restrict__ scale_ptr, float* __restrict__ out) {
+    constexpr int WR = C::WR, WC = C::WC;
     __shared__ __align__(16) uint8_t lds[2][C::STAGE];
     const int t = threadIdx.x, lane = t % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
@@ -117,8 +123,6 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
     const int b_row_bytes = TERN ? J / 4 : J * 2;
     const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(A + r0 * J), (short)0, a_rows * J * 2, (int)kBufferWord3);
-    const __amdgpu_buffer_rsrc_t a2res = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(HILO ? A2 + r0 * J : A), (short)0, HILO ? a_rows * J * 2 : 0, (int)kBufferWord3);
     const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(B + c0 * b_row_bytes), (short)0, b_rows * b_row_bytes, (int)kBufferWord3);
 
@@ -134,11 +138,8 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
             const int j = j0 + 8 * g;
             const uint32_t off = (r < a_rows && j < J) ? (uint32_t)((r * J + j) * 2) : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)&lds[buf][base * 16], 16, (int)off, 0, 0, 0);
-            if constexpr (HILO)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(a2res, (lds_void*)&lds[buf][C::A_BYTES + base * 16],
-                                                         16, (int)off, 0, 0, 0);
         }
-        constexpr int BOFF = C::A_BYTES * (HILO ? 2 : 1);
+        constexpr int BOFF = C::A_BYTES;
         if constexpr (TERN) {
             // row c: 16 bytes (64 codes) per stage, slot c
             const int base = wave * kWave;
@@ -159,14 +160,11 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
         }
     };
 
-    v16f acc[WR][2], acc2[HILO ? WR : 1][2];
+    v16f acc[WR][WC];
 #pragma unroll
     for (int i = 0; i < WR; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            acc[i][j] = v16f{};
-            if constexpr (HILO) acc2[i][j] = v16f{};
-        }
+        for (int j = 0; j < WC; ++j) acc[i][j] = v16f{};
 
     const int h = lane / 32, l32 = lane % 32;
     auto frag = [&](const uint8_t* tile, int row, int g) {
@@ -174,18 +172,18 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
     };
     auto compute = [&](int buf) {
         const uint8_t* at = lds[buf];
-        const uint8_t* bt = lds[buf] + C::A_BYTES * (HILO ? 2 : 1);
-        uint4 bq[2];
+        const uint8_t* bt = lds[buf] + C::A_BYTES;
+        uint4 bq[WC];
         if constexpr (TERN) {
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb)
-                bq[cb] = *reinterpret_cast<const uint4*>(bt + (wc * 64 + cb * 32 + l32) * 16);
+            for (int cb = 0; cb < WC; ++cb)
+                bq[cb] = *reinterpret_cast<const uint4*>(bt + (wc * (32 * WC) + cb * 32 + l32) * 16);
         }
 #pragma unroll
         for (int s = 0; s < kBJ / 16; ++s) {
-            uint4 bf[2];
+            uint4 bf[WC];
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
+            for (int cb = 0; cb < WC; ++cb) {
                 if constexpr (TERN) {
                     const uint32_t w = s == 0 ? bq[cb].x : (s == 1 ? bq[cb].y : (s == 2 ? bq[cb].z : bq[cb].w));
                     const uint32_t d0 = (w >> (4 * h)) & 0x03030303u;      // values 8h .. 8h+3 of the step
@@ -193,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
                     bf[cb] = make_uint4(codes_to_bf16x2<0>(d0), codes_to_bf16x2<2>(d0),
                                         codes_to_bf16x2<0>(d1), codes_to_bf16x2<2>(d1));
                 } else {
-                    bf[cb] = frag(bt, wc * 64 + cb * 32 + l32, 2 * s + h);
+                    bf[cb] = frag(bt, wc * (32 * WC) + cb * 32 + l32, 2 * s + h);
                 }
             }
 #pragma unroll
@@ -201,16 +199,9 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
                 const int row = wr * (32 * WR) + rb * 32 + l32;
                 const uint4 af = frag(at, row, 2 * s + h);
 #pragma unroll
-                for (int cb = 0; cb < 2; ++cb)
+                for (int cb = 0; cb < WC; ++cb)
                     acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(v8bf, af), __builtin_bit_cast(v8bf, bf[cb]), acc[rb][cb], 0, 0, 0);
-                if constexpr (HILO) {
-                    const uint4 af2 = frag(at + C::A_BYTES, row, 2 * s + h);
-#pragma unroll
-                    for (int cb = 0; cb < 2; ++cb)
-                        acc2[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(v8bf, af2), __builtin_bit_cast(v8bf, bf[cb]), acc2[rb][cb], 0, 0, 0);
-                }
             }
         }
     };
@@ -228,26 +219,24 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
 #pragma unroll
     for (int rb = 0; rb < WR; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < WC; ++cb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = r0 + wr * (32 * WR) + rb * 32 + 8 * (e / 4) + 4 * h + e % 4;
-                const int64_t col = c0 + wc * 64 + cb * 32 + l32;
-                float v = acc[rb][cb][e];
-                if constexpr (HILO) v += acc2[rb][cb][e];
-                if (row < R && col < Cn) out[row * Cn + col] = v * scale;
+                const int64_t col = c0 + wc * (32 * WC) + cb * 32 + l32;
+                if (row < R && col < Cn) out[row * Cn + col] = acc[rb][cb][e] * scale;
             }
 }
 
 // ---------------------------------------------------------------------------
-// Operands of dL/dW: p = grad_y[m][n] * d_x[m] transposed to [N][Mp] as
-// bf16 hi and lo, and the codes transposed to [K][Mp] as bf16; columns
-// m >= M are zero (Mp = M rounded up to 64).  One 64 x 64 tile per workgroup.
+// Operands of dL/dW, rows of 2 Mp values (Mp = M rounded up to 64; columns
+// m >= M are zero): a[n] = [hi of p[.][n] | lo of p[.][n]] with
+// p = grad_y[m][n] * d_x[m], and b[k] = [codes[.][k] | codes[.][k]] in bf16.
+// One 64 x 64 tile per workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void prep_grad_kernel(const uint16_t* __restrict__ g,
                                                              const float* __restrict__ d_x, int M,
-                                                             int N, int Mp, uint16_t* __restrict__ hi,
-                                                             uint16_t* __restrict__ lo) {
+                                                             int N, int Mp, uint16_t* __restrict__ a) {
     __shared__ float tile[64][65];  // [m][n]
     const int m0 = (int)blockIdx.x * 64, n0 = (int)blockIdx.y * 64;
     const int t = threadIdx.x;
@@ -280,8 +269,8 @@ __global__ __launch_bounds__(kThreads) void prep_grad_kernel(const uint16_t* __r
         hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
         lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
     }
-    uint4* ho = reinterpret_cast<uint4*>(hi + (int64_t)(n0 + nr) * Mp + m0 + mc);
-    uint4* lo4 = reinterpret_cast<uint4*>(lo + (int64_t)(n0 + nr) * Mp + m0 + mc);
+    uint4* ho = reinterpret_cast<uint4*>(a + (int64_t)(n0 + nr) * 2 * Mp + m0 + mc);
+    uint4* lo4 = reinterpret_cast<uint4*>(a + (int64_t)(n0 + nr) * 2 * Mp + Mp + m0 + mc);
     ho[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
     ho[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
     lo4[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
@@ -289,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void prep_grad_kernel(const uint16_t* __r
 }
 
 __global__ __launch_bounds__(kThreads) void prep_codes_kernel(const int8_t* __restrict__ xq, int M,
-                                                              int K, int Mp, uint16_t* __restrict__ xt) {
+                                                              int K, int Mp, uint16_t* __restrict__ b) {
     __shared__ int tile[64][65];  // [m][k]
     const int m0 = (int)blockIdx.x * 64, k0 = (int)blockIdx.y * 64;
     const int t = threadIdx.x;
@@ -311,9 +300,12 @@ __global__ __launch_bounds__(kThreads) void prep_codes_kernel(const int8_t* __re
         const uint32_t b1 = __float_as_uint((float)tile[mc + 2 * e + 1][kr]) >> 16;
         o[e] = b0 | (b1 << 16);
     }
-    uint4* dst = reinterpret_cast<uint4*>(xt + (int64_t)(k0 + kr) * Mp + m0 + mc);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        uint4* dst = reinterpret_cast<uint4*>(b + (int64_t)(k0 + kr) * 2 * Mp + half * Mp + m0 + mc);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -393,8 +385,8 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ p, i
         p[i] = 0.f;
 }
 
-using CfgIn = BwdCfg<4, true, false>;   // dL/dn: 256 x 128 tiles, 2-bit B
-using CfgW = BwdCfg<2, false, true>;    // dL/dW: 128 x 128 tiles, bf16 B, hi + lo A
+using CfgIn = BwdCfg<2, 2, true>;    // dL/dn: 128 x 128 tiles, 2-bit B
+using CfgW = BwdCfg<2, 2, false>;    // dL/dW: 128 x 128 tiles, bf16 B
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -415,32 +407,31 @@ hipError_t launch_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, 
 hipError_t launch_backward_input(const uint16_t* grad_y, const uint8_t* packed_t, const float* w_scale,
                                  int64_t M, int64_t N, int64_t K, float* grad_n, hipStream_t stream) {
     const dim3 grid((unsigned)((K + CfgIn::BC - 1) / CfgIn::BC), (unsigned)((M + CfgIn::BR - 1) / CfgIn::BR));
-    return launch_kernel((bwd_gemm_kernel<CfgIn, true, false>), grid, dim3(kThreads), 0, stream, grad_y,
-                         (const uint16_t*)nullptr, packed_t, (int)M, (int)K, (int)N, w_scale, grad_n);
+    return launch_kernel((bwd_gemm_kernel<CfgIn, true>), grid, dim3(kThreads), 0, stream, grad_y, packed_t,
+                         (int)M, (int)K, (int)N, w_scale, grad_n);
 }
 
 size_t backward_weight_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t Mp = round_up(M, 64);
-    return (size_t)((2 * N + K) * Mp * 2);
+    return (size_t)((N + K) * 2 * Mp * 2);
 }
 
 hipError_t launch_backward_weight(const uint16_t* grad_y, const int8_t* xq, const float* x_scale,
                                   int64_t M, int64_t N, int64_t K, float* grad_w, void* workspace,
                                   hipStream_t stream) {
     const int64_t Mp = round_up(M, 64);
-    uint16_t* hi = static_cast<uint16_t*>(workspace);
-    uint16_t* lo = hi + N * Mp;
-    uint16_t* xt = lo + N * Mp;
+    uint16_t* a = static_cast<uint16_t*>(workspace);  // [N][2 Mp]
+    uint16_t* b = a + N * 2 * Mp;                       // [K][2 Mp]
     hipError_t e = launch_kernel(prep_grad_kernel, dim3((unsigned)(Mp / 64), (unsigned)(N / 64)), dim3(kThreads),
-                                 0, stream, grad_y, x_scale, (int)M, (int)N, (int)Mp, hi, lo);
+                                 0, stream, grad_y, x_scale, (int)M, (int)N, (int)Mp, a);
     if (e != hipSuccess) return e;
     e = launch_kernel(prep_codes_kernel, dim3((unsigned)(Mp / 64), (unsigned)(K / 64)), dim3(kThreads), 0, stream,
-                      xq, (int)M, (int)K, (int)Mp, xt);
+                      xq, (int)M, (int)K, (int)Mp, b);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((K + CfgW::BC - 1) / CfgW::BC), (unsigned)((N + CfgW::BR - 1) / CfgW::BR));
-    return launch_kernel((bwd_gemm_kernel<CfgW, false, true>), grid, dim3(kThreads), 0, stream,
-                         (const uint16_t*)hi, (const uint16_t*)lo, reinterpret_cast<const uint8_t*>(xt), (int)N,
-                         (int)K, (int)Mp, (const float*)nullptr, grad_w);
+    return launch_kernel((bwd_gemm_kernel<CfgW, false>), grid, dim3(kThreads), 0, stream, (const uint16_t*)a,
+                         reinterpret_cast<const uint8_t*>(b), (int)N, (int)K, (int)(2 * Mp), (const float*)nullptr,
+                         grad_w);
 }
 
 size_t rmsnorm_backward_workspace_bytes(int64_t M, int64_t K) {

@@ -7,7 +7,7 @@ Bars (derived from the arithmetic, written out per test):
   final scaling: |got - want| <= N 2^-24 d_w sum_n |grad_y q| + 2^-23 |want|.
 * grad_w = sum_m grad_y d_x q_x: grad_y * d_x is rounded to float32 and carried
   as bf16 hi + lo (|p - hi - lo| <= 2^-16 |p|), products with the codes are
-  exact, and 2 Mp terms are accumulated in float32:
+  exact, and 2 Mp terms (Mp = M rounded up to 64) are accumulated in float32:
   |got - want| <= (2^-16 + 2^-24 + 2 Mp 2^-24) sum_m |grad_y d_x q_x| + 2^-23 |want|.
 * RMSNorm backward: the same float64 formula, summed in another order and
   rounded to float32: |got - want| <= 2^-22 (|g r grad_n| + |x r^3 dot / K|).
