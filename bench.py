@@ -29,6 +29,11 @@ not Python launch overhead.
   block            the seven BitLinear projections of a Llama-3-8B block at
                    M = 1, 16 and 256 tokens: time per block, packed weight GB/s,
                    int TOPS
+  backward         STE backward of the prefill layer: grad_n and grad_w on the bf16
+                   matrix cores, RMSNorm backward, packed-weight transpose
+  pack             offline weight preparation (absmean scale, ternarise, pack;
+                   with the Hadamard pre-rotation for the H-BitLinear weight):
+                   time per matrix and GB/s of its two passes over W
   cpu_baseline     the CPU oracle on this host running the same decode step, on
                    all cores and on one core
 
@@ -75,6 +80,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--prefill-iters", type=int, default=30)
+    ap.add_argument("--pack-iters", type=int, default=10, help="timed calls per matrix of the pack leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall time budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,7 +89,7 @@ def parse_args():
     ap.add_argument("--block-steps", type=int, default=200, help="timed steps per token count of the block leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES, ten times (HBM counter calibration)")
-    ap.add_argument("--legs", default="decode,prefill,hadamard,block,backward",
+    ap.add_argument("--legs", default="decode,prefill,hadamard,block,backward,pack",
                     help="comma-separated legs to run (the headline needs decode)")
     ap.add_argument("--cpu-one-core-seconds", type=float, default=5.0,
                     help="wall time budget of the one-core CPU-oracle sample")
@@ -475,6 +481,35 @@ def backward_bench(args, dev, bt, torch, synth):
     }
 
 
+def pack_bench(args, dev, bt, torch, synth):
+    """Offline weight preparation (absmean scale, ternarise, pack; and the
+    Hadamard pre-rotation) of the prefill and H-BitLinear weight matrices."""
+    out = []
+    cases = [(synth.workload("prefill")[0], False), (synth.workload("hadamard")[1], True)]
+    for layer, had in cases:
+        N, K = layer.N, layer.K
+        W = torch.from_numpy(layer.weights()).to(dev)
+        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+        w_scale = torch.empty(2, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(bt.pack_weights_workspace_bytes(N, K, had), 16), dtype=torch.uint8,
+                         device=dev)
+        call = lambda: bt.pack_weights(W, had, out=(packed, w_scale), workspace=ws)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        ms, _ = timed(lambda n: [call() for _ in range(n)], args.pack_iters, torch)
+        # The scale needs every weight before the first code: two passes over W
+        # (plus, with the rotation, one write and two reads of the rotated copy).
+        passes = 2 if not had else 4
+        bytes_ = passes * 4 * N * K + N * K // 4
+        out.append({"N": N, "K": K, "hadamard": had, "us": round(ms * 1e3, 1),
+                    "algorithmic_bytes": bytes_,
+                    "GB_s": round(bytes_ / (ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        del W, ws
+    return out
+
+
 class GroupedLayer:
     """Projections sharing one input (q|k|v or gate|up) stacked row-wise, run
     with one bitnet_bitlinear_forward_grouped call per step."""
@@ -612,7 +647,8 @@ def main():
     if "decode" not in legs:
         # Secondary legs only (used for per-kernel counter runs); no headline line.
         for name, fn in (("prefill", prefill_bench), ("hadamard", hadamard_bench),
-                         ("block", block_bench), ("backward", backward_bench)):
+                         ("block", block_bench), ("backward", backward_bench),
+                         ("pack", pack_bench)):
             if name in legs:
                 secondary[name] = fn(args, dev, bt, torch, synth)
                 torch.cuda.empty_cache()
@@ -628,7 +664,8 @@ def main():
 
     if not args.no_secondary:
         for name, fn in (("prefill", prefill_bench), ("hadamard", hadamard_bench),
-                         ("block", block_bench), ("backward", backward_bench)):
+                         ("block", block_bench), ("backward", backward_bench),
+                         ("pack", pack_bench)):
             if name in legs:
                 secondary[name] = fn(args, dev, bt, torch, synth)
                 log(f"{name}: {secondary[name]}")

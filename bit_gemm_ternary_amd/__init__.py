@@ -141,15 +141,29 @@ def pack_weights_workspace_bytes(N: int, K: int, hadamard: bool = False) -> int:
     return int(lib().bitnet_pack_weights_workspace_bytes(N, K, int(bool(hadamard))))
 
 
-def pack_weights(W, hadamard: bool = False):
-    """float32 [N][K] device weights -> (packed uint8 [N][K/4], w_scale float32 [2] = (d_w, s_w))."""
+def pack_weights(W, hadamard: bool = False, out=None, workspace=None):
+    """float32 [N][K] device weights -> (packed uint8 [N][K/4], w_scale float32 [2] = (d_w, s_w)).
+
+    ``out`` may hold preallocated (packed, w_scale), ``workspace`` a uint8 device
+    buffer of at least pack_weights_workspace_bytes(N, K, hadamard) bytes.
+    """
     torch = _torch()
     _require(W, "W", torch.float32, 2)
     N, K = W.shape
-    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
-    w_scale = torch.empty(2, dtype=torch.float32, device=W.device)
-    ws_bytes = pack_weights_workspace_bytes(N, K, hadamard)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=W.device)
+    if out is None:
+        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+        w_scale = torch.empty(2, dtype=torch.float32, device=W.device)
+    else:
+        packed, w_scale = out
+        _require(packed, "packed", torch.uint8, 2)
+        _require(w_scale, "w_scale", torch.float32, 1)
+        if tuple(packed.shape) != (N, K // 4) or w_scale.shape[0] < 2:
+            raise ValueError(f"out must be (uint8 [{N}][{K // 4}], float32 [2])")
+    if workspace is None:
+        ws_bytes = pack_weights_workspace_bytes(N, K, hadamard)
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=W.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1)
     _check(lib().bitnet_pack_weights(_ptr(W), N, K, int(bool(hadamard)), _ptr(packed),
                                      _ptr(w_scale), _ptr(workspace), workspace.numel(),
                                      _stream(W.device)))

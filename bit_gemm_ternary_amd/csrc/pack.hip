@@ -9,7 +9,7 @@
 // Steps (each one launch, all on the caller's stream):
 //   [hadamard] rows <- Walsh-Hadamard transform of the rows (float32);
 //   row_abssum: r[n] = sum_k |w[n][k]| in float64, k ascending (one lane per row);
-//   finalize:   S = sum_n r[n] (n ascending), gamma = S / (N K), s_w, d_w;
+//   finalize:   S = sum_n r[n] (n ascending, one wavefront), gamma = S / (N K), s_w, d_w;
 //   ternarize:  q = clamp(rint(w * s_w), -1, 1); 16 weights -> one 32-bit word.
 // The fixed summation order makes s_w bit-identical to a sequential float64 sum.
 #include "common.hpp"
@@ -18,53 +18,118 @@
 namespace bitnet {
 namespace {
 
-constexpr int kRowsPerWave = 64;
-constexpr int kTileK = 64;
-constexpr int kSumThreads = 256;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef float f4 __attribute__((ext_vector_type(4)));
 
-// Lane l of each wave sums row (wave_row0 + l).  The wave stages 64x64 float
-// tiles through LDS (row stride 65 floats: conflict-free column reads) so the
-// HBM reads stay coalesced while each lane still adds its own row in order.
-__global__ __launch_bounds__(kSumThreads) void row_abssum_kernel(const float* __restrict__ src,
-                                                                  int64_t N, int K,
-                                                                  double* __restrict__ row_sum) {
-    __shared__ float tile[kSumThreads / kWave][kRowsPerWave][kTileK + 1];
-    const int lane = threadIdx.x % kWave;
-    const int w = threadIdx.x / kWave;
-    const int64_t row0 = ((int64_t)blockIdx.x * (kSumThreads / kWave) + w) * kRowsPerWave;
-    if (row0 >= N) return;  // wave-uniform; this kernel has no workgroup barrier
-    float(*T)[kTileK + 1] = tile[w];
-    double acc = 0.0;
-    const int sub_row = lane / 16;  // 4 rows per load instruction
-    const int col4 = (lane % 16) * 4;
-    for (int k0 = 0; k0 < K; k0 += kTileK) {
+constexpr uint32_t kBufferWord3 = 0x00020000u;   // gfx9-family raw buffer descriptor word 3
+constexpr int kSumCols = 64;                     // floats of each row per LDS stage (256 B)
+constexpr int kSumStages = 4;                    // stage buffers: three in flight, one summed
+constexpr int kSumLoads = kSumCols * 4 / 16;     // 1 KiB LDS loads per stage (4 rows each)
+
+// Row sums in float64, k ascending: one wavefront per workgroup, lane l owns
+// row 64 * blockIdx.x + l.  Each stage (64 floats of the 64 rows, 16 KiB) is
+// copied from HBM into LDS by 1 KiB buffer_load ... lds instructions (four
+// 256-byte row segments each, whole memory sectors), three stages in flight
+// while the fourth is summed.  The 16-byte piece p of row r sits at slot
+// p ^ (r & 15) of its segment, so when every lane reads the same piece of its
+// own row, 16 consecutive lanes hit 16 distinct bank groups.  The order of the
+// additions is the row's natural order, whatever the staging.
+__global__ __launch_bounds__(kWave) void row_abssum_kernel(const float* __restrict__ src, int64_t N,
+                                                          int K, double* __restrict__ row_sum) {
+    __shared__ __align__(16) float tile[kSumStages][kWave * kSumCols];
+    const int lane = threadIdx.x;
+    const int64_t row0 = (int64_t)blockIdx.x * kWave;
+    const int rows = (int)min((int64_t)kWave, N - row0);
+    // The resource covers this block's rows only: rows past N read zeros.
+    const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + row0 * K), (short)0, rows * K * (int)sizeof(float), (int)kBufferWord3);
+    const int nk = K / kSumCols;
+    auto issue = [&](int j) {
+        float* dst = tile[j % kSumStages];
 #pragma unroll
-        for (int i = 0; i < kRowsPerWave / 4; ++i) {
-            const int r = 4 * i + sub_row;
-            const int64_t row = row0 + r;
-            float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (row < N) a = *reinterpret_cast<const float4*>(src + row * K + k0 + col4);
-            T[r][col4] = a.x;
-            T[r][col4 + 1] = a.y;
-            T[r][col4 + 2] = a.z;
-            T[r][col4 + 3] = a.w;
+        for (int i = 0; i < kSumLoads; ++i) {
+            const int r = 4 * i + lane / 16;
+            const int piece = (lane % 16) ^ (r & 15);
+            const int off = (r * K + j * kSumCols + 4 * piece) * (int)sizeof(float);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)&dst[i * 4 * kSumCols], 16, off,
+                                                     0, 0, 0);
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-#pragma unroll 8
-        for (int k = 0; k < kTileK; ++k) acc += fabs((double)T[lane][k]);
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
+    double acc = 0.0;
+    auto sum = [&](int j) {
+        const float* T = tile[j % kSumStages] + lane * kSumCols;
+#pragma unroll
+        for (int p = 0; p < kSumCols / 4; ++p) {
+            // (an ext_vector read: with a float4 struct read the compiler adds a
+            // wait for every outstanding LDS load before it)
+            const f4 v = *reinterpret_cast<const f4*>(T + 4 * (p ^ (lane & 15)));
+            acc += fabs((double)v[0]);
+            acc += fabs((double)v[1]);
+            acc += fabs((double)v[2]);
+            acc += fabs((double)v[3]);
+        }
+    };
+    for (int j = 0; j < kSumStages - 1 && j < nk; ++j) issue(j);
+    int j = 0;
+    for (; j + kSumStages - 1 < nk; ++j) {
+        // Buffer (j - 1) % kSumStages was read in the previous iteration: its
+        // reads have returned before the loads of stage j + 3 overwrite it.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(j + kSumStages - 1);
+        // Stage j has landed once at most the three later stages' loads are
+        // outstanding (loads complete in order).
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kSumStages - 1) * kSumLoads) : "memory");
+        sum(j);
     }
-    if (row0 + lane < N) row_sum[row0 + lane] = acc;
+    // The last stages (at most three), nothing more to issue.
+    static_assert(kSumStages == 4, "tail below drains three stages");
+    if (nk - j == 3) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kSumLoads) : "memory");
+        sum(j++);
+    }
+    if (nk - j == 2) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSumLoads) : "memory");
+        sum(j++);
+    }
+    if (nk - j == 1) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        sum(j);
+    }
+    if (lane < rows) row_sum[row0 + lane] = acc;
 }
 
-// One thread: total in row order, then the two float32 scales.
-__global__ void finalize_scale_kernel(const double* __restrict__ row_sum, int64_t N, int64_t K,
-                                      int hadamard, double sqrt_k, float* __restrict__ w_scale) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// One wavefront: S = sum of the row sums in row order, then the two float32
+// scales.  The additions form one dependent chain; the row sums arrive 512 at
+// a time (eight per lane, the next group's loads in flight while this group is
+// added) and are broadcast lane by lane.  Entries past N are read as +0, which
+// leaves a sum of non-negative terms unchanged.
+__global__ __launch_bounds__(kWave) void finalize_scale_kernel(const double* __restrict__ row_sum,
+                                                               int64_t N, int64_t K, int hadamard,
+                                                               double sqrt_k,
+                                                               float* __restrict__ w_scale) {
+    constexpr int G = 8;
+    const int lane = threadIdx.x;
+    double cur[G], nxt[G];
+    auto load = [&](double(&v)[G], int64_t g) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int64_t n = (g * G + i) * kWave + lane;
+            v[i] = n < N ? row_sum[n] : 0.0;
+        }
+    };
+    const int64_t groups = (N + G * kWave - 1) / (G * kWave);
+    load(cur, 0);
     double S = 0.0;
-    for (int64_t n = 0; n < N; ++n) S += row_sum[n];
+    for (int64_t g = 0; g < groups; ++g) {
+        if (g + 1 < groups) load(nxt, g + 1);
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+#pragma unroll
+            for (int l = 0; l < kWave; ++l) S += read_lane(cur[i], l);
+#pragma unroll
+        for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+    }
+    if (lane != 0) return;
     const double gamma = S / ((double)N * (double)K);
     float s_w = 0.f, d_w = 0.f;
     if (gamma != 0.0) {
@@ -125,9 +190,8 @@ hipError_t launch_pack_weights(const float* W, int64_t N, int64_t K, int hadamar
         if (e != hipSuccess) return e;
         src = rot;
     }
-    const int64_t rows_per_block = (kSumThreads / kWave) * kRowsPerWave;
-    hipLaunchKernelGGL(row_abssum_kernel, dim3((unsigned)((N + rows_per_block - 1) / rows_per_block)),
-                       dim3(kSumThreads), 0, stream, src, N, (int)K, row_sum);
+    hipLaunchKernelGGL(row_abssum_kernel, dim3((unsigned)((N + kWave - 1) / kWave)), dim3(kWave), 0,
+                       stream, src, N, (int)K, row_sum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(finalize_scale_kernel, dim3(1), dim3(64), 0, stream, row_sum, N, K,

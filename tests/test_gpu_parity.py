@@ -59,6 +59,7 @@ PACK_CASES = [
     (4096, 11008, False),    # decode down projection (K = 11008)
     (1, 64, False),          # smallest
     (37, 192, False),        # ragged rows, K not a power of two
+    (70, 128, False),        # two row blocks, the second ragged; two K stages
     (300, 4096, True),       # H-BitLinear weights
     (4096, 16384, True),     # H-BitLinear down projection
     (33, 256, True),
