@@ -17,8 +17,11 @@ not Python launch overhead.
                    and the warm number (one weight copy, Infinity-Cache resident)
   roofline         the fused decode kernel alone: algorithmic bytes (packed
                    weights, bf16 activations, codes and outputs) per launch /
-                   average kernel duration, from HIP events that the kernel's
-                   own dispatch stamps (hipExtLaunchKernelGGL), on its stream
+                   average launch duration, each projection launched back to
+                   back from HIP graphs over its own >= 1 GiB weight rotation,
+                   timed by HIP events on the graphs' stream (per_launch also
+                   gives the eager duration of one launch on an idle GPU, from
+                   events stamped by the kernel's own dispatch)
   prefill          W1.58A8 prefill M=2048, K=4096, N=14336: int8 TOPS of the
                    matrix-core GEMM against the dense int8 peak, and against that
                    peak scaled to the engine clock measured during the kernel
@@ -321,15 +324,36 @@ def decode_bench(args, dev, bt, torch, synth):
             bt.set_kernel_events(*pairs[s][i])
             L.forward(bt, r)
     torch.cuda.synchronize()
-    per_layer_us = [float(np.mean([hev.elapsed_ms(*pairs[s][i]) for s in range(n_instr)])) * 1e3
-                    for i in range(len(layers))]
+    isolated_us = [float(np.mean([hev.elapsed_ms(*pairs[s][i]) for s in range(n_instr)])) * 1e3
+                   for i in range(len(layers))]
     hev.close()
+
+    # Average launch duration in a stream of launches: each projection alone,
+    # back to back from HIP graphs over its own rotation of >= 1 GiB of weight
+    # copies, between two HIP events on the stream the graphs run on.  (The
+    # eager, kernel-stamped durations above also count each launch's ramp-up on
+    # an idle GPU.)
+    per_layer_us = []
+    for L in layers:
+        extra = max(0, math.ceil(ROTATE_BYTES / L.weight_bytes) - len(L.packed))
+        own = L.packed + [L.packed[0].clone() for _ in range(extra)]
+
+        def one(r, L=L, own=own):
+            bt.bitlinear_forward(L.x, own[r], L.w_scale, None, 1e-5, out=L.y, codes=L.codes)
+
+        run = graph_runner(one, len(own), args.eager, torch)
+        launches = max(1, min(3 * args.steps, 6000) // len(own)) * len(own)
+        ms, _ = timed(run, launches, torch)
+        per_layer_us.append(ms * 1e3)
+        del run, own, one
+        torch.cuda.empty_cache()
     kernel_bytes = sum(L.kernel_bytes for L in layers)
     kernel_us = sum(per_layer_us)
     per_layer = [{"K": L.layer.K, "N": L.layer.N, "packed_bytes": L.weight_bytes,
                   "kernel_bytes": L.kernel_bytes, "avg_us": round(us, 3),
-                  "GB_s": round(L.kernel_bytes / us / 1e3, 1)}
-                 for L, us in zip(layers, per_layer_us)]
+                  "GB_s": round(L.kernel_bytes / us / 1e3, 1),
+                  "isolated_us": round(iso, 3)}
+                 for L, us, iso in zip(layers, per_layer_us, isolated_us)]
     return {
         "step_bytes": step_bytes, "copies": copies, "ms_per_step": ms_per_step,
         "wall_s": wall_s, "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -373,6 +397,21 @@ def prefill_bench(args, dev, bt, torch, synth):
     quant_us = time_launches(quant, args.prefill_iters, bt)
     gemm_us = time_launches(gemm, args.prefill_iters, bt)
     tops = 2.0 * M * N * K / (gemm_us * 1e-6) / 1e12
+    # Context only: the vendor int8 GEMM (hipBLASLt, through torch._int_mm) on
+    # the same shape with the weights stored unpacked, one int8 code each
+    # (ternary values drawn at random), int32 output and no dequantisation.
+    lib_us = None
+    try:
+        gen = torch.Generator(device="cpu").manual_seed(11)
+        wq = torch.randint(-1, 2, (N, K), generator=gen, dtype=torch.int8).to(dev)
+        ref = lambda: torch._int_mm(xq, wq.t())
+        for _ in range(3):
+            ref()
+        lib_ms, _ = timed(lambda n: [ref() for _ in range(n)], args.prefill_iters, torch)
+        lib_us = lib_ms * 1e3
+        del wq
+    except (RuntimeError, AttributeError) as ex:  # not every torch build exposes it
+        log(f"prefill: no library int8 GEMM reference ({ex})")
     quant_bytes = M * K * 2 + M * K + 8 * M
     counters = summary_data(GEMM_SUMMARY, GEMM_SOURCES)
     # Engine clock of this run: the kernel's cycles per CU (counter summary)
@@ -389,6 +428,10 @@ def prefill_bench(args, dev, bt, torch, synth):
                      round(tops / (INT8_PEAK_TOPS * clock / PEAK_CLOCK_GHZ), 4)},
         "quant_us": round(quant_us, 2), "quant_GB_s": round(quant_bytes / quant_us / 1e3, 1),
         "step_ms": round((gemm_us + quant_us) / 1e3, 4),
+        "library_int8_gemm_reference": None if lib_us is None else {
+            "what": "hipBLASLt int8 GEMM via torch._int_mm, unpacked int8 ternary weights, "
+                    "int32 output, no dequantisation (context, not this path)",
+            "us": round(lib_us, 2), "TOPS": round(2.0 * M * N * K / (lib_us * 1e-6) / 1e12, 1)},
     }
 
 
