@@ -43,7 +43,10 @@
 // (RMSNorm + absmax int8, the arithmetic of quant_act.hip) from the bf16 input,
 // which every workgroup reads from L2, and shares the codes through LDS.  The
 // activation (and gain) loads are issued first and the first weight batch right
-// after them, so the weight stream is in flight through that prologue.
+// after them, so the weight stream is in flight through that prologue.  The
+// prologue is straight-line code between its two barriers (vectors past K are
+// zeros): the float64 scale d_x and the code sums are formed alongside the codes,
+// so after the second barrier a wave only reads its codes and starts on rows.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -167,9 +170,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     constexpr int LV = log2_of(NV);
     constexpr int XV = (CH * 512 + NT - 1) / NT;  // 8-value bf16 vectors per thread per token
     static_assert(NV <= kWave && (NV & (NV - 1)) == 0, "values per batch: a power of 2, <= 64");
+    static_assert(XV * NT == CH * 512, "the fused prologue's vectors tile the code array exactly");
     __shared__ __align__(16) int8_t codes[MT][FUSED ? CH * 4096 : 16];
     __shared__ float red_f[MT][NW];
     __shared__ double red_d[MT][NW];
+    __shared__ int red_i[MT][NW];
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
@@ -253,22 +258,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
         };
 
         // 2. Per-token absmax of x*gain and sum of x^2 (four independent f64
-        // chains per thread): one workgroup reduction.
+        // chains per thread): one workgroup reduction.  Vectors past K were
+        // loaded as zeros and leave both unchanged, so no guard is needed.
 #pragma unroll
         for (int tok = 0; tok < MT; ++tok) {
             float amax = 0.f;
             double ss[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
             for (int i = 0; i < XV; ++i) {
-                if (t + NT * i < nvec) {
-                    float u[8];
-                    values(tok, i, u, false);
+                float u[8];
+                values(tok, i, u, false);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) ss[e % 4] = __fma_rn((double)u[e], (double)u[e], ss[e % 4]);
-                    values(tok, i, u, true);
+                for (int e = 0; e < 8; ++e) ss[e % 4] = __fma_rn((double)u[e], (double)u[e], ss[e % 4]);
+                values(tok, i, u, true);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(u[e]));
-                }
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(u[e]));
             }
             amax = wave_max_dpp(amax);
             const double s = wave_sum_dpp((ss[0] + ss[1]) + (ss[2] + ss[3]));
@@ -284,40 +288,53 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
         // two's complement, in the low byte of the float's bit pattern.  The
         // clamp to [-128, 127] never acts: |x * gain| <= amax, so
         // |x * gain * rn(127 / amax)| < 127.5.
-        float tok_amax[MT];
+        // The per-token float64 factor d_x = amax * rstd / 127 is computed here
+        // too, by every wave, in the same straight-line code as the codes, so
+        // its long-latency divisions and square root overlap the code work
+        // instead of following the second barrier.  Vectors past K give zero
+        // codes, written to LDS past the token's K codes (the array holds
+        // XV * NT * 8 >= CH * 4096 codes) and never read.  Each thread also sums
+        // its codes; the wave totals go to LDS with the codes.
 #pragma unroll
         for (int tok = 0; tok < MT; ++tok) {
             float amax = red_f[tok][0];
 #pragma unroll
             for (int wv = 1; wv < NW; ++wv) amax = fmaxf(amax, red_f[tok][wv]);
-            tok_amax[tok] = amax;
+            double ss = red_d[tok][0];
+#pragma unroll
+            for (int wv = 1; wv < NW; ++wv) ss += red_d[tok][wv];
+            const double rstd = 1.0 / sqrt(ss / (double)K + (double)a.eps);
+            tok_scale[tok] = amax < kTinyAbsmax ? 0.f : (float)(((double)amax * rstd) / 127.0);
             const float scale = amax < kTinyAbsmax ? 0.f : 127.0f / amax;
+            int part = 0;
 #pragma unroll
             for (int i = 0; i < XV; ++i) {
                 const int v = t + NT * i;
-                if (v < nvec) {
-                    float u[8];
-                    values(tok, i, u, true);
-                    uint32_t b[8];
+                float u[8];
+                values(tok, i, u, true);
+                uint32_t b[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        b[e] = __float_as_uint(__fadd_rn(__fmul_rn(u[e], scale), 12582912.0f));
-                    const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
-                                                              __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u),
-                                                              0x05040100u);
-                    const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
-                                                              __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
-                                                              0x05040100u);
-                    *reinterpret_cast<uint2*>(&codes[tok][8 * v]) = make_uint2(lo, hi);
-                }
+                for (int e = 0; e < 8; ++e)
+                    b[e] = __float_as_uint(__fadd_rn(__fmul_rn(u[e], scale), 12582912.0f));
+                const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                          __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u),
+                                                          0x05040100u);
+                const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                                          __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
+                                                          0x05040100u);
+                *reinterpret_cast<uint2*>(&codes[tok][8 * v]) = make_uint2(lo, hi);
+                part = dot4(lo, 0x01010101u, part);
+                part = dot4(hi, 0x01010101u, part);
             }
+            part = wave_sum_dpp(part);
+            if (lane == 0) red_i[tok][wave] = part;
         }
         __syncthreads();
 
-        // 4. Codes of my chunks into registers; each wave sums them itself.
+        // 4. Codes of my chunks into registers (chunks past K read as zeros);
+        // the token's code sum from the wave totals.
 #pragma unroll
         for (int tok = 0; tok < MT; ++tok) {
-            int part = 0;
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 const int c = lane + kWave * j;
@@ -329,19 +346,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
                     xv[tok][j][4 * q + 1] = v.y;
                     xv[tok][j][4 * q + 2] = v.z;
                     xv[tok][j][4 * q + 3] = v.w;
-                    part = dot4(v.x, 0x01010101u, part);
-                    part = dot4(v.y, 0x01010101u, part);
-                    part = dot4(v.z, 0x01010101u, part);
-                    part = dot4(v.w, 0x01010101u, part);
                 }
             }
-            tok_sum[tok] = wave_sum_dpp(part);
-            double ss = red_d[tok][0];
+            int sum = red_i[tok][0];
 #pragma unroll
-            for (int wv = 1; wv < NW; ++wv) ss += red_d[tok][wv];
-            const double rstd = 1.0 / sqrt(ss / (double)K + (double)a.eps);
-            tok_scale[tok] = tok_amax[tok] < kTinyAbsmax ? 0.f
-                                                         : (float)(((double)tok_amax[tok] * rstd) / 127.0);
+            for (int wv = 1; wv < NW; ++wv) sum += red_i[tok][wv];
+            tok_sum[tok] = sum;
         }
         if (blockIdx.x == 0) {
             for (int tok = 0; tok < MT; ++tok)
