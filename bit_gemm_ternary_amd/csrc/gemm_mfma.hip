@@ -517,6 +517,7 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_q
 // workgroups per CU).
 using CfgLarge = GemmCfg<448, 128, 7, 2, 1>;   // 14 waves, wave tile 64 x 64, 120 KiB LDS
 using CfgMid = GemmCfg<256, 128, 4, 2, 1>;     // 8 waves, wave tile 64 x 64, 96 KiB LDS
+using CfgWide = GemmCfg<256, 64, 4, 1, 1>;     // 4 waves, wave tile 64 x 64, 64 KiB LDS
 using CfgTiny = GemmCfg<64, 64, 2, 2, 2>;      // 4 waves, wave tile 32 x 32, 40 KiB LDS
 // The same tiles with 6-bit activations (FP4 x FP6 matrix core).
 using CfgLargeF6 = GemmCfg<448, 128, 7, 2, 1, 2, true>;
@@ -545,6 +546,10 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_
         return launch_cfg<CfgLarge>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     if (tiles_of<CfgMid>(M, N) >= kCus)
         return launch_cfg<CfgMid>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    // Few tokens, many weight rows (a grouped gate|up at 256 tokens): 256-row
+    // tiles read each activation stage once per 256 rows instead of 64.
+    if (tiles_of<CfgWide>(M, N) >= kCus)
+        return launch_cfg<CfgWide>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     return launch_cfg<CfgTiny>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
 }
 

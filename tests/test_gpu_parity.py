@@ -180,6 +180,7 @@ FORWARD_FULL_CASES = [
     (2000, 4100, 64),    # 256 x 128 tiles
     (999, 4100, 320),    # 64 x 64 tiles
     (200, 900, 4160),    # 64 x 64 tiles, long K
+    (250, 16400, 192),   # 256 x 64 tiles (few tokens, many rows)
     (9, 4100, 576),      # skinny, K split over eight waves
     (16, 9000, 1088),    # skinny, K split over four waves
 ]
@@ -205,6 +206,7 @@ FORWARD_SAMPLED_CASES = [
     (256, 14336, 4096, False),    # Llama-3-8B block gate/up at M = 256
     (16, 14336, 4096, False),     # ... at M = 16
     (256, 4096, 14336, False),    # down projection at M = 256
+    (256, 28672, 4096, False),    # grouped gate|up at M = 256 (256 x 64 tiles)
 ]
 
 
