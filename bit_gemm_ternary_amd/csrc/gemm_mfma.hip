@@ -393,44 +393,56 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     }
 }
 
-// Skinny contraction (M <= 16 tokens).  One workgroup owns a 16-row block of
-// weights; its K range is split over the workgroup's KW waves (stage kt goes to
-// wave kt % KW, so at any time the waves read adjacent bytes of each row).  A
-// lane's MFMA fragments are contiguous in memory (16 bytes of packed weights,
-// 64 bytes of activations per stage, in the K assignment described above), so
-// they are loaded straight into registers with no LDS staging; the next
-// stage's loads are issued before the current stage's MFMAs.  The KW partial
-// accumulators are summed through LDS by wave 0, which runs the epilogue.
-template <int KW>
+// Skinny contraction (M <= 16 tokens).  One workgroup owns R blocks of 16
+// weight rows; its K range is split over the workgroup's KW waves (stage kt
+// goes to wave kt % KW, so at any time the waves read adjacent bytes of each
+// row).  A lane's MFMA fragments are contiguous in memory (16 bytes of packed
+// weights per row block, 64 bytes of activations per stage, in the K assignment
+// described above), so they are loaded straight into registers with no LDS
+// staging; the next stage's loads are issued before the current stage's MFMAs.
+// A wave loads each activation fragment once and uses it for all R row blocks,
+// so the activations read from L2 shrink to 64 / R bytes per 16 bytes of packed
+// weights.  The KW partial accumulators are summed through LDS, row block r by
+// wave r % KW, which runs its epilogue.
+template <int KW, int R>
 __global__ __launch_bounds__(KW * kWave) void skinny_kernel(
     const int8_t* __restrict__ X, const uint8_t* __restrict__ P, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_qsum, const RowScales scales, int M, int N, int K,
     int vec_store, float* __restrict__ y, int32_t* __restrict__ acc_out) {
-    __shared__ v4i part[KW][kWave];
+    __shared__ v4i part[KW][R][kWave];
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int fr = lane % 16, fg = lane / 16;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * R;
     const int row_bytes = K / 4;
-    const bool w_ok = n0 + fr < N;
+    bool w_ok[R];
+    const uint8_t* wp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t n = n0 + 16 * r + fr;
+        w_ok[r] = n < N;
+        // Rows past N or M read row 0 (always valid) and are masked to zero.
+        wp[r] = P + (w_ok[r] ? n * row_bytes : 0) + 16 * fg;
+    }
     const bool x_ok = fr < M;
-    // Rows past N or M read row 0 (always valid) and are masked to zero.
-    const uint8_t* wp = P + (w_ok ? (n0 + fr) * row_bytes : 0) + 16 * fg;
     const int8_t* xp = X + (x_ok ? (int64_t)fr * K : 0) + 64 * fg;
     const int nk = (K + kBK - 1) / kBK;
 
     struct Frag {
-        v4u w;
+        v4u w[R];
         v4i x[4];
     };
     auto load = [&](int kt, Frag& f) {
         const int k0 = kt * kBK;
         // K is a multiple of 64, so a lane group's 64 K-values are all in range or all out.
         const bool in_k = kt < nk && k0 + 64 * fg < K;
-        if (in_k && w_ok) {
-            f.w = *reinterpret_cast<const v4u*>(wp + k0 / 4);
-        } else {
-            f.w = v4u{0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (in_k && w_ok[r]) {
+                f.w[r] = *reinterpret_cast<const v4u*>(wp[r] + k0 / 4);
+            } else {
+                f.w[r] = v4u{0, 0, 0, 0};
+            }
         }
         if (in_k && x_ok) {
             const v4i* src = reinterpret_cast<const v4i*>(xp + k0);
@@ -442,59 +454,66 @@ __global__ __launch_bounds__(KW * kWave) void skinny_kernel(
         }
     };
 
-    v4i acc = v4i{0, 0, 0, 0};
+    v4i acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = v4i{0, 0, 0, 0};
     Frag cur, nxt;
     load(wave, cur);
     for (int kt = wave; kt < nk; kt += KW) {
         load(kt + KW, nxt);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_codes(cur.w[ks]), cur.x[ks], acc, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_codes(cur.w[r][ks]), cur.x[ks], acc[r],
+                                                               0, 0, 0);
         cur = nxt;
     }
-    part[wave][lane] = acc;
+#pragma unroll
+    for (int r = 0; r < R; ++r) part[wave][r][lane] = acc[r];
     __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int w = 1; w < KW; ++w) acc += part[w][lane];
 
-    // D[n][m] sits in lane m + 16 * (n / 4), element n % 4.
     const int m = fr;
-    const int64_t nb = n0 + 4 * fg;
-    if (m >= M || nb >= N) return;
-    const int32_t qs = x_qsum[m];
-    const float sx = x_scale[m];
+    const int32_t qs = m < M ? x_qsum[m] : 0;
+    const float sx = m < M ? x_scale[m] : 0.f;
     const float dw0 = scales.w_scale[0];
-    if (vec_store && nb + 3 < N) {
-        const v4i a = acc - v4i{qs, qs, qs, qs};
-        if (acc_out != nullptr) *reinterpret_cast<v4i*>(&acc_out[m * N + nb]) = a;
-        float4 v;
-        v.x = ((float)a[0] * sx) * scales.of(nb, dw0);
-        v.y = ((float)a[1] * sx) * scales.of(nb + 1, dw0);
-        v.z = ((float)a[2] * sx) * scales.of(nb + 2, dw0);
-        v.w = ((float)a[3] * sx) * scales.of(nb + 3, dw0);
-        *reinterpret_cast<float4*>(&y[m * N + nb]) = v;
-    } else {
+    for (int r = wave; r < R; r += KW) {   // wave-uniform
+        v4i a = part[0][r][lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (nb + e < N) {
-                const int a = acc[e] - qs;
-                if (acc_out != nullptr) acc_out[m * N + nb + e] = a;
-                y[m * N + nb + e] = ((float)a * sx) * scales.of(nb + e, dw0);
+        for (int w = 1; w < KW; ++w) a += part[w][r][lane];
+        // D[n][m] sits in lane m + 16 * (n / 4), element n % 4.
+        const int64_t nb = n0 + 16 * r + 4 * fg;
+        if (m >= M || nb >= N) continue;
+        a -= v4i{qs, qs, qs, qs};
+        if (vec_store && nb + 3 < N) {
+            if (acc_out != nullptr) *reinterpret_cast<v4i*>(&acc_out[m * N + nb]) = a;
+            float4 v;
+            v.x = ((float)a[0] * sx) * scales.of(nb, dw0);
+            v.y = ((float)a[1] * sx) * scales.of(nb + 1, dw0);
+            v.z = ((float)a[2] * sx) * scales.of(nb + 2, dw0);
+            v.w = ((float)a[3] * sx) * scales.of(nb + 3, dw0);
+            *reinterpret_cast<float4*>(&y[m * N + nb]) = v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (nb + e < N) {
+                    if (acc_out != nullptr) acc_out[m * N + nb + e] = a[e];
+                    y[m * N + nb + e] = ((float)a[e] * sx) * scales.of(nb + e, dw0);
+                }
             }
         }
     }
 }
 
-template <int KW>
+template <int KW, int R>
 hipError_t launch_skinny(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                          const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                          int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     const int vec_store = (N % 4 == 0) && ((uintptr_t)y % 16 == 0) &&
                           (acc == nullptr || (uintptr_t)acc % 16 == 0);
-    return launch_kernel(skinny_kernel<KW>, dim3((unsigned)((N + 15) / 16)), dim3(KW * kWave), 0,
-                         stream, xq, packed, x_scale, x_qsum, scales, (int)M, (int)N, (int)K,
-                         vec_store, y, acc);
+    return launch_kernel(skinny_kernel<KW, R>, dim3((unsigned)((N + 16 * R - 1) / (16 * R))),
+                         dim3(KW * kWave), 0, stream, xq, packed, x_scale, x_qsum, scales, (int)M,
+                         (int)N, (int)K, vec_store, y, acc);
 }
 
 template <class C>
@@ -533,10 +552,17 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_
                        int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     if (M <= 16) {
-        // About 2048 waves in flight: split K eight ways when there are few row blocks.
-        if ((N + 15) / 16 < 2 * kCus)
-            return launch_skinny<8>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
-        return launch_skinny<4>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+        // Row blocks per workgroup grow with N (fewer activation re-reads from
+        // L2) while the grid keeps >= ~1300 waves; K is split eight ways, or
+        // four for the largest N.  Measured at M = 16 on 7B / 8B projection
+        // shapes (N 1024 ... 28672, K 4096 ... 14336).
+        if (N >= 24576)
+            return launch_skinny<4, 4>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+        if (N >= 10240)
+            return launch_skinny<8, 4>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+        if (N >= 5120)
+            return launch_skinny<8, 2>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+        return launch_skinny<8, 1>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     }
     // The largest tile that still gives every CU enough work: two rounds of the
     // large tile, one of the mid tile.  With fewer tiles the stage loop is bound

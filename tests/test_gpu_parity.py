@@ -181,8 +181,11 @@ FORWARD_FULL_CASES = [
     (999, 4100, 320),    # 64 x 64 tiles
     (200, 900, 4160),    # 64 x 64 tiles, long K
     (250, 16400, 192),   # 256 x 64 tiles (few tokens, many rows)
-    (9, 4100, 576),      # skinny, K split over eight waves
-    (16, 9000, 1088),    # skinny, K split over four waves
+    (9, 4100, 576),      # skinny, one row block per workgroup, K split over eight waves
+    (16, 9000, 1088),    # skinny, two row blocks
+    (7, 6000, 4096),     # skinny, two row blocks, ragged N
+    (12, 12300, 320),    # skinny, four row blocks, K split over eight waves
+    (16, 30000, 192),    # skinny, four row blocks, K split over four waves
 ]
 
 
