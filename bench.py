@@ -508,6 +508,27 @@ def backward_bench(args, dev, bt, torch, synth):
     flops = 2.0 * M * N * K
     w_us = w_ms * 1e3
     rb_bytes = M * K * (2 + 4 + 4) + 8 * M
+    # Context only: the vendor bf16 GEMM (hipBLASLt through torch.matmul) on the
+    # two contraction shapes, with the ternary weights and the activation codes
+    # stored unpacked as bf16 and one bf16 pass for dL/dW.
+    lib = None
+    try:
+        gen = torch.Generator(device="cpu").manual_seed(13)
+        wb = torch.randint(-1, 2, (N, K), generator=gen).to(torch.bfloat16).to(dev)
+        xb = xq.to(torch.bfloat16)
+        gyt = gy.t().contiguous()
+        ref_n = lambda: torch.matmul(gy, wb)
+        ref_w = lambda: torch.matmul(gyt, xb)
+        for _ in range(2):
+            ref_n(); ref_w()
+        n_ms, _ = timed(lambda n: [ref_n() for _ in range(n)], iters, torch)
+        w2_ms, _ = timed(lambda n: [ref_w() for _ in range(n)], iters, torch)
+        lib = {"what": "hipBLASLt bf16 GEMM via torch.matmul, unpacked bf16 operands, one bf16 pass "
+                       "(context, not this path)",
+               "grad_n_us": round(n_ms * 1e3, 2), "grad_w_us": round(w2_ms * 1e3, 2)}
+        del wb, xb, gyt
+    except RuntimeError as ex:
+        log(f"backward: no library bf16 GEMM reference ({ex})")
     return {
         "workload": f"STE backward of the prefill layer: grad_y bf16 [{M}][{N}], ternary W [{N}][{K}], "
                     "int8 codes of x; grad_n, grad_w, RMSNorm backward",
@@ -521,6 +542,7 @@ def backward_bench(args, dev, bt, torch, synth):
         "rmsnorm_bwd_us": round(rb_us, 2),
         "rmsnorm_bwd_GB_s": round(rb_bytes / rb_us / 1e3, 1),
         "transpose_packed_us": round(tr_us, 2),
+        "library_bf16_gemm_reference": lib,
     }
 
 

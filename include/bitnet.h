@@ -62,7 +62,7 @@ typedef enum {
     BITNET_OK = 0,
     BITNET_ERR_NULL = 1,         /* a required pointer is NULL */
     BITNET_ERR_SHAPE = 2,        /* M, N or K out of range, or K % 64 != 0 */
-    BITNET_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement
+    BITNET_ERR_UNSUPPORTED = 3,  /* valid request the library does not implement
                                     (Hadamard with K not a power of two in [256, 32768]) */
     BITNET_ERR_ALIGN = 4,        /* a device pointer is not aligned as documented */
     BITNET_ERR_WORKSPACE = 5,    /* a workspace is missing or too small */
