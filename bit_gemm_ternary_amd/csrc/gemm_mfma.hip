@@ -63,10 +63,15 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int BN_, int BM_, int WN_, int WM_, int OCC_, int S_ = 2, bool F6_ = false>
+template <int BN_, int BM_, int WN_, int WM_, int OCC_, int S_ = 2, bool F6_ = false, int KS_ = 1>
 struct GemmCfg {
     static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
     static constexpr int S = S_;                    // LDS stage buffers (S - 1 stages in flight)
+    // K groups: KS sets of WN x WM waves share the tile; group g takes the
+    // stages g, g + KS, ... with its own stage buffers, and the groups' sums
+    // are added through LDS at the end.  With small tiles a single group runs
+    // one wave per SIMD, whose stage work (LDS reads, unpacking, dependent
+    // MFMAs) has nothing to overlap with; a second group fills that gap.
     // Activation format: int8 codes, or 6-bit E3M2 codes (F6: 192 bytes per
     // row per stage, padded to 208 in LDS so 16-byte reads of 16 consecutive
     // rows fall in distinct bank groups).
@@ -75,24 +80,28 @@ struct GemmCfg {
     static constexpr int X_ROW_SLOTS = X_ROW / 16;
     static constexpr int STEPS = F6 ? 4 : 8;         // MFMA K steps per stage (64 or 32 K each)
     static constexpr int OCC = OCC_;                // workgroups per CU the tile is sized for
-    static constexpr int NT = WN * WM * kWave;
+    static constexpr int KS = KS_;
+    static constexpr int NTG = WN * WM * kWave;      // threads per K group
+    static constexpr int NT = NTG * KS;
     static constexpr int TN = BN / WN, TM = BM / WM;
     static constexpr int FN = TN / 32, FM = TM / 32;
     static constexpr int X_STAGE = BM * X_ROW;       // bytes
     static constexpr int W_STAGE = BN * (kBK / 4);   // bytes
     static constexpr int X_SLOTS = BM * X_ROW_SLOTS; // 16-byte slots per stage
     static constexpr int W_SLOTS = BN * 4;
-    static constexpr int XL = (X_SLOTS + NT - 1) / NT;
-    static constexpr int WL = (W_SLOTS + NT - 1) / NT;
+    static constexpr int XL = (X_SLOTS + NTG - 1) / NTG;
+    static constexpr int WL = (W_SLOTS + NTG - 1) / NTG;
     static constexpr int ROW_F = TN + 4;             // epilogue staging row stride (floats)
     static_assert((ROW_F / 4) % 2 == 1, "odd number of 16-byte units per staging row");
     static_assert(WN * WM * 16 * ROW_F * 4 <= S * (X_STAGE + W_STAGE), "epilogue staging fits");
     static_assert(TN % 32 == 0 && TM % 32 == 0, "wave tile must be whole MFMA blocks");
     static_assert(X_SLOTS % kWave == 0 && W_SLOTS % kWave == 0, "whole waves per load");
-    static_assert(S * (X_STAGE + W_STAGE) <= 160 * 1024, "LDS");
+    static_assert(KS * S * (X_STAGE + W_STAGE) <= 160 * 1024, "LDS");
+    static_assert(KS == 1 || WN * WM * kWave * FN * FM * 16 * 4 <= S * (X_STAGE + W_STAGE),
+                  "a K group's partial sums fit its stage buffers");
     // With more than one stage in flight the stage barrier counts outstanding
     // loads, so every wave must issue the same number per stage.
-    static_assert(S == 2 || (X_SLOTS % NT == 0 && W_SLOTS % NT == 0), "uniform loads per wave");
+    static_assert(S == 2 || (X_SLOTS % NTG == 0 && W_SLOTS % NTG == 0), "uniform loads per wave");
     static_assert(S >= 2 && (S - 2) * (XL + WL) <= 63, "vmcnt range");
     static_assert(NT <= 1024, "workgroup size");
 };
@@ -146,12 +155,15 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     const int8_t* __restrict__ X, const uint8_t* __restrict__ P, const float* __restrict__ x_scale,
     const int32_t* __restrict__ x_qsum, const RowScales scales, int M, int N, int K,
     int vec_store, float* __restrict__ y, int32_t* __restrict__ acc_out) {
-    __shared__ __align__(16) int8_t lds[C::S][C::X_STAGE + C::W_STAGE];
+    __shared__ __align__(16) int8_t lds_all[C::KS][C::S][C::X_STAGE + C::W_STAGE];
 
     const int t = threadIdx.x;
     const int lane = t % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform, in an SGPR
+    const int wave_all = __builtin_amdgcn_readfirstlane(t / kWave);   // wave-uniform, in an SGPR
+    const int kg = wave_all / (C::WN * C::WM);                       // K group
+    const int wave = wave_all % (C::WN * C::WM);                     // wave within the group
     const int wn = wave % C::WN, wm = wave / C::WN;
+    auto& lds = lds_all[kg];
 
     // Launch index -> tile: contiguous ranges per XCD, grouped order.
     const int tiles_n = (N + C::BN - 1) / C::BN;
@@ -183,33 +195,36 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     // of this wave moves 1 KiB; lane l of the wave fills the 16-byte slot
     // base + l, so the global address each lane reads is chosen to realise the
     // swizzled layout.
+    // When `live` is false the load reads out of range (zeros, no memory
+    // traffic) but is still issued, so a stage's loads are straight-line code
+    // and every wave counts the same number of them.
     constexpr int kLoads = C::XL + C::WL;
-    auto issue_one = [&](int buf, int k0, int idx) {
+    auto issue_one = [&](int buf, int k0, int idx, bool live) {
         if (idx < C::XL) {
-            const int base = idx * C::NT + wave * kWave;   // wave-uniform
-            if (base < C::X_SLOTS) {
+            const int base = idx * C::NTG + wave * kWave;   // wave-uniform
+            if (C::X_SLOTS % C::NTG == 0 || base < C::X_SLOTS) {
                 const int p = base + lane;
                 uint32_t off;
                 if constexpr (C::F6) {
                     // 12 data slots and one padding slot per row, in order.
                     const int r = p / C::X_ROW_SLOTS, s = p % C::X_ROW_SLOTS;
                     const int b = k0 / 4 * 3 + 16 * s;             // byte in the token's row
-                    off = (s < 12 && b < x_row_bytes) ? (uint32_t)(r * x_row_bytes + b) : kOutOfRange;
+                    off = (live && s < 12 && b < x_row_bytes) ? (uint32_t)(r * x_row_bytes + b) : kOutOfRange;
                 } else {
                     const int r = p >> 4, s = (p & 15) ^ (r & 15);
                     const int k = k0 + 16 * s;
-                    off = k < K ? (uint32_t)(r * K + k) : kOutOfRange;
+                    off = (live && k < K) ? (uint32_t)(r * K + k) : kOutOfRange;
                 }
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void*)&lds[buf][base * 16], 16,
                                                          (int)off, 0, 0, 0);
             }
         } else {
-            const int base = (idx - C::XL) * C::NT + wave * kWave;
-            if (base < C::W_SLOTS) {
+            const int base = (idx - C::XL) * C::NTG + wave * kWave;
+            if (C::W_SLOTS % C::NTG == 0 || base < C::W_SLOTS) {
                 const int p = base + lane;
                 const int r = p >> 2, f = (p & 3) ^ w_swizzle(r);
                 const int k = k0 + 64 * f;
-                const uint32_t off = k < K ? (uint32_t)(r * row_bytes + k / 4) : kOutOfRange;
+                const uint32_t off = (live && k < K) ? (uint32_t)(r * row_bytes + k / 4) : kOutOfRange;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     wres, (lds_void*)&lds[buf][C::X_STAGE + base * 16], 16, (int)off, 0, 0, 0);
             }
@@ -254,11 +269,9 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
             if (st == C::STEPS / 4) __builtin_amdgcn_s_setprio(2);
             if (st == C::STEPS / 2) __builtin_amdgcn_s_setprio(1);
             if (st == 3 * C::STEPS / 4) __builtin_amdgcn_s_setprio(0);
-            if (has_next) {
 #pragma unroll
-                for (int idx = 0; idx < kLoads; ++idx)
-                    if (idx * (C::STEPS / 2) / kLoads == st) issue_one(nbuf, next_k0, idx);
-            }
+            for (int idx = 0; idx < kLoads; ++idx)
+                if (idx * (C::STEPS / 2) / kLoads == st) issue_one(nbuf, next_k0, idx, has_next);
             if constexpr (C::F6) {
                 // K step st of lane half fh: packed words 8 fh + 2 st and 8 fh + 2 st + 1
                 // (64 consecutive K values per step over the two halves) against the
@@ -299,24 +312,63 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
         }
     };
 
+    // Group kg takes the stages kg, kg + KS, ...; every group runs the same
+    // number of iterations (a group past the end computes nothing and loads
+    // zeros) so the workgroup barriers line up.
     const int nk = (K + kBK - 1) / kBK;
+    const int nkl = (nk + C::KS - 1) / C::KS;
+    auto stage_k0 = [&](int local) { return (local * C::KS + kg) * kBK; };
+    auto stage_live = [&](int local) { return local * C::KS + kg < nk; };
 #pragma unroll
     for (int sp = 0; sp < C::S - 1; ++sp) {
-        if (sp < nk) {
+        if (sp < nkl) {
 #pragma unroll
-            for (int idx = 0; idx < kLoads; ++idx) issue_one(sp, sp * kBK, idx);
+            for (int idx = 0; idx < kLoads; ++idx) issue_one(sp, stage_k0(sp), idx, stage_live(sp));
         }
     }
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = 0; kt < nkl; ++kt) {
         // Stage kt has landed once at most the loads of the stages issued after
         // it are outstanding; every wave has finished reading buffer
         // (kt - 1) % S, which the loads of stage kt + S - 1 overwrite.
-        if (kt + C::S - 2 < nk)
+        if (kt + C::S - 2 < nkl)
             stage_barrier<(C::S - 2) * kLoads>();
         else
             stage_barrier<0>();
+        // (A stage past K holds zeros and adds nothing; its loads are still
+        // issued, so the outstanding-load counts stay uniform.)
         const int ahead = kt + C::S - 1;
-        compute(kt % C::S, ahead < nk, ahead % C::S, ahead * kBK);
+        compute(kt % C::S, stage_live(ahead), ahead % C::S, stage_k0(ahead));
+    }
+
+    // The last stages' out-of-range loads may still be writing (zeros) into
+    // LDS; every wave waits for its own before the stage buffers are reused.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (C::KS > 1) {
+        // Groups 1.. add their sums into group 0 through LDS (each group's
+        // stage buffers hold its partials), group by group.
+        __syncthreads();
+        using Elem = typename std::conditional<C::F6, float, int>::type;
+        Elem* part = reinterpret_cast<Elem*>(&lds_all[kg][0][0]) + wave * (kWave * C::FN * C::FM * 16);
+        if (kg > 0) {
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) part[((i * C::FM + j) * 16 + e) * kWave + lane] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (kg > 0) return;   // wave-uniform; no workgroup barrier follows
+#pragma unroll
+        for (int g = 1; g < C::KS; ++g) {
+            const Elem* src = reinterpret_cast<const Elem*>(&lds_all[g][0][0]) + wave * (kWave * C::FN * C::FM * 16);
+#pragma unroll
+            for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) acc[i][j][e] += src[((i * C::FM + j) * 16 + e) * kWave + lane];
+        }
     }
 
     // Epilogue.  D[n][m] of a 32x32 block sits in lane m + 32 * ((n / 4) % 2),
@@ -326,8 +378,8 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     // LDS region (row stride TN + 4 floats keeps the 16-byte writes conflict
     // free) and writes them back as whole row segments of TN floats.
     const float dw0 = scales.w_scale[0];
-    __syncthreads();   // every wave is done with the stage buffers
-    float* stage = reinterpret_cast<float*>(&lds[0][0]) + wave * 16 * C::ROW_F;
+    if constexpr (C::KS == 1) __syncthreads();   // every wave is done with the stage buffers
+    float* stage = reinterpret_cast<float*>(&lds_all[0][0][0]) + wave * 16 * C::ROW_F;
     constexpr int PPR = C::TN / 4;              // 16-byte pieces per row segment
     constexpr int RPI = kWave / PPR;            // row segments per store instruction
     static_assert(RPI >= 1 && 16 % RPI == 0, "row segments per store");
@@ -533,17 +585,48 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_q
 }
 
 // Tile configurations (weight rows x tokens, waves along N x along M,
-// workgroups per CU).
-using CfgLarge = GemmCfg<448, 128, 7, 2, 1>;   // 14 waves, wave tile 64 x 64, 120 KiB LDS
-using CfgMid = GemmCfg<256, 128, 4, 2, 1>;     // 8 waves, wave tile 64 x 64, 96 KiB LDS
-using CfgWide = GemmCfg<256, 64, 4, 1, 1>;     // 4 waves, wave tile 64 x 64, 64 KiB LDS
-using CfgTiny = GemmCfg<64, 64, 2, 2, 2>;      // 4 waves, wave tile 32 x 32, 40 KiB LDS
-// The same tiles with 6-bit activations (FP4 x FP6 matrix core).
-using CfgLargeF6 = GemmCfg<448, 128, 7, 2, 1, 2, true>;
-using CfgMidF6 = GemmCfg<256, 128, 4, 2, 1, 2, true>;
-using CfgTinyF6 = GemmCfg<64, 64, 2, 2, 2, 2, true>;
+// workgroups per CU, stage buffers, 6-bit activations, K groups).
+template <bool F6>
+struct Tiles {
+    using Large = GemmCfg<448, 128, 7, 2, 1, 2, F6>;        // 14 waves, wave tile 64 x 64
+    using Mid = GemmCfg<256, 128, 4, 2, 1, 2, F6>;          // 8 waves, wave tile 64 x 64
+    using Wide = GemmCfg<256, 64, 4, 1, 1, 2, F6>;          // 4 waves, wave tile 64 x 64
+    using TallK3 = GemmCfg<128, 64, 2, 2, 1, 2, F6, 3>;     // 3 K groups of 4 waves (64 x 32)
+    using Tiny = GemmCfg<64, 64, 2, 2, 2, 2, F6>;           // 4 waves, wave tile 32 x 32
+    using TinyK2 = GemmCfg<64, 64, 2, 2, 2, 2, F6, 2>;      // 2 K groups of 4 waves
+    using TinyK4 = GemmCfg<64, 64, 2, 2, 1, 2, F6, 4>;      // 4 K groups of 4 waves
+};
 
 constexpr int64_t kCus = 256;
+
+// The largest tile that still gives every CU enough work: two rounds of the
+// large tile, one of the mid tile, one of the wide tile (few tokens, many
+// weight rows: each activation stage is read once per 256 rows).  Below that
+// the 64 x 64 tile, whose waves (one 32 x 32 block each) have little to overlap
+// a stage's LDS reads and dependent MFMAs with: K groups add waves that work
+// on other stages of the same tile, the more the longer K.  Measured on the
+// prefill, H-BitLinear (M 512) and Llama-block (M 256) shapes.
+template <bool F6>
+hipError_t launch_tiled(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
+                        const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
+                        int64_t K, float* y, int32_t* acc, hipStream_t stream) {
+    using T = Tiles<F6>;
+    if (tiles_of<typename T::Large>(M, N) >= 2 * kCus)
+        return launch_cfg<typename T::Large>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    if (tiles_of<typename T::Mid>(M, N) >= kCus)
+        return launch_cfg<typename T::Mid>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    if (tiles_of<typename T::Wide>(M, N) >= kCus)
+        return launch_cfg<typename T::Wide>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    const int64_t tiles = tiles_of<typename T::Tiny>(M, N);
+    const int64_t stages = (K + kBK - 1) / kBK;
+    if (stages >= 48 && tiles >= 2 * kCus)
+        return launch_cfg<typename T::TallK3>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    if (stages >= 48)
+        return launch_cfg<typename T::TinyK4>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    if (tiles >= 384 && stages <= 32)
+        return launch_cfg<typename T::Tiny>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    return launch_cfg<typename T::TinyK2>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+}
 
 }  // namespace
 
@@ -564,31 +647,15 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_
             return launch_skinny<8, 2>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
         return launch_skinny<8, 1>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     }
-    // The largest tile that still gives every CU enough work: two rounds of the
-    // large tile, one of the mid tile.  With fewer tiles the stage loop is bound
-    // by load latency, not by the matrix cores, and more, smaller tiles keep
-    // more loads in flight (measured on the prefill and Llama-block shapes).
-    if (tiles_of<CfgLarge>(M, N) >= 2 * kCus)
-        return launch_cfg<CfgLarge>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
-    if (tiles_of<CfgMid>(M, N) >= kCus)
-        return launch_cfg<CfgMid>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
-    // Few tokens, many weight rows (a grouped gate|up at 256 tokens): 256-row
-    // tiles read each activation stage once per 256 rows instead of 64.
-    if (tiles_of<CfgWide>(M, N) >= kCus)
-        return launch_cfg<CfgWide>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
-    return launch_cfg<CfgTiny>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    return launch_tiled<false>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
 }
 
 hipError_t launch_gemm_f6(const uint8_t* xq6, const float* x_scale, const int32_t* x_qsum,
                           const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                           int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    const int8_t* x = reinterpret_cast<const int8_t*>(xq6);
-    if (tiles_of<CfgLargeF6>(M, N) >= 2 * kCus)
-        return launch_cfg<CfgLargeF6>(x, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
-    if (tiles_of<CfgMidF6>(M, N) >= kCus)
-        return launch_cfg<CfgMidF6>(x, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
-    return launch_cfg<CfgTinyF6>(x, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    return launch_tiled<true>(reinterpret_cast<const int8_t*>(xq6), x_scale, x_qsum, packed, scales, M,
+                              N, K, y, acc, stream);
 }
 
 }  // namespace bitnet

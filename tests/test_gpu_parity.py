@@ -179,8 +179,9 @@ FORWARD_FULL_CASES = [
     (2100, 14000, 192),  # 448 x 128 tiles
     (2000, 4100, 64),    # 256 x 128 tiles
     (999, 4100, 320),    # 64 x 64 tiles
-    (200, 900, 4160),    # 64 x 64 tiles, long K
+    (200, 900, 4160),    # 64 x 64 tiles in two K groups (17 stages: one group runs past K)
     (250, 16400, 192),   # 256 x 64 tiles (few tokens, many rows)
+    (100, 333, 12352),   # 64 x 64 tiles in four K groups (49 stages)
     (9, 4100, 576),      # skinny, one row block per workgroup, K split over eight waves
     (16, 9000, 1088),    # skinny, two row blocks
     (7, 6000, 4096),     # skinny, two row blocks, ragged N
@@ -210,6 +211,7 @@ FORWARD_SAMPLED_CASES = [
     (16, 14336, 4096, False),     # ... at M = 16
     (256, 4096, 14336, False),    # down projection at M = 256
     (256, 28672, 4096, False),    # grouped gate|up at M = 256 (256 x 64 tiles)
+    (1000, 2100, 12352, False),   # 128 x 64 tiles in three K groups, ragged M, N and K
 ]
 
 
@@ -429,6 +431,7 @@ F6_FORWARD_CASES = [
     (2100, 14000, 256),   # 448 x 128 tiles
     (2000, 4100, 192),    # 256 x 128 tiles, K not a multiple of the 256-deep stage
     (512, 4096, 64),
+    (100, 333, 12352),    # 64 x 64 tiles in four K groups
 ]
 
 
@@ -451,10 +454,11 @@ def test_linear_forward_f6(orc, dev, M, N, K):
     assert_close_rel(host(y), want_y)
 
 
-def test_h_bitlinear_f6_matches_int8_path(orc, dev):
-    """Full H-BitLinear at the benchmark shape: the f6 path gives the int8 path's
+@pytest.mark.parametrize("K", [4096, 16384])
+def test_h_bitlinear_f6_matches_int8_path(orc, dev, K):
+    """Full H-BitLinear at the benchmark shapes: the f6 path gives the int8 path's
     accumulators and outputs bit for bit, and both match the oracle on samples."""
-    M, N, K = 512, 4096, 4096
+    M, N = 512, 4096
     W = synth.weights(N, K, 1600)
     x_bits = _activation(M, K, 1601, dist="student_t")
     x = bf16_to_dev(x_bits, dev)
