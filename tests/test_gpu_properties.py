@@ -8,16 +8,18 @@
   different choices must give identical int32 accumulators.
 * Properties: power-of-two scaling of a token leaves its codes unchanged;
   permuting weight rows permutes the outputs; zero and single-spike tokens;
-  random small shapes (hypothesis) against the oracle; a rejected call leaves
-  its outputs untouched.
+  random shapes (hypothesis) against the oracle, small ones through the fused
+  path and larger ones through every tiling of the int8 and FP4 x FP6
+  contractions; a rejected call leaves its outputs untouched.
 """
 import ctypes
 
 import numpy as np
 import pytest
-from hypothesis import HealthCheck, given, settings, strategies as st
+from hypothesis import HealthCheck, assume, given, settings, strategies as st
 
 import bit_gemm_ternary_amd as bt
+import f6_layout  # host encoder of the 6-bit activation layout
 from bit_gemm_ternary_amd import synth
 
 torch = pytest.importorskip("torch")
@@ -238,6 +240,34 @@ def test_random_small_shapes_match_the_oracle(orc, dev, M, N, k64, seed):
         y, acc = bt.linear_forward(q, dx, qs, packed, ws, return_acc=True)
     np.testing.assert_array_equal(host(packed), want_packed)
     np.testing.assert_array_equal(host(q), wq)
+    np.testing.assert_array_equal(host(acc), want_acc)
+    got = host(y).astype(np.float64)
+    assert np.all(np.abs(got - want_y) <= 1e-5 * np.abs(want_y))
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(M=st.integers(5, 700), N=st.integers(1, 4000), k64=st.integers(1, 260), f6=st.booleans(),
+       seed=st.integers(0, 10 ** 6))
+def test_random_tiled_shapes_match_the_oracle(orc, dev, M, N, k64, f6, seed):
+    # The tiled paths at random shapes: skinny (M <= 16), the 64 x 64 tiles in
+    # one, two or four K groups, 128 x 64 tiles in three, the 256-row tiles;
+    # ragged M, N and K (K need not fill the last 256-deep stage).
+    K = 64 * k64
+    assume(M * N * K <= 2_500_000_000)
+    rng = np.random.default_rng(seed)
+    W = synth.weights(N, K, seed=seed)
+    packed, d_w, _, _ = orc.pack_weights(W)
+    lo, hi = (-8, 8) if f6 else (-127, 128)
+    codes = rng.integers(lo, hi, (M, K)).astype(np.int8)
+    d_x = rng.uniform(1e-3, 1e-2, M).astype(np.float32)
+    qsum = codes.astype(np.int64).sum(axis=1).astype(np.int32)
+    want_acc, want_y = orc.linear_forward(codes, d_x, packed, d_w, K)
+    args = (to_dev(d_x, dev), to_dev(qsum, dev), to_dev(packed, dev),
+            to_dev(np.array([d_w, 0], np.float32), dev))
+    if f6:
+        y, acc = bt.linear_forward_f6(to_dev(f6_layout.encode(codes), dev), *args, return_acc=True)
+    else:
+        y, acc = bt.linear_forward(to_dev(codes, dev), *args, return_acc=True)
     np.testing.assert_array_equal(host(acc), want_acc)
     got = host(y).astype(np.float64)
     assert np.all(np.abs(got - want_y) <= 1e-5 * np.abs(want_y))
