@@ -99,35 +99,50 @@ __global__ __launch_bounds__(kWave) void row_abssum_kernel(const float* __restri
 }
 
 // One wavefront: S = sum of the row sums in row order, then the two float32
-// scales.  The additions form one dependent chain; the row sums arrive 512 at
-// a time (eight per lane, the next group's loads in flight while this group is
-// added) and are broadcast lane by lane.  Entries past N are read as +0, which
-// leaves a sum of non-negative terms unchanged.
+// scales.  The additions form one dependent chain, run by lane 0 from LDS
+// (reads issued ahead of the adds, so the chain waits only on the float64 add
+// latency); meanwhile the whole wave loads the next 2048 row sums into
+// registers and stores them to the other LDS buffer after the chain.
+constexpr int kScaleChunk = 2048;   // row sums per LDS buffer (16 KiB)
+
 __global__ __launch_bounds__(kWave) void finalize_scale_kernel(const double* __restrict__ row_sum,
                                                                int64_t N, int64_t K, int hadamard,
                                                                double sqrt_k,
                                                                float* __restrict__ w_scale) {
-    constexpr int G = 8;
+    constexpr int PER_LANE = kScaleChunk / kWave;
+    __shared__ double buf[2][kScaleChunk];
     const int lane = threadIdx.x;
-    double cur[G], nxt[G];
-    auto load = [&](double(&v)[G], int64_t g) {
+    double nxt[PER_LANE];
+    auto load = [&](int64_t c0) {
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const int64_t n = (g * G + i) * kWave + lane;
-            v[i] = n < N ? row_sum[n] : 0.0;
+        for (int j = 0; j < PER_LANE; ++j) {
+            const int64_t n = c0 + lane + kWave * j;
+            nxt[j] = n < N ? row_sum[n] : 0.0;
         }
     };
-    const int64_t groups = (N + G * kWave - 1) / (G * kWave);
-    load(cur, 0);
+    auto store = [&](int b) {
+#pragma unroll
+        for (int j = 0; j < PER_LANE; ++j) buf[b][lane + kWave * j] = nxt[j];
+    };
+    load(0);
+    store(0);
+    __syncthreads();
     double S = 0.0;
-    for (int64_t g = 0; g < groups; ++g) {
-        if (g + 1 < groups) load(nxt, g + 1);
+    for (int64_t c0 = 0; c0 < N; c0 += kScaleChunk) {
+        const int b = (int)((c0 / kScaleChunk) & 1);
+        const bool more = c0 + kScaleChunk < N;
+        if (more) load(c0 + kScaleChunk);
+        if (lane == 0) {
+            const int cnt = (int)min((int64_t)kScaleChunk, N - c0);
+            int i = 0;
+            for (; i + 16 <= cnt; i += 16) {
 #pragma unroll
-        for (int i = 0; i < G; ++i)
-#pragma unroll
-            for (int l = 0; l < kWave; ++l) S += read_lane(cur[i], l);
-#pragma unroll
-        for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+                for (int e = 0; e < 16; ++e) S += buf[b][i + e];
+            }
+            for (; i < cnt; ++i) S += buf[b][i];
+        }
+        if (more) store(b ^ 1);
+        __syncthreads();
     }
     if (lane != 0) return;
     const double gamma = S / ((double)N * (double)K);
