@@ -42,11 +42,13 @@
 // Fused variant: each workgroup first quantises the (<= 4) tokens itself
 // (RMSNorm + absmax int8, the arithmetic of quant_act.hip) from the bf16 input,
 // which every workgroup reads from L2, and shares the codes through LDS.  The
-// activation (and gain) loads are issued first and the first weight batch right
-// after them, so the weight stream is in flight through that prologue.  The
-// prologue is straight-line code between its two barriers (vectors past K are
-// zeros): the float64 scale d_x and the code sums are formed alongside the codes,
-// so after the second barrier a wave only reads its codes and starts on rows.
+// activation (and gain) loads are issued first, then the first rows of each
+// wave's batch, and the rest of the batch once the token is reduced, so the
+// weight stream is in flight through that prologue without the token queueing
+// behind the whole batch.  The prologue is straight-line code between its two
+// barriers (vectors past K are zeros): the float64 scale d_x and the code sums
+// are formed alongside the codes, so after the second barrier a wave only
+// reads its codes and starts on rows.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -188,13 +190,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     auto has_row = [&](int i) { return (int64_t)g + (int64_t)i * W < N; };
     const float dw0 = a.scales.w_scale[0];              // before any store (see RowScales::of)
 
-    // Weight loads of rows i0 .. i0 + RB - 1 of this wave (zeros past the last).
-    auto load = [&](uint4 (&w)[RB][CH], int i0) {
+    // Weight loads of rows i0 + rb0 .. i0 + rb1 - 1 of this wave's batch
+    // starting at row i0 (zeros past the last row).
+    auto load_rows = [&](uint4 (&w)[RB][CH], int i0, int rb0, int rb1) {
         const int64_t r0 = has_row(i0) ? (int64_t)g + (int64_t)i0 * W : 0;
         const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(a.packed + r0 * row_bytes), (short)0, kMaxRecords, (int)kBufferWord3);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+            if (rb < rb0 || rb >= rb1) continue;   // compile-time after unrolling
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 const int c = lane + kWave * j;
@@ -205,6 +209,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
             }
         }
     };
+    auto load = [&](uint4 (&w)[RB][CH], int i0) { load_rows(w, i0, 0, RB); };
+    // Fused single batch: rows issued before the token is reduced.  The rest
+    // follow once it is, so a wave's own token does not queue behind its
+    // whole batch (measured: up to 13% per launch on the 7B / 8B shapes).
+    constexpr int kEarlyRows = RB >= 4 ? 2 : 1;
 
     uint32_t xv[MT][CH][16];  // codes of my chunks: chunk c covers x[64c .. 64c+63]
     int tok_sum[MT];
@@ -241,8 +250,12 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
                 gv[i][6] = __uint_as_float(g1.z); gv[i][7] = __uint_as_float(g1.w);
             }
         }
-        load(w0, 0);
-        if constexpr (MULTI) load(w1, RB);
+        if constexpr (MULTI) {
+            load(w0, 0);
+            load(w1, RB);
+        } else {
+            load_rows(w0, 0, 0, kEarlyRows);
+        }
 
         auto values = [&](int tok, int i, float (&u)[8], bool with_gain) {
             const uint32_t ws[4] = {raw[tok][i].x, raw[tok][i].y, raw[tok][i].z, raw[tok][i].w};
@@ -281,6 +294,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
                 red_d[tok][wave] = s;
             }
         }
+        if constexpr (!MULTI) load_rows(w0, 0, kEarlyRows, RB);
         __syncthreads();
 
         // 3. Codes into LDS.  For |v| <= 127.00002, v + 1.5 * 2^23 rounds v to
