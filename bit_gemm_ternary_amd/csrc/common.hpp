@@ -82,4 +82,21 @@ __device__ __forceinline__ int round_clamp(float v, float lo, float hi) {
 // Tokens whose absmax is below this quantise to all-zero codes.
 constexpr float kTinyAbsmax = 0x1p-120f;
 
+// Per-token dequantisation factor d_x = amax * rstd * inv_denom, with
+// rstd = 1 / sqrt(ss * inv_k + eps) and ss the float64 sum of x^2 over the
+// token (inv_k = 1 / K; inv_denom = 1 / 127 for int8 codes, 1 / (7 sqrt K) for
+// the Hadamard int4 codes).  The reciprocal square root is the hardware
+// float64 estimate refined by one Newton step, and the result is rounded once
+// to float32: a few float32 ulps from the correctly rounded float64 chain
+// (two divisions and a square root) at a fraction of its latency.  No code
+// depends on d_x; it only scales outputs.  Zero for an all-zero token.
+__device__ __forceinline__ float token_scale(float amax, double ss, double inv_k, float eps,
+                                             double inv_denom) {
+    if (amax < kTinyAbsmax) return 0.f;
+    const double v = ss * inv_k + (double)eps;
+    double r = __builtin_amdgcn_rsq(v);
+    r = r * (1.5 - (0.5 * v) * r * r);
+    return (float)(((double)amax * r) * inv_denom);
+}
+
 }  // namespace bitnet

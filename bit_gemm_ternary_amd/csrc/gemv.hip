@@ -221,6 +221,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     uint4 w0[RB][CH], w1[RB][CH];
 
     if constexpr (FUSED) {
+        const double inv_k = 1.0 / (double)K;
         // 1. Activation (and gain) loads, then the first weight batch, which
         // stays in flight through the prologue.
         const int nvec = K / 8;
@@ -302,10 +303,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
         // two's complement, in the low byte of the float's bit pattern.  The
         // clamp to [-128, 127] never acts: |x * gain| <= amax, so
         // |x * gain * rn(127 / amax)| < 127.5.
-        // The per-token float64 factor d_x = amax * rstd / 127 is computed here
-        // too, by every wave, in the same straight-line code as the codes, so
-        // its long-latency divisions and square root overlap the code work
-        // instead of following the second barrier.  Vectors past K give zero
+        // The per-token factor d_x = amax * rstd / 127 is computed here too, by
+        // every wave, in the same straight-line code as the codes, so its
+        // latency overlaps the code work instead of following the second
+        // barrier.  Vectors past K give zero
         // codes, written to LDS past the token's K codes (the array holds
         // XV * NT * 8 >= CH * 4096 codes) and never read.  Each thread also sums
         // its codes; the wave totals go to LDS with the codes.
@@ -317,8 +318,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
             double ss = red_d[tok][0];
 #pragma unroll
             for (int wv = 1; wv < NW; ++wv) ss += red_d[tok][wv];
-            const double rstd = 1.0 / sqrt(ss / (double)K + (double)a.eps);
-            tok_scale[tok] = amax < kTinyAbsmax ? 0.f : (float)(((double)amax * rstd) / 127.0);
+            tok_scale[tok] = token_scale(amax, ss, inv_k, a.eps, 1.0 / 127.0);
             const float scale = amax < kTinyAbsmax ? 0.f : 127.0f / amax;
             int part = 0;
 #pragma unroll

@@ -234,8 +234,7 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
             sum_sq += red_d[w];
             qsum += red_i[w];
         }
-        const double rstd = 1.0 / sqrt(sum_sq / (double)K + (double)eps);
-        x_scale[m] = zero ? 0.f : (float)(((double)amax * rstd) / (7.0 * sqrt_k));
+        x_scale[m] = zero ? 0.f : token_scale(amax, sum_sq, 1.0 / (double)K, eps, 1.0 / (7.0 * sqrt_k));
         x_qsum[m] = qsum;
     }
 }
