@@ -90,6 +90,13 @@ constexpr float kTinyAbsmax = 0x1p-120f;
 // to float32: a few float32 ulps from the correctly rounded float64 chain
 // (two divisions and a square root) at a fraction of its latency.  No code
 // depends on d_x; it only scales outputs.  Zero for an all-zero token.
+// 1 / K for token_scale: the hardware float32 reciprocal (within an ulp or so),
+// one instruction instead of a float64 division; every kernel that forms d_x
+// for the int8 codes uses this same value.
+__device__ __forceinline__ double inv_count(int K) {
+    return (double)__builtin_amdgcn_rcpf((float)K);
+}
+
 __device__ __forceinline__ float token_scale(float amax, double ss, double inv_k, float eps,
                                              double inv_denom) {
     if (amax < kTinyAbsmax) return 0.f;

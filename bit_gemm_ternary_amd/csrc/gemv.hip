@@ -221,7 +221,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     uint4 w0[RB][CH], w1[RB][CH];
 
     if constexpr (FUSED) {
-        const double inv_k = 1.0 / (double)K;
+        const double inv_k = inv_count(K);
         // 1. Activation (and gain) loads, then the first weight batch, which
         // stays in flight through the prologue.
         const int nvec = K / 8;

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
             sum_sq += red_d[w];
             qsum += red_i[w];
         }
-        x_scale[m] = zero ? 0.f : token_scale(amax, sum_sq, 1.0 / (double)K, eps, 1.0 / 127.0);
+        x_scale[m] = zero ? 0.f : token_scale(amax, sum_sq, inv_count(K), eps, 1.0 / 127.0);
         x_qsum[m] = qsum;
     }
 }
