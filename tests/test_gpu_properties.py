@@ -60,7 +60,7 @@ def tokens_on(dev, M, K, seed, dist="normal"):
 # Determinism.
 # ---------------------------------------------------------------------------
 
-def _runs_identical(fn, n=10):
+def _runs_identical(fn, n=20):
     first = [host(t) for t in fn()]
     for _ in range(n - 1):
         cur = [host(t) for t in fn()]
@@ -271,3 +271,54 @@ def test_random_tiled_shapes_match_the_oracle(orc, dev, M, N, k64, f6, seed):
     np.testing.assert_array_equal(host(acc), want_acc)
     got = host(y).astype(np.float64)
     assert np.all(np.abs(got - want_y) <= 1e-5 * np.abs(want_y))
+
+
+# ---------------------------------------------------------------------------
+# The layer against the dense computation it replaces (smoke checks of the
+# method, not parity: ternary weights cost ~0.5 relative error by themselves).
+# ---------------------------------------------------------------------------
+
+def _dense(W, bits, eps=1e-5):
+    """RMSNorm(x) @ W^T in float64."""
+    x = synth.bf16_to_float(bits).astype(np.float64)
+    n = x / np.sqrt((x * x).mean(axis=1, keepdims=True) + eps)
+    return n @ W.astype(np.float64).T
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def test_bitlinear_tracks_the_dense_layer(dev):
+    M, K, N = 64, 4096, 1024
+    W = synth.weights(N, K, seed=870)
+    bits = synth.activations(M, K, 871, 872)
+    packed, ws = bt.pack_weights(to_dev(W, dev))
+    y = host(bt.bitlinear_forward(bf16_to_dev(bits, dev), packed, ws)).astype(np.float64)
+    ref = _dense(W, bits)
+    cos = float((y * ref).sum() / np.linalg.norm(y) / np.linalg.norm(ref))
+    assert 0.85 <= cos <= 0.92, cos
+    assert 0.45 <= _rel(y, ref) <= 0.56
+
+
+def test_hadamard_lowers_the_int4_error_on_heavy_tails(orc, dev):
+    # Student-t (3 degrees of freedom) tokens: int4 codes of the raw token lose
+    # more than int4 codes of its Hadamard transform (the H-BitLinear premise).
+    M, K, N = 64, 4096, 1024
+    W = synth.weights(N, K, seed=873)
+    bits = synth.activations(M, K, 874, 875, dist="student_t")
+    ref = _dense(W, bits)
+    # H path on the GPU
+    packed, ws = bt.pack_weights(to_dev(W, dev), hadamard=True)
+    q, dx, qs = bt.hadamard_quant_act(bf16_to_dev(bits, dev))
+    y_h = host(bt.linear_forward(q, dx, qs, packed, ws)).astype(np.float64)
+    # int4 codes without the transform, on the CPU, from the oracle's ternary weights
+    _, d_w, _, qw = orc.pack_weights(W)
+    x = synth.bf16_to_float(bits).astype(np.float64)
+    a = np.abs(x).max(axis=1, keepdims=True)
+    codes = np.clip(np.rint(x * (7.0 / a)), -8, 7)
+    rstd = 1.0 / np.sqrt((x * x).mean(axis=1, keepdims=True) + 1e-5)
+    y_plain = (codes @ qw.astype(np.float64).T) * (a * rstd / 7.0) * float(d_w)
+    e_h, e_plain = _rel(y_h, ref), _rel(y_plain, ref)
+    assert e_h < e_plain - 0.05, (e_h, e_plain)
+    assert 0.45 <= e_h <= 0.60, e_h
