@@ -331,8 +331,12 @@ int bitnet_linear_backward_input(const uint16_t* grad_y, const uint8_t* packed_t
                       fn);
 }
 
+// dL/dW contracts over the tokens with operand rows of 2 M bf16 values; up to
+// 2^21 tokens a 128-row tile of them spans at most 2^30 bytes.
+constexpr int64_t kMaxBackwardWeightRows = int64_t(1) << 21;
+
 size_t bitnet_linear_backward_weight_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    if (M < 1 || M > kMaxRows || N < 64 || N > kMaxK || N % 64 != 0 || K < kMinK || K > kMaxK ||
+    if (M < 1 || M > kMaxBackwardWeightRows || N < 64 || N > kMaxK || N % 64 != 0 || K < kMinK || K > kMaxK ||
         K % 64 != 0)
         return 0;
     return bitnet::backward_weight_workspace_bytes(M, N, K);
@@ -343,7 +347,8 @@ int bitnet_linear_backward_weight(const uint16_t* grad_y, const int8_t* xq, cons
                                   size_t workspace_bytes, void* stream) {
     DisarmEvents disarm;
     const char* fn = "bitnet_linear_backward_weight";
-    if (M < 0 || M > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
+    if (M < 0 || M > kMaxBackwardWeightRows)
+        return fail(BITNET_ERR_SHAPE, "%s: M=%lld out of range [0, 2^21]", fn, (long long)M);
     int s = check_backward_nk(N, K, fn);
     if (s != BITNET_OK) return s;
     if (!grad_w) return fail(BITNET_ERR_NULL, "%s: grad_w must not be NULL", fn);

@@ -15,17 +15,18 @@
 // staged into LDS by the buffer-load-to-LDS path.  For dL/dn, B is the packed
 // ternary matrix transposed once to [K][N/4] (pack once, like the forward):
 // its tile stays 2-bit in LDS and each lane turns 8 codes into 8 bf16 values
-// in {-1, 0, 1} with two byte permutes per pair (the codes index a four-entry
-// table of bf16 bytes), so the products grad_y * q are exact and only the
-// float32 accumulation rounds.  For dL/dW, p = grad_y * d_x is carried as a
-// bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi), |p - hi - lo| <= 2^-16 |p|)
-// and the activation codes (exact in bf16) are repeated: the operands are
-// A = [hi | lo] ([N][2 Mp]) and B = [codes | codes] ([K][2 Mp]), transposed so
-// that the token index m runs along the rows, and the same kernel sums the
-// 2 Mp products.  Tiles are 128 x 128 with four waves of 64 x 64: small enough
-// for two workgroups per CU, which measured faster than one workgroup with
-// larger tiles (less operand reuse, but the second workgroup hides the LDS and
-// barrier latencies).
+// in {-1, 0, 1} with byte permutes (the codes index a table of bf16 bytes),
+// so the products grad_y * q are exact and only the float32 accumulation
+// rounds.  That conversion is vector-ALU work per 32 x 32 block of B, shared
+// by the WR blocks of A a wave multiplies it with, so dL/dn uses tall wave
+// tiles (128 x 64) and two K groups to keep two waves per SIMD.  For dL/dW,
+// p = grad_y * d_x is carried as a bf16 pair hi + lo (hi = bf16(p),
+// lo = bf16(p - hi), |p - hi - lo| <= 2^-16 |p|) and the activation codes
+// (exact in bf16) are repeated: the operands are A = [hi | lo] ([N][2 Mp]) and
+// B = [codes | codes] ([K][2 Mp]), transposed so that the token index m runs
+// along the rows, and the same kernel sums the 2 Mp products; with both tiles
+// bf16 it is bound by LDS bandwidth and capacity, and 64 x 64 wave tiles with
+// two workgroups per CU measured best.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,12 +35,14 @@ namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // offset past every buffer here: loads 0
 constexpr int kBJ = 64;                          // reduction values per LDS stage
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;                         // XCDs on MI355X, each with its own L2
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {  // finite inputs
     const uint32_t u = __float_as_uint(f);
@@ -80,43 +83,88 @@ __global__ __launch_bounds__(kThreads) void transpose_packed_kernel(const uint8_
 // 2 x 2 waves, a wave WR x WC blocks of 32 x 32; K steps of 16 inside LDS
 // stages of 64.  TERN: B is 2-bit codes q+1 ([C][J/4] bytes), else bf16.
 // ---------------------------------------------------------------------------
-template <int WR_, int WC_, bool TERN>
+template <int WR_, int WC_, int GR_, int GC_, int KS_, bool TERN_, int NS_, int GROUP_>
 struct BwdCfg {
+    static constexpr bool TERN = TERN_;                      // B is 2-bit codes, else bf16
     static constexpr int WR = WR_, WC = WC_;                 // 32 x 32 blocks per wave
-    static constexpr int BR = 64 * WR;                       // rows per workgroup
-    static constexpr int BC = 64 * WC;                       // columns per workgroup
+    static constexpr int GR = GR_, GC = GC_;                 // waves of a K group along rows / columns
+    static constexpr int KS = KS_;                           // K groups (stage js goes to group js % KS)
+    static constexpr int NS = NS_;                           // LDS stages in each group's ring
+    static constexpr int GROUP = GROUP_;                     // row tiles per group of the tile order
+    static constexpr int GW = GR * GC;                       // waves per K group
+    static constexpr int GT = GW * kWave;                    // threads per K group
+    static constexpr int NT = GT * KS;                       // threads per workgroup
+    static constexpr int BR = 32 * WR * GR;                  // rows per workgroup
+    static constexpr int BC = 32 * WC * GC;                  // columns per workgroup
     static constexpr int A_BYTES = BR * kBJ * 2;             // one A stage
     static constexpr int B_BYTES = TERN ? BC * kBJ / 4 : BC * kBJ * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int RING = NS * STAGE;                  // one group's stages
     static constexpr int A_SLOTS = A_BYTES / 16;              // 16-byte load slots
     static constexpr int B_SLOTS = B_BYTES / 16;
-    static_assert(A_SLOTS % kThreads == 0, "whole A loads per thread");
-    static_assert(TERN ? (B_SLOTS % kWave == 0 && B_SLOTS <= kThreads) : B_SLOTS % kThreads == 0,
-                  "whole B loads per wave");
-    static_assert(2 * STAGE <= 160 * 1024, "LDS");
+    // 2-bit B: waves 0 .. B_WAVES - 1 of a group load the codes, the others
+    // issue an out-of-range load into a spare 1 KiB, so every wave counts the
+    // same loads.
+    static constexpr int B_WAVES = TERN ? B_SLOTS / kWave : 0;
+    static constexpr int SPARE = TERN && B_WAVES < GW ? kWave * 16 : 0;
+    static constexpr int LOADS = A_SLOTS / GT + (TERN ? 1 : B_SLOTS / GT);  // per wave per stage
+    static constexpr int PARTIAL = KS > 1 ? GW * WR * WC * 16 * kWave * 4 : 0;  // one group's sums
+    static constexpr int LDS = KS * RING + SPARE > PARTIAL ? KS * RING + SPARE : PARTIAL;
+    static_assert(A_SLOTS % GT == 0, "whole A loads per thread");
+    static_assert(TERN ? (B_SLOTS % kWave == 0 && B_WAVES <= GW) : B_SLOTS % GT == 0, "whole B loads per wave");
+    static_assert(NS >= 2 && (NS - 2) * LOADS <= 63, "vmcnt range");
+    static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// Two bf16 values (-1, 0 or +1) from the codes (0, 1, 2) in bytes b and b + 1
-// of d: the codes select bytes of a table (low bytes 80 00 80, high bytes
-// BF 00 3F), so code c becomes the bf16 pattern of c - 1.
-template <int B>
-__device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t d) {
-    constexpr uint32_t dup = B == 0 ? 0x01010000u : 0x03030202u;
-    const uint32_t sel = __builtin_amdgcn_perm(d, d, dup) + 0x04000400u;
-    return __builtin_amdgcn_perm(0x003F00BFu, 0x00800080u, sel);
+// This wave's loads older than the newest N have landed and its LDS reads are
+// done, then the workgroup barrier: one asm statement with a memory clobber,
+// so the compiler neither moves LDS accesses across it nor adds a wait of its
+// own for the loads still in flight.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <class C, bool TERN>
-__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
+// Four bf16 values (-1, 0 or +1), two per dword, from the codes (0, 1, 2) in
+// the four bytes of d: a first permute pairs each code c with c + 4, and the
+// pair selects the low byte (80 00 80 for c = 0, 1, 2, table positions 0 .. 2)
+// and the high byte (BF 00 3F, positions 4 .. 6) of the bf16 pattern of c - 1.
+__device__ __forceinline__ void codes_to_bf16x4(uint32_t d, uint32_t& v01, uint32_t& v23) {
+    const uint32_t d4 = d | 0x04040404u;
+    v01 = __builtin_amdgcn_perm(0x003F00BFu, 0x00800080u, __builtin_amdgcn_perm(d4, d, 0x05010400u));
+    v23 = __builtin_amdgcn_perm(0x003F00BFu, 0x00800080u, __builtin_amdgcn_perm(d4, d, 0x07030602u));
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void bwd_gemm_kernel(
     const uint16_t* __restrict__ A, const uint8_t* __restrict__ B, int R, int Cn, int J,
     const float* __restrict__ scale_ptr, float* __restrict__ out) {
-    constexpr int WR = C::WR, WC = C::WC;
-    __shared__ __align__(16) uint8_t lds[2][C::STAGE];
+    constexpr bool TERN = C::TERN;
+    constexpr int WR = C::WR, WC = C::WC, NS = C::NS, KS = C::KS;
+    __shared__ __align__(16) uint8_t lds[C::LDS];
     const int t = threadIdx.x, lane = t % kWave;
-    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
-    const int wr = wave / 2, wc = wave % 2;
-    const int64_t r0 = (int64_t)blockIdx.y * C::BR;
-    const int64_t c0 = (int64_t)blockIdx.x * C::BC;
+    const int wave_all = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int kg = wave_all / C::GW, wave = wave_all % C::GW;
+    const int wr = wave / C::GC, wc = wave % C::GC;
+    uint8_t* ring = lds + kg * C::RING;
+
+    // Launch index -> tile: a contiguous range of tiles per XCD (workgroups go
+    // round-robin over the XCDs), ordered in groups of GROUP row tiles with the
+    // column index outermost, so the blocks running together on one XCD share
+    // their A rows and B columns in its L2.
+    const int tiles_r = (R + C::BR - 1) / C::BR, tiles_c = (Cn + C::BC - 1) / C::BC;
+    const int total = tiles_r * tiles_c;
+    const int per = total / kXcds, rem = total % kXcds;
+    const int xcd = (int)blockIdx.x % kXcds, idx = (int)blockIdx.x / kXcds;
+    const int tile = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+    const int first_r = tile / (C::GROUP * tiles_c) * C::GROUP;
+    const int gsize = min(tiles_r - first_r, C::GROUP);
+    const int in_group = tile % (C::GROUP * tiles_c);
+    // (the divisions run on the vector unit: readfirstlane keeps the tile origin,
+    // and so the buffer resources, in scalar registers)
+    const int64_t r0 = (int64_t)__builtin_amdgcn_readfirstlane(first_r + in_group % gsize) * C::BR;
+    const int64_t c0 = (int64_t)__builtin_amdgcn_readfirstlane(in_group / gsize) * C::BC;
+
     const float scale = scale_ptr != nullptr ? scale_ptr[0] : 1.0f;
     const int a_rows = (int)min((int64_t)C::BR, (int64_t)R - r0);
     const int b_rows = (int)min((int64_t)C::BC, (int64_t)Cn - c0);
@@ -125,38 +173,56 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
         (void*)(A + r0 * J), (short)0, a_rows * J * 2, (int)kBufferWord3);
     const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(B + c0 * b_row_bytes), (short)0, b_rows * b_row_bytes, (int)kBufferWord3);
+    const int nj = J / kBJ;                 // J is a multiple of kBJ
+    const int steps = (nj + KS - 1) / KS;  // stages per group, the same for every group
 
-    // A (and B when bf16) tiles: row r of 64 values = 8 granules of 16 bytes,
-    // granule g stored at position g ^ (r & 7) so that the 32 rows a fragment
-    // read touches spread over all banks.  Slot p of the tile is filled by a
-    // load of row p / 8, granule (p % 8) ^ (row & 7).
-    auto load_stage = [&](int buf, int j0) {
+    // Group kg's i-th stage is stage js = kg + KS i.  A (and B when bf16)
+    // tiles: row r of 64 values = 8 granules of 16 bytes, granule g stored at
+    // position g ^ (r & 7) so that the 32 rows a fragment read touches spread
+    // over all banks.  Slot p of the tile is filled by a load of row p / 8,
+    // granule (p % 8) ^ (row & 7).  Each lane's load offsets are fixed up front
+    // (kFar for rows past the block's valid rows); a stage adds its column
+    // offset, or kFar for a stage past the last, which then reads out of range
+    // (zeros, no memory traffic) but is still issued, so every wave counts
+    // LOADS loads per stage.  A buffer here spans at most 2^30 bytes, so
+    // kFar, and kFar plus any offset, lies past its end.
+    constexpr uint32_t kFar = 0x40000000u;
+    constexpr int AL = C::A_SLOTS / C::GT, BL = TERN ? 1 : C::B_SLOTS / C::GT;
+    uint32_t a_off[AL], b_off[BL];
 #pragma unroll
-        for (int i = 0; i < C::A_SLOTS / kThreads; ++i) {
-            const int base = i * kThreads + wave * kWave;  // wave-uniform
-            const int p = base + lane, r = p / 8, g = (p % 8) ^ (r & 7);
-            const int j = j0 + 8 * g;
-            const uint32_t off = (r < a_rows && j < J) ? (uint32_t)((r * J + j) * 2) : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)&lds[buf][base * 16], 16, (int)off, 0, 0, 0);
+    for (int u = 0; u < AL; ++u) {
+        const int p = u * C::GT + wave * kWave + lane, r = p / 8, g = (p % 8) ^ (r & 7);
+        a_off[u] = r < a_rows ? (uint32_t)((r * J + 8 * g) * 2) : kFar;
+    }
+    if constexpr (TERN) {
+        const int c = wave * kWave + lane;  // row c: 16 bytes (64 codes) per stage, slot c
+        b_off[0] = (wave < C::B_WAVES && c < b_rows) ? (uint32_t)(c * b_row_bytes) : kFar;
+    } else {
+#pragma unroll
+        for (int u = 0; u < BL; ++u) {
+            const int p = u * C::GT + wave * kWave + lane, r = p / 8, g = (p % 8) ^ (r & 7);
+            b_off[u] = r < b_rows ? (uint32_t)((r * J + 8 * g) * 2) : kFar;
         }
-        constexpr int BOFF = C::A_BYTES;
+    }
+    auto load_stage = [&](int i, int slot) {
+        const int js = kg + KS * i;
+        const bool live = js < nj;
+        const uint32_t a_add = live ? (uint32_t)(js * kBJ * 2) : kFar;
+        const uint32_t b_add = live ? (uint32_t)(TERN ? js * kBJ / 4 : js * kBJ * 2) : kFar;
+        uint8_t* st = ring + slot * C::STAGE;
+#pragma unroll
+        for (int u = 0; u < AL; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_void*)(st + (u * C::GT + wave * kWave) * 16), 16,
+                                                     (int)(a_off[u] + a_add), 0, 0, 0);
         if constexpr (TERN) {
-            // row c: 16 bytes (64 codes) per stage, slot c
-            const int base = wave * kWave;
-            if (base < C::B_SLOTS) {
-                const int c = base + lane;
-                const uint32_t off = c < b_rows ? (uint32_t)(c * b_row_bytes + j0 / 4) : kOutOfRange;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (lds_void*)&lds[buf][BOFF + base * 16], 16, (int)off, 0, 0, 0);
-            }
+            uint8_t* dst = wave < C::B_WAVES ? st + C::A_BYTES + wave * kWave * 16 : lds + KS * C::RING;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (lds_void*)dst, 16, (int)(b_off[0] + b_add), 0, 0, 0);
         } else {
 #pragma unroll
-            for (int i = 0; i < C::B_SLOTS / kThreads; ++i) {
-                const int base = i * kThreads + wave * kWave;
-                const int p = base + lane, r = p / 8, g = (p % 8) ^ (r & 7);
-                const int j = j0 + 8 * g;
-                const uint32_t off = (r < b_rows && j < J) ? (uint32_t)((r * J + j) * 2) : kOutOfRange;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(bres, (lds_void*)&lds[buf][BOFF + base * 16], 16, (int)off, 0, 0, 0);
-            }
+            for (int u = 0; u < BL; ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    bres, (lds_void*)(st + C::A_BYTES + (u * C::GT + wave * kWave) * 16), 16,
+                    (int)(b_off[u] + b_add), 0, 0, 0);
         }
     };
 
@@ -168,28 +234,29 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
 
     const int h = lane / 32, l32 = lane % 32;
     auto frag = [&](const uint8_t* tile, int row, int g) {
-        return *reinterpret_cast<const uint4*>(tile + (row * 8 + (g ^ (row & 7))) * 16);
+        return *reinterpret_cast<const v4u*>(tile + (row * 8 + (g ^ (row & 7))) * 16);
     };
-    auto compute = [&](int buf) {
-        const uint8_t* at = lds[buf];
-        const uint8_t* bt = lds[buf] + C::A_BYTES;
-        uint4 bq[WC];
+    auto compute = [&](int slot) {
+        const uint8_t* at = ring + slot * C::STAGE;
+        const uint8_t* bt = at + C::A_BYTES;
+        v4u bq[WC];
         if constexpr (TERN) {
 #pragma unroll
             for (int cb = 0; cb < WC; ++cb)
-                bq[cb] = *reinterpret_cast<const uint4*>(bt + (wc * (32 * WC) + cb * 32 + l32) * 16);
+                bq[cb] = *reinterpret_cast<const v4u*>(bt + (wc * (32 * WC) + cb * 32 + l32) * 16);
         }
 #pragma unroll
         for (int s = 0; s < kBJ / 16; ++s) {
-            uint4 bf[WC];
+            v4u bf[WC];
 #pragma unroll
             for (int cb = 0; cb < WC; ++cb) {
                 if constexpr (TERN) {
-                    const uint32_t w = s == 0 ? bq[cb].x : (s == 1 ? bq[cb].y : (s == 2 ? bq[cb].z : bq[cb].w));
-                    const uint32_t d0 = (w >> (4 * h)) & 0x03030303u;      // values 8h .. 8h+3 of the step
-                    const uint32_t d1 = (w >> (4 * h + 2)) & 0x03030303u;  // values 8h+4 .. 8h+7
-                    bf[cb] = make_uint4(codes_to_bf16x2<0>(d0), codes_to_bf16x2<2>(d0),
-                                        codes_to_bf16x2<0>(d1), codes_to_bf16x2<2>(d1));
+                    const uint32_t w = bq[cb][s] >> (4 * h);
+                    // values 8h .. 8h+3 of the step, then 8h+4 .. 8h+7
+                    uint32_t v0, v1, v2, v3;
+                    codes_to_bf16x4(w & 0x03030303u, v0, v1);
+                    codes_to_bf16x4((w >> 2) & 0x03030303u, v2, v3);
+                    bf[cb] = v4u{v0, v1, v2, v3};
                 } else {
                     bf[cb] = frag(bt, wc * (32 * WC) + cb * 32 + l32, 2 * s + h);
                 }
@@ -197,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
 #pragma unroll
             for (int rb = 0; rb < WR; ++rb) {
                 const int row = wr * (32 * WR) + rb * 32 + l32;
-                const uint4 af = frag(at, row, 2 * s + h);
+                const v4u af = frag(at, row, 2 * s + h);
 #pragma unroll
                 for (int cb = 0; cb < WC; ++cb)
                     acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -206,13 +273,50 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(
         }
     };
 
-    const int nj = (J + kBJ - 1) / kBJ;
-    load_stage(0, 0);
-    for (int js = 0; js < nj; ++js) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();  // stage js landed for every wave; stage js - 1 fully read
-        if (js + 1 < nj) load_stage((js + 1) % 2, (js + 1) * kBJ);
-        compute(js % 2);
+    // Each group's ring of NS stages: NS - 1 in flight ahead of the one being
+    // computed.  At step i the slot refilled is the one computed at step i - 1,
+    // which the barrier has just released; step i uses slot i % NS.
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) load_stage(i, i);
+    for (int i0 = 0; i0 < steps; i0 += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {  // slot u: fixed LDS addresses in the unrolled body
+            if (i0 + u < steps) {
+                stage_barrier<(NS - 2) * C::LOADS>();  // stage i0 + u landed for every wave
+                load_stage(i0 + u + NS - 1, (u + NS - 1) % NS);
+                if (kg + KS * (i0 + u) < nj) compute(u);
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no transfer into LDS outlives the workgroup
+
+    // K groups: group 0 adds the other groups' sums, group KS - 1 first.
+    if constexpr (KS > 1) {
+        float* part = reinterpret_cast<float*>(lds);
+#pragma unroll 1
+        for (int g = KS - 1; g >= 1; --g) {
+            __syncthreads();  // every wave is done with the stage buffers (or the previous sums)
+            if (kg == g) {
+#pragma unroll
+                for (int rb = 0; rb < WR; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < WC; ++cb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            part[((wave * WR * WC + rb * WC + cb) * 16 + e) * kWave + lane] = acc[rb][cb][e];
+            }
+            __syncthreads();
+            if (kg == 0) {
+#pragma unroll
+                for (int rb = 0; rb < WR; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < WC; ++cb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e)
+                            acc[rb][cb][e] += part[((wave * WR * WC + rb * WC + cb) * 16 + e) * kWave + lane];
+            }
+        }
+        if (kg != 0) return;
     }
 
     // D[i][j] of a 32 x 32 block: lane j + 32 ((i / 4) % 2), element 4 (i / 8) + i % 4.
@@ -385,8 +489,18 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ p, i
         p[i] = 0.f;
 }
 
-using CfgIn = BwdCfg<2, 2, true>;    // dL/dn: 128 x 128 tiles, 2-bit B
-using CfgW = BwdCfg<2, 2, false>;    // dL/dW: 128 x 128 tiles, bf16 B
+// dL/dn: 256 x 128 tiles of 2 x 2 waves with 128 x 64 each, two K groups (8
+// waves, one workgroup per CU); the grid is small (M/256 x K/128 tiles), so
+// consecutive tiles on an XCD share their grad_y rows.
+using CfgIn = BwdCfg<4, 2, 2, 2, 2, true, 2, 1>;
+// dL/dW: 128 x 128 tiles of 2 x 2 waves with 64 x 64 each (two workgroups per
+// CU: bf16 B tiles leave no LDS for larger ones), groups of 8 row tiles.
+using CfgW = BwdCfg<2, 2, 2, 2, 1, false, 2, 8>;
+
+template <class C>
+dim3 bwd_grid(int64_t R, int64_t Cn) {
+    return dim3((unsigned)(((R + C::BR - 1) / C::BR) * ((Cn + C::BC - 1) / C::BC)));
+}
 
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
@@ -406,9 +520,18 @@ hipError_t launch_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, 
 
 hipError_t launch_backward_input(const uint16_t* grad_y, const uint8_t* packed_t, const float* w_scale,
                                  int64_t M, int64_t N, int64_t K, float* grad_n, hipStream_t stream) {
-    const dim3 grid((unsigned)((K + CfgIn::BC - 1) / CfgIn::BC), (unsigned)((M + CfgIn::BR - 1) / CfgIn::BR));
-    return launch_kernel((bwd_gemm_kernel<CfgIn, true>), grid, dim3(kThreads), 0, stream, grad_y, packed_t,
-                         (int)M, (int)K, (int)N, w_scale, grad_n);
+    // Row ranges of at most 2^20 tokens per launch keep the tile count and the
+    // one-dimensional grid well inside 32 bits.
+    constexpr int64_t kRowsPerLaunch = int64_t(1) << 20;
+    static_assert(kRowsPerLaunch % CfgIn::BR == 0, "whole tiles per launch");
+    for (int64_t m0 = 0; m0 < M; m0 += kRowsPerLaunch) {
+        const int64_t rows = std::min(M - m0, kRowsPerLaunch);
+        const hipError_t e = launch_kernel(bwd_gemm_kernel<CfgIn>, bwd_grid<CfgIn>(rows, K), dim3(CfgIn::NT), 0,
+                                           stream, grad_y + m0 * N, packed_t, (int)rows, (int)K, (int)N, w_scale,
+                                           grad_n + m0 * K);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 size_t backward_weight_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -428,8 +551,7 @@ hipError_t launch_backward_weight(const uint16_t* grad_y, const int8_t* xq, cons
     e = launch_kernel(prep_codes_kernel, dim3((unsigned)(Mp / 64), (unsigned)(K / 64)), dim3(kThreads), 0, stream,
                       xq, (int)M, (int)K, (int)Mp, b);
     if (e != hipSuccess) return e;
-    const dim3 grid((unsigned)((K + CfgW::BC - 1) / CfgW::BC), (unsigned)((N + CfgW::BR - 1) / CfgW::BR));
-    return launch_kernel((bwd_gemm_kernel<CfgW, false>), grid, dim3(kThreads), 0, stream, (const uint16_t*)a,
+    return launch_kernel(bwd_gemm_kernel<CfgW>, bwd_grid<CfgW>(N, K), dim3(CfgW::NT), 0, stream, (const uint16_t*)a,
                          reinterpret_cast<const uint8_t*>(b), (int)N, (int)K, (int)(2 * Mp), (const float*)nullptr,
                          grad_w);
 }

@@ -305,7 +305,8 @@ size_t bitnet_linear_backward_weight_workspace_bytes(int64_t M, int64_t N, int64
  *              16-byte aligned (transposed operands; contents undefined after).
  * grad_y * d_x is rounded once to float32 and carried as two bf16 halves
  * (relative error <= 2^-16 per term); the codes are exact; the sum over m is
- * accumulated in float32 on the bf16 matrix cores.  M = 0 writes zeros.
+ * accumulated in float32 on the bf16 matrix cores.  M = 0 writes zeros; M
+ * above 2^21 is rejected with BITNET_ERR_SHAPE.
  */
 int bitnet_linear_backward_weight(const uint16_t* grad_y, const int8_t* xq, const float* x_scale,
                                   int64_t M, int64_t N, int64_t K, float* grad_w,

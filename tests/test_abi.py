@@ -230,9 +230,12 @@ def test_backward_argument_errors(L):
     assert need == (128 + 256) * 2 * 64 * 2
     assert L.bitnet_linear_backward_weight_workspace_bytes(0, 128, 256) == 0
     assert L.bitnet_linear_backward_weight_workspace_bytes(8, 100, 256) == 0
+    assert L.bitnet_linear_backward_weight_workspace_bytes(2 ** 21, 128, 256) > 0
+    assert L.bitnet_linear_backward_weight_workspace_bytes(2 ** 21 + 1, 128, 256) == 0
     bw = lambda gy=A16, xq=A16, sx=A4, M=8, N=128, K=256, out=A4, ws=A16, wsb=need: \
         L.bitnet_linear_backward_weight(p(gy), p(xq), p(sx), M, N, K, p(out), p(ws), wsb, None)
     assert bw(N=64 + 32) == 2
+    assert bw(M=2 ** 21 + 1) == 2
     assert bw(out=0) == 1
     assert bw(gy=0) == 1
     assert bw(xq=A4) == 4

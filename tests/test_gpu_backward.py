@@ -91,7 +91,7 @@ def check_backward_input(orc, g_bits, packed, d_w, q, K, got):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (5, 128, 256), (300, 192, 320), (64, 4096, 4096),
-                                   (33, 11008, 4096), (17, 4096, 11008)])
+                                   (33, 11008, 4096), (17, 4096, 11008), (513, 640, 1152)])
 def test_linear_backward_input(orc, dev, M, N, K):
     packed, d_w, q, pd, ws = packed_for(orc, N, K, 310 + M, dev)
     g = grad_bits(M, N, 311 + N % 97)
@@ -140,7 +140,7 @@ def check_backward_weight(orc, g_bits, xq, d_x, got):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (7, 128, 256), (300, 192, 320), (100, 4096, 4096),
-                                   (64, 11008, 4096), (65, 4096, 11008)])
+                                   (64, 11008, 4096), (65, 4096, 11008), (129, 1088, 704)])
 def test_linear_backward_weight(orc, dev, M, N, K):
     xq, d_x = codes(M, K, 330 + M)
     g = grad_bits(M, N, 331 + N % 89)
