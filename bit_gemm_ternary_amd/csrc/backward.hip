@@ -22,11 +22,11 @@
 // tiles (128 x 64) and two K groups to keep two waves per SIMD.  For dL/dW,
 // p = grad_y * d_x is carried as a bf16 pair hi + lo (hi = bf16(p),
 // lo = bf16(p - hi), |p - hi - lo| <= 2^-16 |p|) and the activation codes
-// (exact in bf16) are repeated: the operands are A = [hi | lo] ([N][2 Mp]) and
-// B = [codes | codes] ([K][2 Mp]), transposed so that the token index m runs
-// along the rows, and the same kernel sums the 2 Mp products; with both tiles
-// bf16 it is bound by LDS bandwidth and capacity, and 64 x 64 wave tiles with
-// two workgroups per CU measured best.
+// (exact in bf16) are shared: the operands are A = [hi | lo] ([N][2 Mp]) and
+// B = codes ([K][Mp]), transposed so that the token index m runs along the
+// rows; a stage holds both planes of A, and each B fragment read from LDS
+// feeds the hi and the lo product.  With both tiles bf16 the kernel is bound
+// by LDS bandwidth and capacity.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -83,9 +83,13 @@ __global__ __launch_bounds__(kThreads) void transpose_packed_kernel(const uint8_
 // 2 x 2 waves, a wave WR x WC blocks of 32 x 32; K steps of 16 inside LDS
 // stages of 64.  TERN: B is 2-bit codes q+1 ([C][J/4] bytes), else bf16.
 // ---------------------------------------------------------------------------
-template <int WR_, int WC_, int GR_, int GC_, int KS_, bool TERN_, int NS_, int GROUP_>
+template <int WR_, int WC_, int GR_, int GC_, int KS_, bool TERN_, int NS_, int GROUP_, int PL_ = 1>
 struct BwdCfg {
     static constexpr bool TERN = TERN_;                      // B is 2-bit codes, else bf16
+    // A planes: with PL = 2 a row of A holds two J-long planes (the hi and lo
+    // halves of dL/dW's left operand), both multiplied with the same B value,
+    // so each B fragment read from LDS serves both.
+    static constexpr int PL = PL_;
     static constexpr int WR = WR_, WC = WC_;                 // 32 x 32 blocks per wave
     static constexpr int GR = GR_, GC = GC_;                 // waves of a K group along rows / columns
     static constexpr int KS = KS_;                           // K groups (stage js goes to group js % KS)
@@ -96,7 +100,8 @@ struct BwdCfg {
     static constexpr int NT = GT * KS;                       // threads per workgroup
     static constexpr int BR = 32 * WR * GR;                  // rows per workgroup
     static constexpr int BC = 32 * WC * GC;                  // columns per workgroup
-    static constexpr int A_BYTES = BR * kBJ * 2;             // one A stage
+    static constexpr int A_PLANE = BR * kBJ * 2;             // one A plane of a stage
+    static constexpr int A_BYTES = PL * A_PLANE;
     static constexpr int B_BYTES = TERN ? BC * kBJ / 4 : BC * kBJ * 2;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int RING = NS * STAGE;                  // one group's stages
@@ -110,7 +115,8 @@ struct BwdCfg {
     static constexpr int LOADS = A_SLOTS / GT + (TERN ? 1 : B_SLOTS / GT);  // per wave per stage
     static constexpr int PARTIAL = KS > 1 ? GW * WR * WC * 16 * kWave * 4 : 0;  // one group's sums
     static constexpr int LDS = KS * RING + SPARE > PARTIAL ? KS * RING + SPARE : PARTIAL;
-    static_assert(A_SLOTS % GT == 0, "whole A loads per thread");
+    static_assert(A_SLOTS % GT == 0 && (A_PLANE / 16) % GT == 0, "whole A loads per thread and plane");
+    static_assert(PL == 1 || (PL == 2 && !TERN), "two A planes only with bf16 B");
     static_assert(TERN ? (B_SLOTS % kWave == 0 && B_WAVES <= GW) : B_SLOTS % GT == 0, "whole B loads per wave");
     static_assert(NS >= 2 && (NS - 2) * LOADS <= 63, "vmcnt range");
     static_assert(LDS <= 160 * 1024, "LDS");
@@ -169,8 +175,9 @@ __global__ __launch_bounds__(C::NT) void bwd_gemm_kernel(
     const int a_rows = (int)min((int64_t)C::BR, (int64_t)R - r0);
     const int b_rows = (int)min((int64_t)C::BC, (int64_t)Cn - c0);
     const int b_row_bytes = TERN ? J / 4 : J * 2;
+    const int a_stride = C::PL * J;  // values per row of A
     const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A + r0 * J), (short)0, a_rows * J * 2, (int)kBufferWord3);
+        (void*)(A + r0 * a_stride), (short)0, a_rows * a_stride * 2, (int)kBufferWord3);
     const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(B + c0 * b_row_bytes), (short)0, b_rows * b_row_bytes, (int)kBufferWord3);
     const int nj = J / kBJ;                 // J is a multiple of kBJ
@@ -191,8 +198,10 @@ __global__ __launch_bounds__(C::NT) void bwd_gemm_kernel(
     uint32_t a_off[AL], b_off[BL];
 #pragma unroll
     for (int u = 0; u < AL; ++u) {
-        const int p = u * C::GT + wave * kWave + lane, r = p / 8, g = (p % 8) ^ (r & 7);
-        a_off[u] = r < a_rows ? (uint32_t)((r * J + 8 * g) * 2) : kFar;
+        const int pa = u * C::GT + wave * kWave + lane;
+        const int plane = pa / (C::A_PLANE / 16), p = pa % (C::A_PLANE / 16);
+        const int r = p / 8, g = (p % 8) ^ (r & 7);
+        a_off[u] = r < a_rows ? (uint32_t)((r * a_stride + plane * J + 8 * g) * 2) : kFar;
     }
     if constexpr (TERN) {
         const int c = wave * kWave + lane;  // row c: 16 bytes (64 codes) per stage, slot c
@@ -262,14 +271,16 @@ __global__ __launch_bounds__(C::NT) void bwd_gemm_kernel(
                 }
             }
 #pragma unroll
-            for (int rb = 0; rb < WR; ++rb) {
-                const int row = wr * (32 * WR) + rb * 32 + l32;
-                const v4u af = frag(at, row, 2 * s + h);
+            for (int pl = 0; pl < C::PL; ++pl)  // planes in turn: WR x WC MFMAs between dependent ones
 #pragma unroll
-                for (int cb = 0; cb < WC; ++cb)
-                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(v8bf, af), __builtin_bit_cast(v8bf, bf[cb]), acc[rb][cb], 0, 0, 0);
-            }
+                for (int rb = 0; rb < WR; ++rb) {
+                    const int row = wr * (32 * WR) + rb * 32 + l32;
+                    const v4u af = frag(at + pl * C::A_PLANE, row, 2 * s + h);
+#pragma unroll
+                    for (int cb = 0; cb < WC; ++cb)
+                        acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(v8bf, af), __builtin_bit_cast(v8bf, bf[cb]), acc[rb][cb], 0, 0, 0);
+                }
         }
     };
 
@@ -333,9 +344,9 @@ __global__ __launch_bounds__(C::NT) void bwd_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Operands of dL/dW, rows of 2 Mp values (Mp = M rounded up to 64; columns
-// m >= M are zero): a[n] = [hi of p[.][n] | lo of p[.][n]] with
-// p = grad_y[m][n] * d_x[m], and b[k] = [codes[.][k] | codes[.][k]] in bf16.
+// Operands of dL/dW (Mp = M rounded up to 64; columns m >= M are zero):
+// a[n] = [hi of p[.][n] | lo of p[.][n]], 2 Mp values, with
+// p = grad_y[m][n] * d_x[m], and b[k] = codes[.][k] in bf16, Mp values.
 // One 64 x 64 tile per workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void prep_grad_kernel(const uint16_t* __restrict__ g,
@@ -404,12 +415,9 @@ __global__ __launch_bounds__(kThreads) void prep_codes_kernel(const int8_t* __re
         const uint32_t b1 = __float_as_uint((float)tile[mc + 2 * e + 1][kr]) >> 16;
         o[e] = b0 | (b1 << 16);
     }
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        uint4* dst = reinterpret_cast<uint4*>(b + (int64_t)(k0 + kr) * 2 * Mp + half * Mp + m0 + mc);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    }
+    uint4* dst = reinterpret_cast<uint4*>(b + (int64_t)(k0 + kr) * Mp + m0 + mc);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 // ---------------------------------------------------------------------------
@@ -493,9 +501,10 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(float* __restrict__ p, i
 // waves, one workgroup per CU); the grid is small (M/256 x K/128 tiles), so
 // consecutive tiles on an XCD share their grad_y rows.
 using CfgIn = BwdCfg<4, 2, 2, 2, 2, true, 2, 1>;
-// dL/dW: 128 x 128 tiles of 2 x 2 waves with 64 x 64 each (two workgroups per
-// CU: bf16 B tiles leave no LDS for larger ones), groups of 8 row tiles.
-using CfgW = BwdCfg<2, 2, 2, 2, 1, false, 2, 8>;
+// dL/dW: 128 x 256 tiles of 2 x 4 waves with 64 x 64 each and the hi and lo
+// planes of A in one stage (one workgroup per CU: bf16 B tiles leave no LDS
+// for a second), groups of 8 row tiles.
+using CfgW = BwdCfg<2, 2, 2, 4, 1, false, 2, 8, 2>;
 
 template <class C>
 dim3 bwd_grid(int64_t R, int64_t Cn) {
@@ -536,15 +545,15 @@ hipError_t launch_backward_input(const uint16_t* grad_y, const uint8_t* packed_t
 
 size_t backward_weight_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t Mp = round_up(M, 64);
-    return (size_t)((N + K) * 2 * Mp * 2);
+    return (size_t)((2 * N + K) * Mp * 2);
 }
 
 hipError_t launch_backward_weight(const uint16_t* grad_y, const int8_t* xq, const float* x_scale,
                                   int64_t M, int64_t N, int64_t K, float* grad_w, void* workspace,
                                   hipStream_t stream) {
     const int64_t Mp = round_up(M, 64);
-    uint16_t* a = static_cast<uint16_t*>(workspace);  // [N][2 Mp]
-    uint16_t* b = a + N * 2 * Mp;                       // [K][2 Mp]
+    uint16_t* a = static_cast<uint16_t*>(workspace);  // [N][2 Mp]: hi and lo planes
+    uint16_t* b = a + N * 2 * Mp;                       // [K][Mp]
     hipError_t e = launch_kernel(prep_grad_kernel, dim3((unsigned)(Mp / 64), (unsigned)(N / 64)), dim3(kThreads),
                                  0, stream, grad_y, x_scale, (int)M, (int)N, (int)Mp, a);
     if (e != hipSuccess) return e;
@@ -552,7 +561,7 @@ hipError_t launch_backward_weight(const uint16_t* grad_y, const int8_t* xq, cons
                       xq, (int)M, (int)K, (int)Mp, b);
     if (e != hipSuccess) return e;
     return launch_kernel(bwd_gemm_kernel<CfgW>, bwd_grid<CfgW>(N, K), dim3(CfgW::NT), 0, stream, (const uint16_t*)a,
-                         reinterpret_cast<const uint8_t*>(b), (int)N, (int)K, (int)(2 * Mp), (const float*)nullptr,
+                         reinterpret_cast<const uint8_t*>(b), (int)N, (int)K, (int)Mp, (const float*)nullptr,
                          grad_w);
 }
 

@@ -227,7 +227,7 @@ def test_backward_argument_errors(L):
     assert bi(M=0, gy=0, pt=0) == 0   # empty batch: nothing enqueued
     # grad_w: workspace size and alignment
     need = L.bitnet_linear_backward_weight_workspace_bytes(8, 128, 256)
-    assert need == (128 + 256) * 2 * 64 * 2
+    assert need == (2 * 128 + 256) * 64 * 2
     assert L.bitnet_linear_backward_weight_workspace_bytes(0, 128, 256) == 0
     assert L.bitnet_linear_backward_weight_workspace_bytes(8, 100, 256) == 0
     assert L.bitnet_linear_backward_weight_workspace_bytes(2 ** 21, 128, 256) > 0
