@@ -99,9 +99,11 @@ def test_linear_backward_input(orc, dev, M, N, K):
     check_backward_input(orc, g, packed, d_w, q, K, got)
 
 
-def test_linear_backward_input_full_size_sampled(orc, dev):
-    # the prefill shape (M 2048, N 4096 -> K 4096 back), checked on 24 sampled tokens
-    M, N, K = 2048, 4096, 4096
+@pytest.mark.parametrize("N", [4096, 14336])
+def test_linear_backward_input_full_size_sampled(orc, dev, N):
+    # M 2048 tokens back through N outputs to K 4096 (N 14336: the benchmark's
+    # prefill layer), checked on 24 sampled tokens
+    M, K = 2048, 4096
     packed, d_w, q, pd, ws = packed_for(orc, N, K, 320, dev)
     g = grad_bits(M, N, 321)
     got = host(bt.linear_backward_input(bf16_to_dev(g, dev), bt.transpose_packed(pd, K), ws))
@@ -148,9 +150,11 @@ def test_linear_backward_weight(orc, dev, M, N, K):
     check_backward_weight(orc, g, xq, d_x, got)
 
 
-def test_linear_backward_weight_full_size_sampled(orc, dev):
-    # M 2048 tokens, N 4096, K 4096; sampled 32 x 64 block of grad_w
-    M, N, K = 2048, 4096, 4096
+@pytest.mark.parametrize("N", [4096, 14336])
+def test_linear_backward_weight_full_size_sampled(orc, dev, N):
+    # M 2048 tokens, N outputs, K 4096 (N 14336: the benchmark's prefill
+    # layer); sampled 32 x 64 block of grad_w
+    M, K = 2048, 4096
     xq, d_x = codes(M, K, 340)
     g = grad_bits(M, N, 341)
     got = host(bt.linear_backward_weight(bf16_to_dev(g, dev), to_dev(xq, dev), to_dev(d_x, dev)))
