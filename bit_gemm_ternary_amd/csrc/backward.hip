@@ -132,13 +132,14 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // Four bf16 values (-1, 0 or +1), two per dword, from the codes (0, 1, 2) in
-// the four bytes of d: a first permute pairs each code c with c + 4, and the
-// pair selects the low byte (80 00 80 for c = 0, 1, 2, table positions 0 .. 2)
-// and the high byte (BF 00 3F, positions 4 .. 6) of the bf16 pattern of c - 1.
+// the four bytes of d: the codes select from a table of low bytes (80 00 80)
+// and from one of high bytes (BF 00 3F) of the bf16 patterns of c - 1, and two
+// permutes interleave the low and high bytes into bf16 pairs.
 __device__ __forceinline__ void codes_to_bf16x4(uint32_t d, uint32_t& v01, uint32_t& v23) {
-    const uint32_t d4 = d | 0x04040404u;
-    v01 = __builtin_amdgcn_perm(0x003F00BFu, 0x00800080u, __builtin_amdgcn_perm(d4, d, 0x05010400u));
-    v23 = __builtin_amdgcn_perm(0x003F00BFu, 0x00800080u, __builtin_amdgcn_perm(d4, d, 0x07030602u));
+    const uint32_t lo = __builtin_amdgcn_perm(0u, 0x00800080u, d);
+    const uint32_t hi = __builtin_amdgcn_perm(0u, 0x003F00BFu, d);
+    v01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    v23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
 }
 
 template <class C>
