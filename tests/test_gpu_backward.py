@@ -112,6 +112,18 @@ def test_linear_backward_input_full_size_sampled(orc, dev, N):
     check_backward_input(orc, g[rows], packed, d_w, q, K, got[rows])
 
 
+def test_linear_backward_input_over_a_million_tokens(orc, dev):
+    # more tokens than one launch covers (2^20 rows each): the row ranges must
+    # join without a gap; sampled tokens on both sides of the seam
+    M, N, K = (1 << 20) + 300, 64, 64
+    packed, d_w, q, pd, ws = packed_for(orc, N, K, 323, dev)
+    g = grad_bits(M, N, 324)
+    got = host(bt.linear_backward_input(bf16_to_dev(g, dev), bt.transpose_packed(pd, K), ws))
+    rows = np.array([0, 1, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, M - 1])
+    rows = np.concatenate([rows, np.random.default_rng(325).choice(M, 26, replace=False)])
+    check_backward_input(orc, g[rows], packed, d_w, q, K, got[rows])
+
+
 def test_linear_backward_input_empty_batch(dev):
     packed = torch.full((64, 64 // 4), 0x55, dtype=torch.uint8, device=dev)
     out = bt.linear_backward_input(torch.empty((0, 64), dtype=torch.bfloat16, device=dev),
@@ -162,6 +174,16 @@ def test_linear_backward_weight_full_size_sampled(orc, dev, N):
     ns = np.sort(rng.choice(N, 32, replace=False))
     ks = np.sort(rng.choice(K, 64, replace=False))
     ns[-1], ks[-1] = N - 1, K - 1
+    check_backward_weight(orc, g[:, ns], xq[:, ks], d_x, got[np.ix_(ns, ks)])
+
+
+def test_linear_backward_weight_at_the_token_limit(orc, dev):
+    # 2^21 tokens, the most dL/dW takes: operand rows of 2^22 bf16 values
+    M, N, K = 1 << 21, 128, 64
+    xq, d_x = codes(M, K, 343)
+    g = grad_bits(M, N, 344)
+    got = host(bt.linear_backward_weight(bf16_to_dev(g, dev), to_dev(xq, dev), to_dev(d_x, dev)))
+    ns, ks = np.array([0, 77, 127]), np.array([0, 31, 63])
     check_backward_weight(orc, g[:, ns], xq[:, ks], d_x, got[np.ix_(ns, ks)])
 
 
