@@ -52,30 +52,44 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {  // finite inputs
 // ---------------------------------------------------------------------------
 // packed [N][K/4] -> packed_t [K][N/4], both in the forward's layout along
 // their rows (word g holds values 16g..16g+15; value 16g + 4i + b at bits
-// 2i..2i+1 of byte b).  One 64 x 64 tile per workgroup.
+// 2i..2i+1 of byte b).  A workgroup moves 64 rows of N by kTK values of K:
+// each thread loads 16 bytes of one row and writes the 16 bytes (64 codes)
+// of one output row.
 // ---------------------------------------------------------------------------
+constexpr int kTK = 256;
+
 __global__ __launch_bounds__(kThreads) void transpose_packed_kernel(const uint8_t* __restrict__ packed,
                                                                    int N, int K,
                                                                    uint8_t* __restrict__ packed_t) {
-    __shared__ uint32_t tile[64][5];  // [n][word of k], padded
-    const int n0 = (int)blockIdx.y * 64, k0 = (int)blockIdx.x * 64;
+    static_assert(kTK == kThreads && kTK % 64 == 0, "one output row per thread");
+    __shared__ uint32_t tile[64][kTK / 16 + 1];  // [n][word of k], padded
+    const int n0 = (int)blockIdx.y * 64, k0 = (int)blockIdx.x * kTK;
     const int t = threadIdx.x;
     {
-        const int r = t / 4, w = t % 4;
-        tile[r][w] = *reinterpret_cast<const uint32_t*>(packed + (int64_t)(n0 + r) * (K / 4) + k0 / 4 + 4 * w);
+        const int r = t / 4, p = t % 4;  // row n0 + r, values k0 + 64p .. k0 + 64p + 63
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (k0 + 64 * p < K)
+            v = *reinterpret_cast<const uint4*>(packed + (int64_t)(n0 + r) * (K / 4) + k0 / 4 + 16 * p);
+        tile[r][4 * p] = v.x;
+        tile[r][4 * p + 1] = v.y;
+        tile[r][4 * p + 2] = v.z;
+        tile[r][4 * p + 3] = v.w;
     }
     __syncthreads();
-    const int kr = t / 4, wn = t % 4;  // output row k0 + kr, word wn (n = n0 + 16 wn ..)
-    const int kw = kr / 16, kshift = 8 * (kr % 4) + 2 * ((kr % 16) / 4);
-    uint32_t out = 0;
+    const int k = k0 + t;  // my output row
+    if (k >= K) return;
+    const int kw = t / 16, kshift = 8 * (t % 4) + 2 * ((t % 16) / 4);
+    uint32_t out[4] = {0, 0, 0, 0};  // word wn: n = n0 + 16 wn .. n0 + 16 wn + 15
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int wn = 0; wn < 4; ++wn)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t field = (tile[16 * wn + 4 * i + b][kw] >> kshift) & 3u;
-            out |= field << (8 * b + 2 * i);
-        }
-    *reinterpret_cast<uint32_t*>(packed_t + (int64_t)(k0 + kr) * (N / 4) + n0 / 4 + 4 * wn) = out;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t field = (tile[16 * wn + 4 * i + b][kw] >> kshift) & 3u;
+                out[wn] |= field << (8 * b + 2 * i);
+            }
+    *reinterpret_cast<uint4*>(packed_t + (int64_t)k * (N / 4) + n0 / 4) = make_uint4(out[0], out[1], out[2], out[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -524,7 +538,8 @@ hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t stream) {
 
 hipError_t launch_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed_t,
                                    hipStream_t stream) {
-    return launch_kernel(transpose_packed_kernel, dim3((unsigned)(K / 64), (unsigned)(N / 64)), dim3(kThreads),
+    return launch_kernel(transpose_packed_kernel, dim3((unsigned)((K + kTK - 1) / kTK), (unsigned)(N / 64)),
+                         dim3(kThreads),
                          0, stream, packed, (int)N, (int)K, packed_t);
 }
 
