@@ -13,8 +13,9 @@ rotation copy and one per full rotation), so the timed region measures the GPU,
 not Python launch overhead.
 
   value            packed weight bytes per step / step time (GB/s); config also
-                   gives it as a fraction of a plain 2 GiB device read (torch sum)
-                   and the warm number (one weight copy, Infinity-Cache resident)
+                   gives it as a fraction of a plain 1 GiB device copy (torch copy_,
+                   read + write bytes) and the warm number (one weight copy,
+                   Infinity-Cache resident)
   roofline         the fused decode kernel alone: algorithmic bytes (packed
                    weights, bf16 activations, codes and outputs) per launch /
                    average launch duration, each projection launched back to
@@ -22,6 +23,10 @@ not Python launch overhead.
                    timed by HIP events on the graphs' stream (per_launch also
                    gives the eager duration of one launch on an idle GPU, from
                    events stamped by the kernel's own dispatch)
+  decode_sizes     context: the same fused decode kernel (M = 1) on larger
+                   projections (8192 x 8192 up to 16384 x 53248), launched back to
+                   back like roofline.per_launch: per-launch time and GB/s once the
+                   launch's fixed cost is spread over 17-218 MB of packed weights
   prefill          W1.58A8 prefill M=2048, K=4096, N=14336: int8 TOPS of the
                    matrix-core GEMM against the dense int8 peak, and against that
                    peak scaled to the engine clock measured during the kernel
@@ -92,7 +97,7 @@ def parse_args():
     ap.add_argument("--block-steps", type=int, default=200, help="timed steps per token count of the block leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES, ten times (HBM counter calibration)")
-    ap.add_argument("--legs", default="decode,prefill,hadamard,block,backward,pack",
+    ap.add_argument("--legs", default="decode,decode_sizes,prefill,hadamard,block,backward,pack",
                     help="comma-separated legs to run (the headline needs decode)")
     ap.add_argument("--cpu-one-core-seconds", type=float, default=5.0,
                     help="wall time budget of the one-core CPU-oracle sample")
@@ -361,6 +366,52 @@ def decode_bench(args, dev, bt, torch, synth):
         "instrumented_steps": n_instr, "layers": layers,
         "warm_value": step_bytes / (warm_ms * 1e-3) / 1e9,
     }
+
+
+# (K, N) of the larger decode projections: Llama-70B-sized o / gate|up / down
+# and a 405B-sized gate|up.
+DECODE_SIZES = [(8192, 8192), (8192, 28672), (28672, 8192), (16384, 53248)]
+
+
+def decode_sizes_bench(args, dev, bt, torch, synth):
+    """The fused decode kernel (M = 1) on larger projections: average launch
+    duration back to back from HIP graphs over >= 1 GiB of rotating weight
+    copies, as for the headline's per-launch figures.  Seeded N(0, 0.02)
+    weights and N(0, 1) tokens drawn on the device."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5151)
+    rows = []
+    for K, N in DECODE_SIZES:
+        W = torch.randn((N, K), generator=gen, device=dev) * 0.02
+        packed, w_scale = bt.pack_weights(W)
+        del W
+        nbytes = N * K // 4
+        copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+        own = [packed] + [packed.clone() for _ in range(copies - 1)]
+        x = torch.randn((1, K), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        codes = (torch.empty((1, K), dtype=torch.int8, device=dev),
+                 torch.empty(1, dtype=torch.float32, device=dev),
+                 torch.empty(1, dtype=torch.int32, device=dev))
+
+        def one(r, own=own, x=x, y=y, codes=codes, w_scale=w_scale):
+            bt.bitlinear_forward(x, own[r], w_scale, None, 1e-5, out=y, codes=codes)
+
+        for r in range(copies):
+            one(r)
+        torch.cuda.synchronize()
+        run = graph_runner(one, copies, args.eager, torch)
+        launches = max(1, min(3 * args.steps, 3000) // copies) * copies
+        ms, _ = timed(run, launches, torch)
+        us = ms * 1e3
+        kernel_bytes = nbytes + 2 * K + 8 + K + 8 + 4 * N
+        rows.append({"K": K, "N": N, "packed_MB": round(nbytes / 1e6, 1), "copies": copies,
+                     "avg_us": round(us, 2), "GB_s": round(kernel_bytes / us / 1e3, 1),
+                     "frac_hbm": round(kernel_bytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        del run, own, packed, x, y, codes, one
+        torch.cuda.empty_cache()
+    return {"what": "fused decode kernel, M = 1, larger projections (context for the headline, "
+                    "which runs the 7B shapes)", "by_shape": rows}
 
 
 def time_launches(fn, iters, bt):
@@ -711,7 +762,8 @@ def main():
     secondary = {}
     if "decode" not in legs:
         # Secondary legs only (used for per-kernel counter runs); no headline line.
-        for name, fn in (("prefill", prefill_bench), ("hadamard", hadamard_bench),
+        for name, fn in (("decode_sizes", decode_sizes_bench),
+                         ("prefill", prefill_bench), ("hadamard", hadamard_bench),
                          ("block", block_bench), ("backward", backward_bench),
                          ("pack", pack_bench)):
             if name in legs:
@@ -728,7 +780,8 @@ def main():
     stream_ref = hbm_stream_reference(torch)
 
     if not args.no_secondary:
-        for name, fn in (("prefill", prefill_bench), ("hadamard", hadamard_bench),
+        for name, fn in (("decode_sizes", decode_sizes_bench),
+                         ("prefill", prefill_bench), ("hadamard", hadamard_bench),
                          ("block", block_bench), ("backward", backward_bench),
                          ("pack", pack_bench)):
             if name in legs:

@@ -214,6 +214,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     // follow once it is, so a wave's own token does not queue behind its
     // whole batch (measured: up to 13% per launch on the 7B / 8B shapes).
     constexpr int kEarlyRows = RB >= 4 ? 2 : 1;
+    // Two register sets with 6 or more chunks per lane: the second set is
+    // issued once the token's bf16 values are dead, so the prologue does not
+    // hold both sets, the token and the codes at once.
+    constexpr bool kLateSecondSet = MT * CH >= 6;
 
     uint32_t xv[MT][CH][16];  // codes of my chunks: chunk c covers x[64c .. 64c+63]
     int tok_sum[MT];
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
         }
         if constexpr (MULTI) {
             load(w0, 0);
-            load(w1, RB);
+            if constexpr (!kLateSecondSet) load(w1, RB);
         } else {
             load_rows(w0, 0, 0, kEarlyRows);
         }
@@ -343,6 +347,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
             part = wave_sum_dpp(part);
             if (lane == 0) red_i[tok][wave] = part;
         }
+        if constexpr (MULTI && kLateSecondSet) load(w1, RB);  // the bf16 token registers are free now
         __syncthreads();
 
         // 4. Codes of my chunks into registers (chunks past K read as zeros);
@@ -502,7 +507,11 @@ hipError_t launch_rb(const Args& a, int64_t rpw, int64_t waves, hipStream_t stre
         if (rpw <= 8) return launch_shape<MT, CH, NT, 8, false, FUSED>(a, waves, stream);
     if constexpr (CAP_MT >= 16)
         if (rpw <= 16) return launch_shape<MT, CH, NT, 16, false, FUSED>(a, waves, stream);
-    return launch_shape<MT, CH, NT, CAP_MT, true, FUSED>(a, waves, stream);
+    // Two alternating register sets: with 6 or more chunks per lane, two sets
+    // of two rows next to the codes exceed the register file (the compiler
+    // spilled 129 registers at 8 chunks), so each set holds one row.
+    constexpr int MRB = MT * CH >= 6 ? 1 : CAP_MT;
+    return launch_shape<MT, CH, NT, MRB, true, FUSED>(a, waves, stream);
 }
 
 template <int MT, int CH, bool FUSED>

@@ -172,6 +172,9 @@ FORWARD_FULL_CASES = [
     # GEMV (M <= 4)
     (1, 512, 256), (1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008), (2, 1000, 4096),
     (3, 77, 14336), (4, 4097, 8192), (1, 1, 64), (1, 130, 32768), (2, 9, 16384),
+    (1, 40000, 4096),    # 20 rows per wave: two alternating register sets
+    (2, 6000, 12288),    # 2 tokens x 3 chunks per lane: alternating one-row sets
+    (1, 8192, 28672),    # 7 chunks (run as 8), 4 rows per wave: alternating one-row sets
     # matrix-core GEMM
     (5, 512, 256), (16, 4096, 4096), (17, 1000, 4096), (64, 1024, 4096), (100, 333, 192),
     (128, 128, 128), (256, 1024, 4096), (300, 4099, 1024), (1, 70, 65536), (33, 65, 64),
@@ -297,6 +300,13 @@ FUSED_CASES = [
     (1, 14336, 4096, False), (1, 4096, 14336, False), (4, 300, 256, True),
     (5, 100, 1024, False), (64, 257, 4096, True),     # two-kernel path (M > 4)
     (2, 50, 32768, False),                             # M * K beyond the fused limit
+    # more rows per wave than one register set holds (two alternating sets):
+    (1, 40000, 4096, False),                           # 1 chunk per lane, 20 rows per wave
+    (1, 28672, 8192, False),                           # 2 chunks, 14 rows per wave
+    (1, 8192, 28672, True),                            # 7 chunks (run as 8), 4 rows per wave
+    (1, 20000, 16384, False),                          # 4 chunks, 10 rows per wave
+    (2, 6000, 12288, False),                           # 2 tokens x 3 chunks: one-row sets
+    (4, 9000, 8192, True),                             # 4 tokens x 2 chunks: one-row sets
 ]
 
 
