@@ -520,6 +520,16 @@ hipError_t launch_ch(const Args& a, hipStream_t stream) {
     // 512-thread workgroups (2048 waves) for single tokens and matrices larger
     // than 4096 x 4096: they halve each thread's share of the quantisation.
     if constexpr (MT == 1) {
+        // Two such workgroups per CU (4096 waves) for N >= 16384 when K <= 8192
+        // and a wave's rows fit one register set: those variants need at most
+        // ~128 registers, so both workgroups fit, and the second hides the
+        // first's prologue and reduction latency (measured: 8192 -> 28672
+        // 16.8 -> 13.8 us, 4096 -> 28672 8.9 -> 8.3 us; no gain below
+        // N = 16384).
+        if (CH <= 2 && N >= 16384 && N <= 4096 * max_batch<CH>()) {
+            const int64_t rpw = (N + 4095) / 4096;
+            return launch_rb<MT, CH, 512, FUSED>(a, rpw, (N + rpw - 1) / rpw, stream);
+        }
         if (N >= 4096 && (N > 4096 || a.K > 4096)) {
             const int64_t rpw = (N + 2047) / 2048;
             return launch_rb<MT, CH, 512, FUSED>(a, rpw, (N + rpw - 1) / rpw, stream);

@@ -172,7 +172,8 @@ FORWARD_FULL_CASES = [
     # GEMV (M <= 4)
     (1, 512, 256), (1, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008), (2, 1000, 4096),
     (3, 77, 14336), (4, 4097, 8192), (1, 1, 64), (1, 130, 32768), (2, 9, 16384),
-    (1, 40000, 4096),    # 20 rows per wave: two alternating register sets
+    (1, 40000, 4096),    # 10 rows per wave in 4096 waves
+    (1, 70000, 4096),    # 35 rows per wave: two alternating register sets
     (2, 6000, 12288),    # 2 tokens x 3 chunks per lane: alternating one-row sets
     (1, 8192, 28672),    # 7 chunks (run as 8), 4 rows per wave: alternating one-row sets
     # matrix-core GEMM
@@ -301,8 +302,10 @@ FUSED_CASES = [
     (5, 100, 1024, False), (64, 257, 4096, True),     # two-kernel path (M > 4)
     (2, 50, 32768, False),                             # M * K beyond the fused limit
     # more rows per wave than one register set holds (two alternating sets):
-    (1, 40000, 4096, False),                           # 1 chunk per lane, 20 rows per wave
-    (1, 28672, 8192, False),                           # 2 chunks, 14 rows per wave
+    (1, 40000, 4096, False),                           # 1 chunk per lane, 10 rows per wave (4096 waves)
+    (1, 70000, 4096, False),                           # 1 chunk, 35 rows per wave (2048 waves, two sets)
+    (1, 36000, 8192, True),                            # 2 chunks, 18 rows per wave (2048 waves, two sets)
+    (1, 28672, 8192, False),                           # 2 chunks, 7 rows per wave (4096 waves)
     (1, 8192, 28672, True),                            # 7 chunks (run as 8), 4 rows per wave
     (1, 20000, 16384, False),                          # 4 chunks, 10 rows per wave
     (2, 6000, 12288, False),                           # 2 tokens x 3 chunks: one-row sets

@@ -144,7 +144,8 @@ def _fused(dev, x, packed, ws):
 def test_decode_launch_shapes_agree(dev, K, Ns):
     # Rows of one packed matrix under different launch shapes: for K = 4096,
     # 256-thread groups with 4 rows per wave (N 4096), 512-thread groups with 4
-    # and 14 rows per wave (N 8192, 28672); for K = 11008 (3 chunks per lane)
+    # rows per wave (N 8192) and, two per CU, 7 rows per wave (N 28672); for
+    # K = 11008 (3 chunks per lane)
     # 256-thread groups (N 1024), 512-thread groups with 2 and 4 rows per wave,
     # and 5 rows per wave in two alternating register sets (N 10240).  The
     # first 1024 rows must come out the same every time.
