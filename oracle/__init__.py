@@ -66,6 +66,10 @@ def load(path: str):
     lib.oracle_linear_backward_weight.restype = i32
     lib.oracle_rmsnorm_backward.argtypes = [p, p, f32, p, i64, i64, p, p]
     lib.oracle_rmsnorm_backward.restype = i32
+    lib.oracle_pack_base3.argtypes = [p, i64, i64, i64, p]
+    lib.oracle_pack_base3.restype = i32
+    lib.oracle_unpack_base3.argtypes = [p, i64, i64, i64, p]
+    lib.oracle_unpack_base3.restype = i64
     return lib
 
 
@@ -227,6 +231,24 @@ class Oracle:
         return gx, gg
 
 
+    def pack_base3(self, q: np.ndarray, row_bytes: int) -> np.ndarray:
+        """Ternary codes int8 [N][K] -> base-3 packed uint8 [N][row_bytes], five
+        weights per byte (byte j = sum_i (q[5j+i] + 1) 3^i)."""
+        q = _c(q, np.int8)
+        N, K = q.shape
+        out = np.empty((N, row_bytes), np.uint8)
+        if self.lib.oracle_pack_base3(_ptr(q), N, K, row_bytes, _ptr(out)) != 0:
+            raise ValueError(f"oracle_pack_base3 rejected K={K} row_bytes={row_bytes} or a code")
+        return out
+
+    def unpack_base3(self, packed3: np.ndarray, K: int):
+        """(codes int8 [N][K], count of bytes above 242) of a base-3 packing."""
+        packed3 = _c(packed3, np.uint8)
+        N, row_bytes = packed3.shape
+        q = np.empty((N, K), np.int8)
+        bad = self.lib.oracle_unpack_base3(_ptr(packed3), N, K, row_bytes, _ptr(q))
+        return q, int(bad)
+
 _DEFAULT = None
 
 
@@ -236,3 +258,4 @@ def default() -> Oracle:
     if _DEFAULT is None:
         _DEFAULT = Oracle()
     return _DEFAULT
+

@@ -493,3 +493,61 @@ int oracle_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, con
     free(r);
     return 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* Base-3 packing ([QP] "1.58비트는 어디서 나온거에요?": a ternary weight    */
+/* carries log2 3 = 1.58 bits, so five of them fit one byte, 3^5 = 243).     */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * Ternary codes q [N][K] in {-1, 0, 1} -> packed3 [N][row_bytes]: byte j of a
+ * row holds the weights 5j .. 5j+4 as the base-3 number
+ *   c_0 + 3 c_1 + 9 c_2 + 27 c_3 + 81 c_4,   c_i = q[5j + i] + 1 in {0, 1, 2},
+ * so every byte is at most 242.  Weights past K count as c = 0, and bytes past
+ * ceil(K / 5) are zero.  row_bytes must hold ceil(K / 5) bytes.  Returns -1 on
+ * a bad argument or a code outside {-1, 0, 1}.
+ */
+int oracle_pack_base3(const int8_t* q, int64_t N, int64_t K, int64_t row_bytes, uint8_t* packed3) {
+    if (N < 0 || K < 1 || row_bytes < (K + 4) / 5) return -1;
+    int bad = 0;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t j = 0; j < row_bytes; j++) {
+            int byte = 0, place = 1;
+            for (int i = 0; i < 5; i++) {
+                const int64_t k = 5 * j + i;
+                int c = 0;
+                if (k < K) {
+                    const int v = q[n * K + k];
+                    if (v < -1 || v > 1) bad = 1;
+                    c = v + 1;
+                }
+                byte += c * place;
+                place *= 3;
+            }
+            packed3[n * row_bytes + j] = (uint8_t)byte;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * The inverse: the base-3 digits of each byte, c_i = (byte / 3^i) mod 3, back
+ * to q = c - 1 for the K weights of each row.  Returns the number of bytes
+ * above 242 (not base-3 packings of five digits); their digits are still
+ * decoded.
+ */
+int64_t oracle_unpack_base3(const uint8_t* packed3, int64_t N, int64_t K, int64_t row_bytes, int8_t* q) {
+    int64_t bad = 0;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t j = 0; j < row_bytes; j++) {
+            int byte = packed3[n * row_bytes + j];
+            if (byte > 242) bad++;
+            for (int i = 0; i < 5; i++) {
+                const int64_t k = 5 * j + i;
+                if (k < K) q[n * K + k] = (int8_t)(byte % 3 - 1);
+                byte /= 3;
+            }
+        }
+    }
+    return bad;
+}
