@@ -18,6 +18,7 @@ import os
 
 __all__ = [
     "BitnetError", "lib", "library_path", "pack_weights", "pack_weights_workspace_bytes",
+    "base3_row_bytes", "pack_base3", "linear_forward_base3",
     "quant_act", "hadamard_quant_act", "linear_forward", "bitlinear", "bitlinear_forward",
     "BitLinear",
     "STATUS", "set_kernel_events",
@@ -95,6 +96,12 @@ def lib() -> ctypes.CDLL:
     L.bitnet_version.restype = i32
     L.bitnet_set_kernel_events.argtypes = [p, p]
     L.bitnet_set_kernel_events.restype = i32
+    L.bitnet_base3_row_bytes.argtypes = [i64]
+    L.bitnet_base3_row_bytes.restype = sz
+    L.bitnet_pack_base3.argtypes = [p, i64, i64, p, p]
+    L.bitnet_pack_base3.restype = i32
+    L.bitnet_linear_forward_base3.argtypes = [p, p, p, p, p, i64, i64, i64, p, p, p]
+    L.bitnet_linear_forward_base3.restype = i32
     _LIB = L
     return L
 
@@ -405,6 +412,45 @@ def bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5, out=None
 
 
 # --- backward under the straight-through estimator ------------------------
+
+def base3_row_bytes(K: int) -> int:
+    """Bytes per row of the base-3 packing (five weights per byte, rows padded to 16)."""
+    return int(lib().bitnet_base3_row_bytes(K))
+
+
+def pack_base3(packed, K: int, out=None):
+    """2-bit packed uint8 [N][K/4] -> base-3 packed uint8 [N][base3_row_bytes(K)] (bitnet_pack_base3)."""
+    torch = _torch()
+    _require(packed, "packed", torch.uint8, 2)
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}]")
+    rb = base3_row_bytes(K)
+    if out is None:
+        out = torch.empty((N, rb), dtype=torch.uint8, device=packed.device)
+    _check(lib().bitnet_pack_base3(_ptr(packed), N, K, _ptr(out), _stream(packed.device)))
+    return out
+
+
+def linear_forward_base3(xq, x_scale, x_qsum, packed3, w_scale, return_acc: bool = False, out=None):
+    """One token on base-3 packed weights (bitnet_linear_forward_base3): y float32 [1][N]."""
+    torch = _torch()
+    _require(xq, "xq", torch.int8, 2)
+    _require(x_scale, "x_scale", torch.float32, 1)
+    _require(x_qsum, "x_qsum", torch.int32, 1)
+    _require(packed3, "packed3", torch.uint8, 2)
+    _require(w_scale, "w_scale", torch.float32, 1)
+    M, K = xq.shape
+    N = packed3.shape[0]
+    if packed3.shape[1] != base3_row_bytes(K):
+        raise ValueError(f"packed3 is [{N}][{packed3.shape[1]}], expected [{N}][{base3_row_bytes(K)}] for K={K}")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if return_acc else None
+    _check(lib().bitnet_linear_forward_base3(_ptr(xq), _ptr(x_scale), _ptr(x_qsum), _ptr(packed3),
+                                             _ptr(w_scale), M, N, K, _ptr(y), _ptr(acc),
+                                             _stream(xq.device)))
+    return (y, acc) if return_acc else y
+
 
 def transpose_packed(packed, K: int, out=None):
     """packed uint8 [N][K/4] -> packed_t uint8 [K][N/4] (bitnet_transpose_packed)."""

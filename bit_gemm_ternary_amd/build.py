@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libbitnet_hip.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "pack.hip", "quant_act.hip", "hadamard_quant.hip", "gemv.hip", "gemm_mfma.hip",
-           "backward.hip"]
+           "backward.hip", "base3.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -423,4 +423,47 @@ const char* bitnet_last_error(void) { return g_last_error; }
 
 int bitnet_version(void) { return BITNET_ABI_VERSION; }
 
+size_t bitnet_base3_row_bytes(int64_t K) {
+    if (K < kMinK || K > kMaxK || K % 64 != 0) return 0;
+    return (size_t)bitnet::base3_row_bytes(K);
+}
+
+int bitnet_pack_base3(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed3, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_pack_base3";
+    if (N < 0 || N > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (N == 0) return BITNET_OK;
+    if (!packed || !packed3) return fail(BITNET_ERR_NULL, "%s: packed and packed3 must not be NULL", fn);
+    if (!aligned(packed, 16) || !aligned(packed3, 16))
+        return fail(BITNET_ERR_ALIGN, "%s: packed and packed3 must be 16-byte aligned", fn);
+    return hip_status(bitnet::launch_pack_base3(packed, N, K, packed3, (hipStream_t)stream), fn);
+}
+
+int bitnet_linear_forward_base3(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
+                                const uint8_t* packed3, const float* w_scale, int64_t M, int64_t N, int64_t K,
+                                float* y, int32_t* acc, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_linear_forward_base3";
+    if (M < 0 || N < 0 || N > kMaxRows)
+        return fail(BITNET_ERR_SHAPE, "%s: M=%lld or N=%lld out of range", fn, (long long)M, (long long)N);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (M > 1) return fail(BITNET_ERR_UNSUPPORTED, "%s: one token (M = 1) only, got M=%lld", fn, (long long)M);
+    if (!bitnet::base3_gemv_supported(K))
+        return fail(BITNET_ERR_UNSUPPORTED, "%s: K=%lld above 20480", fn, (long long)K);
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!xq || !x_scale || !x_qsum || !packed3 || !w_scale || !y)
+        return fail(BITNET_ERR_NULL, "%s: only acc may be NULL", fn);
+    if (!aligned(xq, 16) || !aligned(packed3, 16))
+        return fail(BITNET_ERR_ALIGN, "%s: xq and packed3 must be 16-byte aligned", fn);
+    if (!aligned(x_scale, 4) || !aligned(x_qsum, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+        (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "%s: scales, sums, y and acc must be 4-byte aligned", fn);
+    return hip_status(bitnet::launch_base3_gemv(xq, x_scale, x_qsum, packed3, w_scale, N, K, y, acc,
+                                                (hipStream_t)stream),
+                      fn);
+}
+
 }  // extern "C"

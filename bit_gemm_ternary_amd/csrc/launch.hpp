@@ -109,6 +109,15 @@ hipError_t launch_gemm_f6(const uint8_t* xq6, const float* x_scale, const int32_
 // --- backward under the straight-through estimator (backward.hip) --------
 // p[0 .. count) = 0 by a kernel (no memset node if the caller captures a graph).
 hipError_t launch_zero_f32(float* p, int64_t count, hipStream_t stream);
+
+// Base-3 packing (five ternary weights per byte) and its one-token GEMV.
+constexpr int kBase3MaxChunks = 4;  // 16-byte chunks per lane: K <= 4 * 64 * 80 = 20480
+int64_t base3_row_bytes(int64_t K);
+bool base3_gemv_supported(int64_t K);
+hipError_t launch_pack_base3(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed3, hipStream_t stream);
+hipError_t launch_base3_gemv(const int8_t* xq, const float* x_scale, const int32_t* x_qsum, const uint8_t* packed3,
+                             const float* w_scale, int64_t N, int64_t K, float* y, int32_t* acc,
+                             hipStream_t stream);
 // packed [N][K/4] -> packed_t [K][N/4] (N, K multiples of 64).
 hipError_t launch_transpose_packed(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed_t,
                                    hipStream_t stream);

@@ -332,6 +332,33 @@ int bitnet_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, con
                             size_t workspace_bytes, void* stream);
 
 /*
+ * Base-3 packing ("1.58 bits" per weight: a ternary weight carries log2 3 bits,
+ * primer on 1.58-bit quantisation, section "1.58비트는 어디서 나온거에요?"):
+ * five weights per byte, byte j of a row = c_0 + 3 c_1 + 9 c_2 + 27 c_3 + 81 c_4
+ * with c_i = q[5j + i] + 1 (weights past K count as 0), rows padded with zero
+ * bytes to bitnet_base3_row_bytes(K) = ceil(ceil(K / 5) / 16) * 16 bytes
+ * (0 for an invalid K): 1.6 bits per weight.
+ */
+size_t bitnet_base3_row_bytes(int64_t K);
+
+/*
+ * Repack 2-bit packed weights (bitnet_pack_weights, [N][K/4], 16-byte aligned)
+ * into the base-3 layout packed3 [N][bitnet_base3_row_bytes(K)] (16-byte
+ * aligned); d_w and s_w are unchanged.  Same N and K rules as the packing.
+ */
+int bitnet_pack_base3(const uint8_t* packed, int64_t N, int64_t K, uint8_t* packed3, void* stream);
+
+/*
+ * bitnet_linear_forward for one token on base-3 packed weights: the same
+ * codes, int32 accumulators and outputs as bitnet_linear_forward on the 2-bit
+ * packing they came from.  M must be 0 or 1 and K at most 20480
+ * (BITNET_ERR_UNSUPPORTED otherwise); xq and packed3 16-byte aligned.
+ */
+int bitnet_linear_forward_base3(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
+                                const uint8_t* packed3, const float* w_scale, int64_t M, int64_t N,
+                                int64_t K, float* y, int32_t* acc, void* stream);
+
+/*
  * Profiling hook: arm two hipEvent_t (passed as void*; either may be NULL) for
  * the first kernel the next bitnet_* call on this thread launches (the
  * contraction kernel of bitnet_linear_forward, the quantisation kernel of the
