@@ -27,6 +27,8 @@ not Python launch overhead.
                    projections (8192 x 8192 up to 16384 x 53248), launched back to
                    back like roofline.per_launch: per-launch time and GB/s once the
                    launch's fixed cost is spread over 17-218 MB of packed weights
+  base3            context: the one-token contraction on base-3 packed weights (five
+                   per byte, 1.6 bits) against the 2-bit packing, codes precomputed
   prefill          W1.58A8 prefill M=2048, K=4096, N=14336: int8 TOPS of the
                    matrix-core GEMM against the dense int8 peak, and against that
                    peak scaled to the engine clock measured during the kernel
@@ -97,7 +99,7 @@ def parse_args():
     ap.add_argument("--block-steps", type=int, default=200, help="timed steps per token count of the block leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES, ten times (HBM counter calibration)")
-    ap.add_argument("--legs", default="decode,decode_sizes,prefill,hadamard,block,backward,pack",
+    ap.add_argument("--legs", default="decode,decode_sizes,base3,prefill,hadamard,block,backward,pack",
                     help="comma-separated legs to run (the headline needs decode)")
     ap.add_argument("--cpu-one-core-seconds", type=float, default=5.0,
                     help="wall time budget of the one-core CPU-oracle sample")
@@ -412,6 +414,52 @@ def decode_sizes_bench(args, dev, bt, torch, synth):
         torch.cuda.empty_cache()
     return {"what": "fused decode kernel, M = 1, larger projections (context for the headline, "
                     "which runs the 7B shapes)", "by_shape": rows}
+
+
+def base3_bench(args, dev, bt, torch, synth):
+    """Base-3 packing (five weights per byte) against the 2-bit packing on the
+    same one-token contraction (codes precomputed, no fused quantisation in
+    either): per-launch time back to back over >= 1 GiB of rotating copies."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6161)
+    rows = []
+    for K, N in [(4096, 4096), (4096, 11008), (11008, 4096), (8192, 28672), (16384, 53248)]:
+        W = torch.randn((N, K), generator=gen, device=dev) * 0.02
+        packed, w_scale = bt.pack_weights(W)
+        del W
+        p3 = bt.pack_base3(packed, K)
+        x = torch.randn((1, K), generator=gen, device=dev).to(torch.bfloat16)
+        q, dx, qs = bt.quant_act(x)
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        row = {"K": K, "N": N}
+        for name, base, fwd in (
+                ("two_bit", packed, lambda w: bt.linear_forward(q, dx, qs, w, w_scale, out=y)),
+                ("base3", p3, lambda w: bt.linear_forward_base3(q, dx, qs, w, w_scale, out=y))):
+            nbytes = base.numel()
+            copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+            own = [base] + [base.clone() for _ in range(copies - 1)]
+
+            def one(r, own=own, fwd=fwd):
+                fwd(own[r])
+
+            for r in range(copies):
+                one(r)
+            torch.cuda.synchronize()
+            run = graph_runner(one, copies, args.eager, torch)
+            launches = max(1, min(3 * args.steps, 3000) // copies) * copies
+            ms, _ = timed(run, launches, torch)
+            us = ms * 1e3
+            row[name] = {"packed_MB": round(nbytes / 1e6, 2), "avg_us": round(us, 2),
+                         "GB_s": round(nbytes / us / 1e3, 1), "Gweights_s": round(N * K / us / 1e3, 1)}
+            del run, own, one
+            torch.cuda.empty_cache()
+        row["base3_speedup"] = round(row["two_bit"]["avg_us"] / row["base3"]["avg_us"], 3)
+        rows.append(row)
+        del packed, p3, x, q, dx, qs, y
+        torch.cuda.empty_cache()
+    return {"what": "one-token contraction, codes precomputed: 2-bit packing (bitnet_linear_forward) "
+                    "against base-3 packing (bitnet_linear_forward_base3), 1.6 instead of 2 bits per weight",
+            "by_shape": rows}
 
 
 def time_launches(fn, iters, bt):
@@ -762,7 +810,7 @@ def main():
     secondary = {}
     if "decode" not in legs:
         # Secondary legs only (used for per-kernel counter runs); no headline line.
-        for name, fn in (("decode_sizes", decode_sizes_bench),
+        for name, fn in (("decode_sizes", decode_sizes_bench), ("base3", base3_bench),
                          ("prefill", prefill_bench), ("hadamard", hadamard_bench),
                          ("block", block_bench), ("backward", backward_bench),
                          ("pack", pack_bench)):
@@ -780,7 +828,7 @@ def main():
     stream_ref = hbm_stream_reference(torch)
 
     if not args.no_secondary:
-        for name, fn in (("decode_sizes", decode_sizes_bench),
+        for name, fn in (("decode_sizes", decode_sizes_bench), ("base3", base3_bench),
                          ("prefill", prefill_bench), ("hadamard", hadamard_bench),
                          ("block", block_bench), ("backward", backward_bench),
                          ("pack", pack_bench)):
