@@ -254,3 +254,31 @@ def test_backward_argument_errors(L):
     assert rb(gg=A4) == 5
     assert rb(gg=A4, ws=A4, wsb=L.bitnet_rmsnorm_backward_workspace_bytes(8, 256)) == 4
     assert L.bitnet_rmsnorm_backward_workspace_bytes(8, 256) == 32 * 8 + 1 * 256 * 8
+
+
+def test_base3_argument_errors(L):
+    p = ctypes.c_void_p
+    # row bytes: ceil(K / 5) rounded up to 16; 0 for an invalid K
+    assert L.bitnet_base3_row_bytes(64) == 16
+    assert L.bitnet_base3_row_bytes(4096) == 832
+    assert L.bitnet_base3_row_bytes(11008) == 2208
+    assert L.bitnet_base3_row_bytes(100) == 0
+    assert L.bitnet_base3_row_bytes(0) == 0
+    # repack: K rules of the packing, pointers 16-byte aligned
+    assert L.bitnet_pack_base3(p(A16), 8, 96, p(A16), None) == 2
+    assert L.bitnet_pack_base3(p(A16), -1, 256, p(A16), None) == 2
+    assert L.bitnet_pack_base3(None, 8, 256, p(A16), None) == 1
+    assert L.bitnet_pack_base3(p(A16), 8, 256, p(A4), None) == 4
+    assert L.bitnet_pack_base3(None, 0, 256, None, None) == 0          # nothing to pack
+    # one-token contraction
+    f = lambda xq=A16, sx=A4, qs=A4, p3=A16, ws=A4, M=1, N=8, K=256, y=A4, acc=None: \
+        L.bitnet_linear_forward_base3(p(xq), p(sx), p(qs), p(p3), p(ws), M, N, K, p(y),
+                                      None if acc is None else p(acc), None)
+    assert f(M=2) == 3                       # one token only
+    assert f(K=20544) == 3                   # above 20480
+    assert f(K=100) == 2
+    assert f(N=-1) == 2
+    assert f(xq=0) == 1
+    assert f(p3=A4) == 4
+    assert f(y=BAD) == 4
+    assert f(M=0, xq=0, p3=0) == 0           # empty batch: nothing enqueued
