@@ -26,11 +26,12 @@ namespace bitnet {
 namespace {
 
 constexpr int kB3Threads = 256;
-// Two rows in flight per wave over up to 4096 waves: measured 10-15% faster on
-// the 4096- and 11008-wide decode shapes than four rows over 2048 waves (and
-// 2% slower on a 218 MB matrix); eight rows per wave were slower still.
-constexpr int kB3Batch = 2;                      // rows in flight per wave
-constexpr int kB3MaxWaves = 4096;
+// One row in flight per wave over up to 8192 waves: measured 3-5% faster than
+// two rows over 4096 waves and 12-16% faster than four over 2048 on the 4096-
+// and 11008-wide decode shapes and on a 218 MB matrix; eight rows per wave
+// were slower still.
+constexpr int kB3Batch = 1;                      // rows in flight per wave
+constexpr int kB3MaxWaves = 8192;
 constexpr uint32_t kB3Word3 = 0x00020000u;       // raw buffer descriptor word 3 (gfx9 family)
 constexpr uint32_t kB3OutOfRange = 0x80000000u;  // offset past every buffer here: loads 0
 
