@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.bitnet_last_error.restype = ctypes.c_char_p
     L.bitnet_version.argtypes = []
     L.bitnet_version.restype = i32
+    L.bitnet_stream_read.argtypes = [p, sz, p, p]
+    L.bitnet_stream_read.restype = i32
     L.bitnet_set_kernel_events.argtypes = [p, p]
     L.bitnet_set_kernel_events.restype = i32
     L.bitnet_base3_row_bytes.argtypes = [i64]
@@ -125,7 +127,7 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _require(t, name, dtype, ndim):
+def _require(t, name, dtype, ndim, device=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -133,10 +135,62 @@ def _require(t, name, dtype, ndim):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _require_shape(t, name, dtype, shape, device=None):
+    """t is a contiguous device tensor of exactly this dtype and shape."""
+    _require(t, name, dtype, len(shape), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+
+
+def _require_at_least(t, name, dtype, n, device=None):
+    """t is a contiguous 1-D device tensor of this dtype with at least n entries."""
+    _require(t, name, dtype, 1, device)
+    if t.shape[0] < n:
+        raise ValueError(f"{name} needs at least {n} entries, got {t.shape[0]}")
+
+
+def _gain(gain, K, device):
+    if gain is not None:
+        _require_shape(gain, "gain", _torch().float32, (K,), device)
+
+
+def _output(t, name, dtype, shape, device):
+    """A caller-supplied output checked against its shape, or a new one."""
+    if t is None:
+        return _torch().empty(shape, dtype=dtype, device=device)
+    _require_shape(t, name, dtype, shape, device)
+    return t
+
+
+def _codes(codes, M, K, device):
+    """(xq int8 [M][K], x_scale float32 [M], x_qsum int32 [M]), given or new."""
+    torch = _torch()
+    if codes is None:
+        codes = (None, None, None)
+    xq, x_scale, x_qsum = codes
+    return (_output(xq, "xq", torch.int8, (M, K), device),
+            _output(x_scale, "x_scale", torch.float32, (M,), device),
+            _output(x_qsum, "x_qsum", torch.int32, (M,), device))
+
+
+def stream_read(buf, sink) -> None:
+    """One plain read of every byte of the device tensor ``buf`` (bitnet_stream_read),
+    the measurement reference for bandwidth-bound kernels; ``sink`` is an int32
+    device tensor of at least one element."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _require_at_least(sink, "sink", torch.int32, 1, buf.device)
+    _check(lib().bitnet_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                    _stream(buf.device)))
 
 
 def set_kernel_events(start_event, stop_event) -> None:
@@ -157,23 +211,18 @@ def pack_weights(W, hadamard: bool = False, out=None, workspace=None):
     torch = _torch()
     _require(W, "W", torch.float32, 2)
     N, K = W.shape
-    if out is None:
-        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
-        w_scale = torch.empty(2, dtype=torch.float32, device=W.device)
-    else:
-        packed, w_scale = out
-        _require(packed, "packed", torch.uint8, 2)
-        _require(w_scale, "w_scale", torch.float32, 1)
-        if tuple(packed.shape) != (N, K // 4) or w_scale.shape[0] < 2:
-            raise ValueError(f"out must be (uint8 [{N}][{K // 4}], float32 [2])")
+    dev = W.device
+    packed, w_scale = (None, None) if out is None else out
+    packed = _output(packed, "packed", torch.uint8, (N, K // 4), dev)
+    w_scale = _output(w_scale, "w_scale", torch.float32, (2,), dev)
     if workspace is None:
         ws_bytes = pack_weights_workspace_bytes(N, K, hadamard)
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=W.device)
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     else:
-        _require(workspace, "workspace", torch.uint8, 1)
+        _require(workspace, "workspace", torch.uint8, 1, dev)
     _check(lib().bitnet_pack_weights(_ptr(W), N, K, int(bool(hadamard)), _ptr(packed),
                                      _ptr(w_scale), _ptr(workspace), workspace.numel(),
-                                     _stream(W.device)))
+                                     _stream(dev)))
     return packed, w_scale
 
 
@@ -187,6 +236,8 @@ def pack_weights_grouped(Ws, hadamard: bool = False):
     torch = _torch()
     if not 1 <= len(Ws) <= 8:
         raise ValueError("between 1 and 8 weight matrices")
+    for W in Ws:
+        _require(W, "W", torch.float32, 2, Ws[0].device)
     K = Ws[0].shape[1]
     rows = [int(W.shape[0]) for W in Ws]
     dev = Ws[0].device
@@ -194,7 +245,6 @@ def pack_weights_grouped(Ws, hadamard: bool = False):
     w_scales = torch.empty((len(Ws), 2), dtype=torch.float32, device=dev)
     r0 = 0
     for g, W in enumerate(Ws):
-        _require(W, "W", torch.float32, 2)
         if W.shape[1] != K:
             raise ValueError("all grouped matrices need the same K")
         N = rows[g]
@@ -214,36 +264,24 @@ def bitlinear_forward_grouped(x, packed, w_scales, group_rows, gain=None, eps: f
     y float32 [M][sum(group_rows)].  Arguments otherwise as bitlinear_forward."""
     torch = _torch()
     _require(x, "x", torch.bfloat16, 2)
-    _require(packed, "packed", torch.uint8, 2)
-    _require(w_scales, "w_scales", torch.float32, 2)
+    dev = x.device
     M, K = x.shape
     rows = [int(r) for r in group_rows]
+    if not 1 <= len(rows) <= 8 or min(rows) < 1:
+        raise ValueError("between 1 and 8 groups, each of at least one row")
     N = sum(rows)
-    if packed.shape[0] != N or packed.shape[1] * 4 != K:
-        raise ValueError(f"packed is {list(packed.shape)}, expected [{N}][{K // 4}]")
-    if tuple(w_scales.shape) != (len(rows), 2):
-        raise ValueError(f"w_scales must be [{len(rows)}][2]")
-    if gain is not None:
-        _require(gain, "gain", torch.float32, 1)
-    if codes is None:
-        codes = (torch.empty((M, K), dtype=torch.int8, device=x.device),
-                 torch.empty(M, dtype=torch.float32, device=x.device),
-                 torch.empty(M, dtype=torch.int32, device=x.device))
-    xq, x_scale, x_qsum = codes
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _require(out, "out", torch.float32, 2)
-    if tuple(out.shape) != (M, N):
-        raise ValueError(f"out must be [{M}][{N}]")
+    _require_shape(packed, "packed", torch.uint8, (N, K // 4), dev)
+    _require_shape(w_scales, "w_scales", torch.float32, (len(rows), 2), dev)
+    _gain(gain, K, dev)
+    xq, x_scale, x_qsum = _codes(codes, M, K, dev)
+    out = _output(out, "out", torch.float32, (M, N), dev)
     if acc_out is not None:
-        _require(acc_out, "acc_out", torch.int32, 2)
-        if tuple(acc_out.shape) != (M, N):
-            raise ValueError(f"acc_out must be [{M}][{N}]")
+        _require_shape(acc_out, "acc_out", torch.int32, (M, N), dev)
     rows_c = (ctypes.c_int64 * len(rows))(*rows)
     _check(lib().bitnet_bitlinear_forward_grouped(
         _ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(packed), _ptr(w_scales),
         ctypes.cast(rows_c, ctypes.c_void_p), len(rows),
-        M, K, _ptr(xq), _ptr(x_scale), _ptr(x_qsum), _ptr(out), _ptr(acc_out), _stream(x.device)))
+        M, K, _ptr(xq), _ptr(x_scale), _ptr(x_qsum), _ptr(out), _ptr(acc_out), _stream(dev)))
     return (out, acc_out) if acc_out is not None else out
 
 
@@ -251,21 +289,8 @@ def _quant(name, x, gain, eps, out):
     torch = _torch()
     _require(x, "x", torch.bfloat16, 2)
     M, K = x.shape
-    if gain is not None:
-        _require(gain, "gain", torch.float32, 1)
-        if gain.shape[0] != K:
-            raise ValueError(f"gain has {gain.shape[0]} entries, x has K={K}")
-    if out is None:
-        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
-        x_scale = torch.empty(M, dtype=torch.float32, device=x.device)
-        x_qsum = torch.empty(M, dtype=torch.int32, device=x.device)
-    else:
-        xq, x_scale, x_qsum = out
-        _require(xq, "xq", torch.int8, 2)
-        _require(x_scale, "x_scale", torch.float32, 1)
-        _require(x_qsum, "x_qsum", torch.int32, 1)
-        if tuple(xq.shape) != (M, K) or x_scale.shape[0] != M or x_qsum.shape[0] != M:
-            raise ValueError("out tensors do not match x")
+    _gain(gain, K, x.device)
+    xq, x_scale, x_qsum = _codes(out, M, K, x.device)
     _check(getattr(lib(), name)(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K, _ptr(xq),
                                 _ptr(x_scale), _ptr(x_qsum), _stream(x.device)))
     return xq, x_scale, x_qsum
@@ -289,43 +314,48 @@ def hadamard_quant_act_f6(x, gain=None, eps: float = 1e-5, out=None):
     x_qsum int32 [M]) (bitnet_hadamard_quant_act_f6)."""
     torch = _torch()
     _require(x, "x", torch.bfloat16, 2)
+    dev = x.device
     M, K = x.shape
-    if gain is not None:
-        _require(gain, "gain", torch.float32, 1)
-    if out is None:
-        out = (torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=x.device),
-               torch.empty(M, dtype=torch.float32, device=x.device),
-               torch.empty(M, dtype=torch.int32, device=x.device))
-    xq6, x_scale, x_qsum = out
-    _require(xq6, "xq6", torch.uint8, 2)
-    if tuple(xq6.shape) != (M, K // 4 * 3):
-        raise ValueError(f"xq6 must be [{M}][{K // 4 * 3}]")
+    _gain(gain, K, dev)
+    xq6, x_scale, x_qsum = (None, None, None) if out is None else out
+    xq6 = _output(xq6, "xq6", torch.uint8, (M, K // 4 * 3), dev)
+    x_scale = _output(x_scale, "x_scale", torch.float32, (M,), dev)
+    x_qsum = _output(x_qsum, "x_qsum", torch.int32, (M,), dev)
     _check(lib().bitnet_hadamard_quant_act_f6(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K,
-                                              _ptr(xq6), _ptr(x_scale), _ptr(x_qsum),
-                                              _stream(x.device)))
+                                              _ptr(xq6), _ptr(x_scale), _ptr(x_qsum), _stream(dev)))
     return xq6, x_scale, x_qsum
+
+
+def _contraction_args(x_scale, x_qsum, packed, w_scale, M, K, dev):
+    torch = _torch()
+    _require_shape(x_scale, "x_scale", torch.float32, (M,), dev)
+    _require_shape(x_qsum, "x_qsum", torch.int32, (M,), dev)
+    _require(packed, "packed", torch.uint8, 2, dev)
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}] for K={K}")
+    _require_at_least(w_scale, "w_scale", torch.float32, 1, dev)
+    return N
 
 
 def linear_forward_f6(xq6, x_scale, x_qsum, packed, w_scale, return_acc: bool = False, out=None,
                       acc_out=None):
     """FP4 x FP6 contraction + dequantisation (bitnet_linear_forward_f6); returns y
-    float32 [M][N], or (y, acc int32 [M][N]) when return_acc."""
+    float32 [M][N], or (y, acc int32 [M][N]) when return_acc or acc_out is given."""
     torch = _torch()
     _require(xq6, "xq6", torch.uint8, 2)
-    _require(packed, "packed", torch.uint8, 2)
-    _require(w_scale, "w_scale", torch.float32, 1)
+    dev = xq6.device
     M = xq6.shape[0]
+    if xq6.shape[1] % 3 != 0:
+        raise ValueError(f"xq6 rows hold 24 bytes per 32 values, got {xq6.shape[1]} bytes")
     K = xq6.shape[1] // 3 * 4
-    N = packed.shape[0]
-    if packed.shape[1] * 4 != K:
-        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}]")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=xq6.device)
-    if return_acc and acc_out is None:
-        acc_out = torch.empty((M, N), dtype=torch.int32, device=xq6.device)
+    N = _contraction_args(x_scale, x_qsum, packed, w_scale, M, K, dev)
+    out = _output(out, "out", torch.float32, (M, N), dev)
+    if return_acc or acc_out is not None:
+        acc_out = _output(acc_out, "acc_out", torch.int32, (M, N), dev)
     _check(lib().bitnet_linear_forward_f6(_ptr(xq6), _ptr(x_scale), _ptr(x_qsum), _ptr(packed),
                                           _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out),
-                                          _stream(xq6.device)))
+                                          _stream(dev)))
     return (out, acc_out) if acc_out is not None else out
 
 
@@ -337,34 +367,16 @@ def linear_forward(xq, x_scale, x_qsum, packed, w_scale, return_acc: bool = Fals
     """
     torch = _torch()
     _require(xq, "xq", torch.int8, 2)
-    _require(x_scale, "x_scale", torch.float32, 1)
-    _require(x_qsum, "x_qsum", torch.int32, 1)
-    _require(packed, "packed", torch.uint8, 2)
-    _require(w_scale, "w_scale", torch.float32, 1)
+    dev = xq.device
     M, K = xq.shape
-    N = packed.shape[0]
-    if packed.shape[1] * 4 != K:
-        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}] for K={K}")
-    if x_scale.shape[0] != M or x_qsum.shape[0] != M or w_scale.shape[0] < 1:
-        raise ValueError("x_scale / x_qsum must have M entries and w_scale at least one")
-    if out is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
-    else:
-        _require(out, "out", torch.float32, 2)
-        if tuple(out.shape) != (M, N):
-            raise ValueError(f"out must be [{M}][{N}]")
-        y = out
+    N = _contraction_args(x_scale, x_qsum, packed, w_scale, M, K, dev)
+    y = _output(out, "out", torch.float32, (M, N), dev)
     acc = acc_out
-    if acc is not None:
-        _require(acc, "acc_out", torch.int32, 2)
-        if tuple(acc.shape) != (M, N):
-            raise ValueError(f"acc_out must be [{M}][{N}]")
-    elif return_acc:
-        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    if return_acc or acc_out is not None:
+        acc = _output(acc_out, "acc_out", torch.int32, (M, N), dev)
     _check(lib().bitnet_linear_forward(_ptr(xq), _ptr(x_scale), _ptr(x_qsum), _ptr(packed),
-                                       _ptr(w_scale), M, N, K, _ptr(y), _ptr(acc),
-                                       _stream(xq.device)))
-    return (y, acc) if (return_acc or acc_out is not None) else y
+                                       _ptr(w_scale), M, N, K, _ptr(y), _ptr(acc), _stream(dev)))
+    return (y, acc) if acc is not None else y
 
 
 def bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5, out=None, codes=None,
@@ -377,41 +389,25 @@ def bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5, out=None
     """
     torch = _torch()
     _require(x, "x", torch.bfloat16, 2)
-    _require(packed, "packed", torch.uint8, 2)
-    _require(w_scale, "w_scale", torch.float32, 1)
+    dev = x.device
     M, K = x.shape
+    _require(packed, "packed", torch.uint8, 2, dev)
     N = packed.shape[0]
     if packed.shape[1] * 4 != K:
         raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}] for K={K}")
-    if gain is not None:
-        _require(gain, "gain", torch.float32, 1)
-    if codes is None:
-        codes = (torch.empty((M, K), dtype=torch.int8, device=x.device),
-                 torch.empty(M, dtype=torch.float32, device=x.device),
-                 torch.empty(M, dtype=torch.int32, device=x.device))
-    xq, x_scale, x_qsum = codes
-    _require(xq, "xq", torch.int8, 2)
-    _require(x_scale, "x_scale", torch.float32, 1)
-    _require(x_qsum, "x_qsum", torch.int32, 1)
-    if tuple(xq.shape) != (M, K) or x_scale.shape[0] != M or x_qsum.shape[0] != M:
-        raise ValueError("codes tensors do not match x")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _require(out, "out", torch.float32, 2)
-    if tuple(out.shape) != (M, N):
-        raise ValueError(f"out must be [{M}][{N}]")
+    _require_at_least(w_scale, "w_scale", torch.float32, 1, dev)
+    _gain(gain, K, dev)
+    xq, x_scale, x_qsum = _codes(codes, M, K, dev)
+    out = _output(out, "out", torch.float32, (M, N), dev)
     if acc_out is not None:
-        _require(acc_out, "acc_out", torch.int32, 2)
-        if tuple(acc_out.shape) != (M, N):
-            raise ValueError(f"acc_out must be [{M}][{N}]")
+        _require_shape(acc_out, "acc_out", torch.int32, (M, N), dev)
     _check(lib().bitnet_bitlinear_forward(_ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(packed),
                                           _ptr(w_scale), M, N, K, _ptr(xq), _ptr(x_scale),
-                                          _ptr(x_qsum), _ptr(out), _ptr(acc_out),
-                                          _stream(x.device)))
+                                          _ptr(x_qsum), _ptr(out), _ptr(acc_out), _stream(dev)))
     return (out, acc_out) if acc_out is not None else out
 
 
-# --- backward under the straight-through estimator ------------------------
+# --- base-3 packing ---------------------------------------------------------
 
 def base3_row_bytes(K: int) -> int:
     """Bytes per row of the base-3 packing (five weights per byte, rows padded to 16)."""
@@ -422,13 +418,15 @@ def pack_base3(packed, K: int, out=None):
     """2-bit packed uint8 [N][K/4] -> base-3 packed uint8 [N][base3_row_bytes(K)] (bitnet_pack_base3)."""
     torch = _torch()
     _require(packed, "packed", torch.uint8, 2)
+    dev = packed.device
     N = packed.shape[0]
     if packed.shape[1] * 4 != K:
         raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}]")
     rb = base3_row_bytes(K)
-    if out is None:
-        out = torch.empty((N, rb), dtype=torch.uint8, device=packed.device)
-    _check(lib().bitnet_pack_base3(_ptr(packed), N, K, _ptr(out), _stream(packed.device)))
+    if rb == 0:
+        raise ValueError(f"K={K} is not a valid packing width")
+    out = _output(out, "out", torch.uint8, (N, rb), dev)
+    _check(lib().bitnet_pack_base3(_ptr(packed), N, K, _ptr(out), _stream(dev)))
     return out
 
 
@@ -436,32 +434,36 @@ def linear_forward_base3(xq, x_scale, x_qsum, packed3, w_scale, return_acc: bool
     """One token on base-3 packed weights (bitnet_linear_forward_base3): y float32 [1][N]."""
     torch = _torch()
     _require(xq, "xq", torch.int8, 2)
-    _require(x_scale, "x_scale", torch.float32, 1)
-    _require(x_qsum, "x_qsum", torch.int32, 1)
-    _require(packed3, "packed3", torch.uint8, 2)
-    _require(w_scale, "w_scale", torch.float32, 1)
+    dev = xq.device
     M, K = xq.shape
+    _require_shape(x_scale, "x_scale", torch.float32, (M,), dev)
+    _require_shape(x_qsum, "x_qsum", torch.int32, (M,), dev)
+    _require(packed3, "packed3", torch.uint8, 2, dev)
+    _require_at_least(w_scale, "w_scale", torch.float32, 1, dev)
     N = packed3.shape[0]
     if packed3.shape[1] != base3_row_bytes(K):
         raise ValueError(f"packed3 is [{N}][{packed3.shape[1]}], expected [{N}][{base3_row_bytes(K)}] for K={K}")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=xq.device)
-    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if return_acc else None
+    y = _output(out, "out", torch.float32, (M, N), dev)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if return_acc else None
     _check(lib().bitnet_linear_forward_base3(_ptr(xq), _ptr(x_scale), _ptr(x_qsum), _ptr(packed3),
-                                             _ptr(w_scale), M, N, K, _ptr(y), _ptr(acc),
-                                             _stream(xq.device)))
+                                             _ptr(w_scale), M, N, K, _ptr(y), _ptr(acc), _stream(dev)))
     return (y, acc) if return_acc else y
 
+
+# --- backward under the straight-through estimator ------------------------
 
 def transpose_packed(packed, K: int, out=None):
     """packed uint8 [N][K/4] -> packed_t uint8 [K][N/4] (bitnet_transpose_packed)."""
     torch = _torch()
     _require(packed, "packed", torch.uint8, 2)
+    dev = packed.device
     N = packed.shape[0]
     if packed.shape[1] * 4 != K:
         raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}]")
-    if out is None:
-        out = torch.empty((K, N // 4), dtype=torch.uint8, device=packed.device)
-    _check(lib().bitnet_transpose_packed(_ptr(packed), N, K, _ptr(out), _stream(packed.device)))
+    if N % 4 != 0:
+        raise ValueError(f"N={N} must be a multiple of 4 (of 64 for the library)")
+    out = _output(out, "out", torch.uint8, (K, N // 4), dev)
+    _check(lib().bitnet_transpose_packed(_ptr(packed), N, K, _ptr(out), _stream(dev)))
     return out
 
 
@@ -469,16 +471,16 @@ def linear_backward_input(grad_y, packed_t, w_scale, out=None):
     """grad_n float32 [M][K] = d_w * grad_y (bf16 [M][N]) @ q_w, from packed_t [K][N/4]."""
     torch = _torch()
     _require(grad_y, "grad_y", torch.bfloat16, 2)
-    _require(packed_t, "packed_t", torch.uint8, 2)
-    _require(w_scale, "w_scale", torch.float32, 1)
+    dev = grad_y.device
+    _require(packed_t, "packed_t", torch.uint8, 2, dev)
+    _require_at_least(w_scale, "w_scale", torch.float32, 1, dev)
     M, N = grad_y.shape
     K = packed_t.shape[0]
     if packed_t.shape[1] * 4 != N:
         raise ValueError(f"packed_t is [{K}][{packed_t.shape[1]}], expected [{K}][{N // 4}]")
-    if out is None:
-        out = torch.empty((M, K), dtype=torch.float32, device=grad_y.device)
+    out = _output(out, "out", torch.float32, (M, K), dev)
     _check(lib().bitnet_linear_backward_input(_ptr(grad_y), _ptr(packed_t), _ptr(w_scale), M, N, K,
-                                              _ptr(out), _stream(grad_y.device)))
+                                              _ptr(out), _stream(dev)))
     return out
 
 
@@ -486,20 +488,22 @@ def linear_backward_weight(grad_y, xq, x_scale, out=None, workspace=None):
     """grad_w float32 [N][K] = sum_m grad_y[m][n] d_x[m] q_x[m][k] (bitnet_linear_backward_weight)."""
     torch = _torch()
     _require(grad_y, "grad_y", torch.bfloat16, 2)
-    _require(xq, "xq", torch.int8, 2)
-    _require(x_scale, "x_scale", torch.float32, 1)
+    dev = grad_y.device
+    _require(xq, "xq", torch.int8, 2, dev)
     M, N = grad_y.shape
     K = xq.shape[1]
-    if xq.shape[0] != M or x_scale.shape[0] != M:
-        raise ValueError("xq and x_scale must have M rows")
-    if out is None:
-        out = torch.empty((N, K), dtype=torch.float32, device=grad_y.device)
+    if xq.shape[0] != M:
+        raise ValueError("xq must have the M rows of grad_y")
+    _require_shape(x_scale, "x_scale", torch.float32, (M,), dev)
+    out = _output(out, "out", torch.float32, (N, K), dev)
     need = int(lib().bitnet_linear_backward_weight_workspace_bytes(M, N, K))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=grad_y.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1, dev)
     _check(lib().bitnet_linear_backward_weight(_ptr(grad_y), _ptr(xq), _ptr(x_scale), M, N, K,
                                                _ptr(out), _ptr(workspace), workspace.numel(),
-                                               _stream(grad_y.device)))
+                                               _stream(dev)))
     return out
 
 
@@ -507,21 +511,19 @@ def rmsnorm_backward(x, grad_n, gain=None, eps: float = 1e-5, with_gain_grad: bo
     """(grad_x float32 [M][K], grad_gain float32 [K] or None) of n = x * gain * r."""
     torch = _torch()
     _require(x, "x", torch.bfloat16, 2)
-    _require(grad_n, "grad_n", torch.float32, 2)
+    dev = x.device
     M, K = x.shape
-    if tuple(grad_n.shape) != (M, K):
-        raise ValueError("grad_n must have the shape of x")
-    if gain is not None:
-        _require(gain, "gain", torch.float32, 1)
-    grad_x = torch.empty((M, K), dtype=torch.float32, device=x.device)
-    grad_gain = torch.empty(K, dtype=torch.float32, device=x.device) if with_gain_grad else None
+    _require_shape(grad_n, "grad_n", torch.float32, (M, K), dev)
+    _gain(gain, K, dev)
+    grad_x = torch.empty((M, K), dtype=torch.float32, device=dev)
+    grad_gain = torch.empty(K, dtype=torch.float32, device=dev) if with_gain_grad else None
     ws, ws_bytes = None, 0
     if with_gain_grad:
         ws_bytes = int(lib().bitnet_rmsnorm_backward_workspace_bytes(M, K))
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     _check(lib().bitnet_rmsnorm_backward(_ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(grad_n), M, K,
                                          _ptr(grad_x), _ptr(grad_gain), _ptr(ws), ws_bytes,
-                                         _stream(x.device)))
+                                         _stream(dev)))
     return grad_x, grad_gain
 
 

@@ -405,6 +405,17 @@ int bitnet_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, con
                       fn);
 }
 
+int bitnet_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_stream_read";
+    if (bytes < 16 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+        return fail(BITNET_ERR_SHAPE, "%s: bytes=%zu must be a multiple of 16 in [16, 2^40]", fn, bytes);
+    if (!buf || !sink) return fail(BITNET_ERR_NULL, "%s: buf and sink must not be NULL", fn);
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return fail(BITNET_ERR_ALIGN, "%s: buf must be 16-byte and sink 4-byte aligned", fn);
+    return hip_status(bitnet::launch_stream_read(buf, (int64_t)bytes, sink, (hipStream_t)stream), fn);
+}
+
 const char* bitnet_status_string(int status) {
     switch (status) {
         case BITNET_OK: return "ok";

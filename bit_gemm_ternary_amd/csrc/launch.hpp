@@ -137,4 +137,8 @@ hipError_t launch_rmsnorm_backward(const uint16_t* x, const float* gain, float e
                                    int64_t M, int64_t K, float* grad_x, float* grad_gain, void* workspace,
                                    hipStream_t stream);
 
+// Plain read of `bytes` bytes (a multiple of 16) of device memory; a word is
+// written to sink only on a data pattern that does not occur in practice.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace bitnet

@@ -359,6 +359,17 @@ int bitnet_linear_forward_base3(const int8_t* xq, const float* x_scale, const in
                                 int64_t K, float* y, int32_t* acc, void* stream);
 
 /*
+ * Measurement reference, no passage of the pages: one plain read of `bytes`
+ * bytes of device memory at `buf` (16-byte aligned, bytes a multiple of 16 and
+ * >= 16), each byte once with 16-byte loads over the whole chip.  Its rate is
+ * what a simple streaming kernel reaches on this GPU, against which the
+ * bandwidth-bound kernels are also stated.  `sink` (device, 4 bytes, 4-byte
+ * aligned) receives a word only on a data pattern that does not occur in
+ * practice; its contents are otherwise left as they are.
+ */
+int bitnet_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Profiling hook: arm two hipEvent_t (passed as void*; either may be NULL) for
  * the first kernel the next bitnet_* call on this thread launches (the
  * contraction kernel of bitnet_linear_forward, the quantisation kernel of the

@@ -282,3 +282,15 @@ def test_base3_argument_errors(L):
     assert f(p3=A4) == 4
     assert f(y=BAD) == 4
     assert f(M=0, xq=0, p3=0) == 0           # empty batch: nothing enqueued
+
+
+def test_stream_read_argument_errors(L):
+    f = L.bitnet_stream_read
+    v = ctypes.c_void_p
+    assert f(v(A16), 0, v(A4), None) == 2
+    assert f(v(A16), 24, v(A4), None) == 2
+    assert f(v(A16), 8, v(A4), None) == 2
+    assert f(None, 1024, v(A4), None) == 1
+    assert f(v(A16), 1024, None, None) == 1
+    assert f(v(A4), 1024, v(A4), None) == 4
+    assert f(v(A16), 1024, v(BAD), None) == 4
