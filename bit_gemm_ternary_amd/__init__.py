@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.bitnet_pack_weights_workspace_bytes.restype = sz
     L.bitnet_pack_weights.argtypes = [p, i64, i64, i32, p, p, p, sz, p]
     L.bitnet_pack_weights.restype = i32
+    L.bitnet_pack_weights_noalloc.argtypes = [p, i64, i64, i32, p, p, p]
+    L.bitnet_pack_weights_noalloc.restype = i32
     for name in ("bitnet_quant_act", "bitnet_hadamard_quant_act"):
         fn = getattr(L, name)
         fn.argtypes = [p, p, f32, i64, i64, p, p, p, p]
@@ -223,6 +225,26 @@ def pack_weights(W, hadamard: bool = False, out=None, workspace=None):
     _check(lib().bitnet_pack_weights(_ptr(W), N, K, int(bool(hadamard)), _ptr(packed),
                                      _ptr(w_scale), _ptr(workspace), workspace.numel(),
                                      _stream(dev)))
+    return packed, w_scale
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20   # BITNET_NOALLOC_SCRATCH_BYTES
+
+
+def pack_weights_noalloc(W, out, hadamard: bool = False):
+    """pack_weights into the caller's ``out`` = (packed uint8 [N][K/4], w_scale
+    float32 [2]) with no workspace and no allocation (bitnet_pack_weights_noalloc:
+    the library's static per-GPU scratch of NOALLOC_SCRATCH_BYTES bytes serves
+    as the workspace; larger requests raise).  Calls that overlap on one GPU
+    race on that scratch."""
+    torch = _torch()
+    _require(W, "W", torch.float32, 2)
+    N, K = W.shape
+    packed, w_scale = out
+    _require_shape(packed, "packed", torch.uint8, (N, K // 4), W.device)
+    _require_shape(w_scale, "w_scale", torch.float32, (2,), W.device)
+    _check(lib().bitnet_pack_weights_noalloc(_ptr(W), N, K, int(bool(hadamard)), _ptr(packed),
+                                             _ptr(w_scale), _stream(W.device)))
     return packed, w_scale
 
 

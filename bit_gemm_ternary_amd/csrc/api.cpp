@@ -126,6 +126,47 @@ int bitnet_pack_weights(const float* W, int64_t N, int64_t K, int hadamard, uint
                       fn);
 }
 
+static_assert(BITNET_NOALLOC_SCRATCH_BYTES == bitnet::kNoAllocScratchBytes,
+              "the header's scratch size is the library's");
+
+int bitnet_pack_weights_noalloc(const float* W, int64_t N, int64_t K, int hadamard, uint8_t* packed,
+                                float* w_scale, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_pack_weights_noalloc";
+    if (N < 1 || N > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (hadamard != 0 && hadamard != 1) return fail(BITNET_ERR_VALUE, "%s: hadamard must be 0 or 1", fn);
+    if (hadamard && (s = check_hadamard_k(K, fn)) != BITNET_OK) return s;
+    if (!W || !packed || !w_scale)
+        return fail(BITNET_ERR_NULL, "%s: W, packed and w_scale must not be NULL", fn);
+    if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(w_scale, 4))
+        return fail(BITNET_ERR_ALIGN, "%s: W and packed must be 16-byte aligned", fn);
+    const size_t need = bitnet::pack_workspace_bytes(N, K, hadamard);
+    if (need > bitnet::kNoAllocScratchBytes)
+        return fail(BITNET_ERR_WORKSPACE,
+                    "%s: N=%lld K=%lld hadamard=%d needs %zu bytes of scratch; the library's static "
+                    "scratch holds %zu (use bitnet_pack_weights with a workspace)",
+                    fn, (long long)N, (long long)K, hadamard, need, bitnet::kNoAllocScratchBytes);
+    int device = -1;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (stream != nullptr) {
+        int stream_device = -1;
+        e = hipStreamGetDevice((hipStream_t)stream, &stream_device);
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (stream_device != device)
+            return fail(BITNET_ERR_VALUE, "%s: the stream belongs to device %d, the current device is %d",
+                        fn, stream_device, device);
+    }
+    void* scratch = nullptr;
+    e = bitnet::noalloc_scratch(device, &scratch);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(bitnet::launch_pack_weights(W, N, K, hadamard, std::sqrt((double)K), packed, w_scale,
+                                                  scratch, (hipStream_t)stream),
+                      fn);
+}
+
 int bitnet_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
                      int8_t* xq, float* x_scale, int32_t* x_qsum, void* stream) {
     DisarmEvents disarm;

@@ -39,6 +39,12 @@ size_t pack_workspace_bytes(int64_t N, int64_t K, int hadamard);
 hipError_t launch_pack_weights(const float* W, int64_t N, int64_t K, int hadamard,
                                double sqrt_k, uint8_t* packed, float* w_scale, void* workspace,
                                hipStream_t stream);
+// Bytes of the library-owned scratch that bitnet_pack_weights_noalloc uses in
+// place of a workspace (one array per device, in pack.hip).
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+// Device address of that array on `device`, which must be the current device;
+// looked up once per device and kept.
+hipError_t noalloc_scratch(int device, void** ptr);
 
 // --- activation quantisation (quant_act.hip, hadamard_quant.hip) ------------
 hipError_t launch_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,

@@ -12,8 +12,16 @@
 //   finalize:   S = sum_n r[n] (n ascending, one wavefront), gamma = S / (N K), s_w, d_w;
 //   ternarize:  q = clamp(rint(w * s_w), -1, 1); 16 weights -> one 32-bit word.
 // The fixed summation order makes s_w bit-identical to a sequential float64 sum.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
+
+// Library-owned scratch of bitnet_pack_weights_noalloc (row sums, and the
+// rotated rows of the Hadamard path), one copy per GPU the library runs on,
+// held until the process ends.  Host code never uses this name as an address:
+// its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[bitnet::kNoAllocScratchBytes];
 
 namespace bitnet {
 namespace {
@@ -186,7 +194,27 @@ __global__ __launch_bounds__(256) void ternarize_pack_kernel(const float* __rest
     }
 }
 
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
 }  // namespace
+
+hipError_t noalloc_scratch(int device, void** ptr) {
+    if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[device] == nullptr) {
+        // The device address of this GPU's copy of the array; the caller has
+        // made `device` current.
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[device] = p;
+    }
+    *ptr = g_scratch_ptr[device];
+    return hipSuccess;
+}
 
 size_t pack_workspace_bytes(int64_t N, int64_t K, int hadamard) {
     const size_t sums = ((size_t)N * sizeof(double) + 255) / 256 * 256;

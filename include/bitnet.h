@@ -113,6 +113,36 @@ int bitnet_pack_weights(const float* W, int64_t N, int64_t K, int hadamard, uint
                         float* w_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bitnet_pack_weights without a caller workspace and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture (weights re-packed every step of quantisation-aware training),
+ * tight serving loops, harnesses that forbid hipMalloc.  It calls no hipMalloc,
+ * hipFree or allocating library routine; the caller still passes W, packed and
+ * w_scale, with the same meaning, layout and rules as bitnet_pack_weights.
+ *
+ * In place of the workspace it uses a scratch array that the library owns: a
+ * static device array of BITNET_NOALLOC_SCRATCH_BYTES bytes, one per GPU the
+ * library runs on, held until the process ends.  Its address on a GPU is
+ * looked up on the first call on that GPU (hipGetSymbolAddress, with that GPU
+ * current) and kept.  A request whose workspace would exceed the array,
+ * bitnet_pack_weights_workspace_bytes(N, K, hadamard) >
+ * BITNET_NOALLOC_SCRATCH_BYTES (about 524,000 rows without the rotation; N*K
+ * up to about a million weights with it), returns BITNET_ERR_WORKSPACE before
+ * anything is launched.
+ *
+ * `stream` must belong to the calling thread's current device
+ * (BITNET_ERR_VALUE otherwise).  Every call on one GPU shares that GPU's
+ * array and leaves its contents behind (nothing in it needs clearing: each
+ * call writes every scratch word it reads): calls whose work overlaps on one
+ * GPU (different streams, or threads without ordering) race on the array and
+ * must be serialised by the caller.
+ */
+#define BITNET_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+int bitnet_pack_weights_noalloc(const float* W, int64_t N, int64_t K, int hadamard, uint8_t* packed,
+                                float* w_scale, void* stream);
+
+/*
  * Fused RMSNorm + per-token absmax int8 activation quantisation
  * ([FT] "양자화 메커니즘", activations; [QP] absmax factor 127/absmax).
  *

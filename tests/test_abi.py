@@ -294,3 +294,30 @@ def test_stream_read_argument_errors(L):
     assert f(v(A16), 1024, None, None) == 1
     assert f(v(A4), 1024, v(A4), None) == 4
     assert f(v(A16), 1024, v(BAD), None) == 4
+
+
+def test_pack_noalloc_argument_errors(L):
+    f = L.bitnet_pack_weights_noalloc
+    v = ctypes.c_void_p
+    assert f(v(A16), 0, 256, 0, v(A16), v(A4), None) == 2
+    assert f(v(A16), 8, 100, 0, v(A16), v(A4), None) == 2
+    assert f(v(A16), 8, 256, 2, v(A16), v(A4), None) == 7
+    assert f(v(A16), 8, 192, 1, v(A16), v(A4), None) == 3
+    assert f(None, 8, 256, 0, v(A16), v(A4), None) == 1
+    assert f(v(A16), 8, 256, 0, v(A16), None, None) == 1
+    assert f(v(A4), 8, 256, 0, v(A16), v(A4), None) == 4
+    assert f(v(A16), 8, 256, 0, v(A16), v(BAD), None) == 4
+    # Beyond the static scratch: refused before any HIP call.
+    cap = bt.NOALLOC_SCRATCH_BYTES
+    rows = cap // 8 + 1
+    assert L.bitnet_pack_weights_workspace_bytes(rows, 256, 0) > cap
+    assert f(v(A16), rows, 256, 0, v(A16), v(A4), None) == 5
+    assert b"scratch" in L.bitnet_last_error()
+    assert L.bitnet_pack_weights_workspace_bytes(512, 4096, 1) > cap
+    assert f(v(A16), 512, 4096, 1, v(A16), v(A4), None) == 5
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define BITNET_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == bt.NOALLOC_SCRATCH_BYTES
