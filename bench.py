@@ -10,7 +10,7 @@ resident in HBM; the packed weights rotate over enough distinct copies
 (> 1 GiB) that the 256 MB Infinity Cache cannot serve them, so every step
 streams its weights from HBM.  The --steps timed steps are captured into ONE
 HIP graph, replayed once untimed, and the timed region is a single replay of
-it after a cache flush (a 1 GiB device copy through other buffers), so the
+it after a cache flush (a plain 1 GiB read of another buffer), so the
 region measures the GPU, not Python or per-launch host overhead, whatever
 --steps is.
 
@@ -208,18 +208,21 @@ FLUSH_BYTES = 1 << 30        # device-copy traffic that evicts the Infinity Cach
 
 
 class CacheFlush:
-    """A device copy of 512 MiB into another 512 MiB (1 GiB of traffic) through
-    buffers no step touches.  Enqueued just before a timed region it evicts the
-    256 MB Infinity Cache and every XCD's L2, and it keeps the GPU busy while
-    the host submits the graph that follows, so the region's first event is
-    not stamped ahead of that submission."""
+    """One plain read (bitnet_stream_read) of a 1 GiB buffer no step touches.
+    Enqueued just before a timed region it evicts the 256 MB Infinity Cache and
+    every XCD's L2 without leaving dirty lines behind, and it keeps the GPU busy
+    while the host submits the graph that follows, so the region's first event
+    is not stamped ahead of that submission."""
 
     def __init__(self, torch, dev, nbytes=FLUSH_BYTES):
-        self.src = torch.ones(nbytes // 2, dtype=torch.uint8, device=dev)
-        self.dst = torch.empty_like(self.src)
+        import bit_gemm_ternary_amd as bt
+
+        self.bt = bt
+        self.buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        self.sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def __call__(self):
-        self.dst.copy_(self.src)
+        self.bt.stream_read(self.buf, self.sink)
 
 
 def capture_steps(step, n, copies, torch):

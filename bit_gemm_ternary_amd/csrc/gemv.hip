@@ -49,6 +49,11 @@
 // barriers (vectors past K are zeros): the float64 scale d_x and the code sums
 // are formed alongside the codes, so after the second barrier a wave only
 // reads its codes and starts on rows.
+//
+// One token, fused, N < 16384 with ceil(N / 1024) rows per wave in one register
+// set (the 7B / 8B decode projections): decode1_kernel below, the same
+// arithmetic laid out for one 256-thread workgroup per CU with exact rows per
+// wave, every weight load issued before the token's arithmetic.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -62,6 +67,9 @@ constexpr int kMaxXRegsChunks = 8;              // MT * CH limit: 16 * MT * CH c
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+__device__ __forceinline__ int dot4_first(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, 0, true);
 }
 
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t res, uint32_t off) {
@@ -472,6 +480,255 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// One token, fused: the decode fast path for matrices whose rows spread over
+// 1024 waves fit one register set per wave.  One 256-thread workgroup per CU
+// (one wave per SIMD); wave g owns exactly the RB rows g, g + W, ..., so there
+// is no per-row branch (rows past N load zeros and store nothing).  Order of
+// work in a wave:
+//   1. the token's loads (and the gain's), then every weight load of the
+//      wave's rows at once;
+//   2. absmax over the workgroup (an integer maximum of the bf16 magnitude
+//      bits when there is no gain), one barrier;
+//   3. this thread's share of the codes into LDS, with its code sum and its
+//      part of sum x^2 (exact float32 squares in four float32 chains,
+//      combined in float64), one barrier;
+//   4. the wave's code registers from LDS, the dot products of each row as its
+//      loads land, one transposing reduction over the rows, the stores.
+// The arithmetic of every step is that of decode_kernel above.
+// ---------------------------------------------------------------------------
+template <int CH, int RB, bool GAIN>
+__global__ __launch_bounds__(256) void decode1_kernel(const Args a) {
+    constexpr int NT = 256;
+    constexpr int NW = NT / kWave;
+    constexpr int NV = RB <= 1 ? 1 : (RB <= 2 ? 2 : (RB <= 4 ? 4 : (RB <= 8 ? 8 : 16)));
+    constexpr int LV = log2_of(NV);
+    constexpr int XV = CH * 512 / NT;   // 8-value vectors of the token per thread
+    static_assert(RB <= 16 && RB * CH <= 16, "one register set of rows");
+    __shared__ __align__(16) int8_t codes[CH * 4096];
+    __shared__ float red_f[NW];
+    __shared__ double red_d[NW];
+    __shared__ int red_i[NW];
+
+    const int t = threadIdx.x;
+    const int lane = t % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(t / kWave);
+    const int g = (int)blockIdx.x * NW + wave;
+    const int W = (int)gridDim.x * NW;
+    const int N = a.N, K = a.K;
+    const int nchunk = K / 64;
+    const int row_bytes = K / 4;
+    const int nvec = K / 8;
+
+    // Arguments used only at the end are read with the first ones: a scalar
+    // load issued later would be waited for with the LDS traffic.
+    float* const y_out = a.y;
+    int32_t* const acc_out = a.acc;
+    const int groups = a.scales.groups;
+    const float eps = a.eps;
+    asm volatile("" ::"s"(y_out), "s"(acc_out), "s"(groups), "s"(eps));
+
+    // 1. Token (and gain), then all weight loads.
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, K * 2,
+                                                                         (int)kBufferWord3);
+    uint4 raw[XV];
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+        const int v = t + NT * i;
+        raw[i] = load16(xres, v < nvec ? (uint32_t)(16 * v) : kOutOfRange);
+    }
+    // d_w by a vector load issued with the token's: a scalar load here would
+    // be waited for at the first barrier (the LDS and scalar-memory counters
+    // are one), a full memory latency on the critical path.
+    const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc((void*)a.scales.w_scale, (short)0, 4,
+                                                                         (int)kBufferWord3);
+    const float dw0 = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(sres, 0, 0, 0));
+    float gv[GAIN ? XV : 1][8];
+    if constexpr (GAIN) {
+        const __amdgpu_buffer_rsrc_t gres = __builtin_amdgcn_make_buffer_rsrc((void*)a.gain, (short)0, K * 4,
+                                                                             (int)kBufferWord3);
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            const int v = t + NT * i;
+            const uint4 g0 = load16(gres, v < nvec ? (uint32_t)(32 * v) : kOutOfRange);
+            const uint4 g1 = load16(gres, v < nvec ? (uint32_t)(32 * v + 16) : kOutOfRange);
+            gv[i][0] = __uint_as_float(g0.x); gv[i][1] = __uint_as_float(g0.y);
+            gv[i][2] = __uint_as_float(g0.z); gv[i][3] = __uint_as_float(g0.w);
+            gv[i][4] = __uint_as_float(g1.x); gv[i][5] = __uint_as_float(g1.y);
+            gv[i][6] = __uint_as_float(g1.z); gv[i][7] = __uint_as_float(g1.w);
+        }
+    }
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.packed + (int64_t)(g < N ? g : 0) * row_bytes), (short)0, kMaxRecords, (int)kBufferWord3);
+    uint4 w[RB][CH];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int c = lane + kWave * j;
+            const bool ok = (int64_t)g + (int64_t)rb * W < N && c < nchunk;
+            w[rb][j] = load16(wres, ok ? (uint32_t)(rb * W * row_bytes + 16 * c) : kOutOfRange);
+        }
+    // The weight loads stay ahead of the token's arithmetic (the scheduler
+    // would otherwise sink them below the wait for the token).
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto values = [&](int i, float (&u)[8], bool with_gain) {
+        const uint32_t ws[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[2 * e] = bf16_lo(ws[e]);
+            u[2 * e + 1] = bf16_hi(ws[e]);
+        }
+        if constexpr (GAIN) {
+            if (with_gain) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) u[e] *= gv[i][e];
+            }
+        }
+    };
+
+    // 2. absmax of x * gain over the workgroup.
+    float amax = 0.f;
+    if constexpr (!GAIN) {
+        typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+        us2 m2 = {0, 0};
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            const uint32_t ws[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t mag = ws[e] & 0x7fff7fffu;
+                us2 v;
+                __builtin_memcpy(&v, &mag, 4);
+                m2 = __builtin_elementwise_max(m2, v);
+            }
+        }
+        amax = __uint_as_float((uint32_t)(m2.x > m2.y ? m2.x : m2.y) << 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            float u[8];
+            values(i, u, true);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(u[e]));
+        }
+    }
+    amax = wave_max_dpp(amax);
+    if (lane == 0) red_f[wave] = amax;
+    __syncthreads();
+    amax = red_f[0];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) amax = fmaxf(amax, red_f[wv]);
+
+    // 3. Codes (the rounding of decode_kernel step 3), code sum, sum of x^2.
+    const float scale = amax < kTinyAbsmax ? 0.f : 127.0f / amax;
+    int part = 0;
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+        const int v = t + NT * i;
+        float u[8];
+        values(i, u, true);
+        uint32_t b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = __float_as_uint(__fadd_rn(__fmul_rn(u[e], scale), 12582912.0f));
+        const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+        *reinterpret_cast<uint2*>(&codes[8 * v]) = make_uint2(lo, hi);
+        part = dot4(lo, 0x01010101u, part);
+        part = dot4(hi, 0x01010101u, part);
+    }
+    float sf[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+        float u[8];
+        values(i, u, false);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sf[e % 4] = __fmaf_rn(u[e], u[e], sf[e % 4]);
+    }
+    part = wave_sum_dpp(part);
+    const double ssw = wave_sum_dpp(((double)sf[0] + (double)sf[1]) + ((double)sf[2] + (double)sf[3]));
+    if (lane == 0) {
+        red_i[wave] = part;
+        red_d[wave] = ssw;
+    }
+    __syncthreads();
+
+    // 4. Code registers, token scale and sum; the rows.
+    uint32_t xv[CH][16];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int c = lane + kWave * j;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (c < nchunk) v = reinterpret_cast<const uint4*>(&codes[64 * c])[q];
+            xv[j][4 * q] = v.x;
+            xv[j][4 * q + 1] = v.y;
+            xv[j][4 * q + 2] = v.z;
+            xv[j][4 * q + 3] = v.w;
+        }
+    }
+    int tok_sum = red_i[0];
+    double ss = red_d[0];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) {
+        tok_sum += red_i[wv];
+        ss += red_d[wv];
+    }
+    // d_x (float64 chain with a quarter-rate reciprocal square root) is formed
+    // after the rows, where only the storing lanes wait for it.
+    if (blockIdx.x == 0) {
+        for (int v = t; v < K / 16; v += NT)
+            reinterpret_cast<uint4*>(a.xq_out)[v] = reinterpret_cast<const uint4*>(codes)[v];
+        if (t == 0) {
+            a.x_scale_out[0] = token_scale(amax, ss, inv_count(K), eps, 1.0 / 127.0);
+            a.x_qsum_out[0] = tok_sum;
+        }
+    }
+    if (g >= N) return;  // after the last barrier: wave-uniform exit
+
+    int p[NV];
+#pragma unroll
+    for (int r = 0; r < NV; ++r) p[r] = 0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        int s03 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const uint32_t ws[4] = {w[rb][j].x, w[rb][j].y, w[rb][j].z, w[rb][j].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t word = ws[d];
+                if (j == 0 && d == 0) {
+                    s03 = dot4_first(word & 0x03030303u, xv[0][0]);
+                    s1 = dot4_first(word & 0x0C0C0C0Cu, xv[0][1]);
+                    s2 = dot4_first(word & 0x30303030u, xv[0][2]);
+                } else {
+                    s03 = dot4(word & 0x03030303u, xv[j][4 * d + 0], s03);
+                    s1 = dot4(word & 0x0C0C0C0Cu, xv[j][4 * d + 1], s1);
+                    s2 = dot4(word & 0x30303030u, xv[j][4 * d + 2], s2);
+                }
+                s03 = dot4((word >> 6) & 0x03030303u, xv[j][4 * d + 3], s03);
+            }
+        }
+        p[rb] = s03 + (s1 >> 2) + (s2 >> 4);
+    }
+    xreduce<NV>(p, lane);
+    const int idx = lane >> (6 - LV);
+    if ((lane & ((kWave >> LV) - 1)) == 0 && idx < RB) {
+        const int64_t r = (int64_t)g + (int64_t)idx * W;
+        if (r < N) {
+            const float tok_scale = token_scale(amax, ss, inv_count(K), eps, 1.0 / 127.0);
+            const int acc = p[0] - tok_sum;
+            if (acc_out != nullptr) acc_out[r] = acc;
+            y_out[r] = ((float)acc * tok_scale) * (groups == 1 ? dw0 : a.scales.of(r, dw0));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch shape.  A wave's rows stay in registers, so the grid decides how much
 // of the matrix is in flight: about 1024 waves of 256-thread workgroups, or
 // 2048 waves of 512-thread workgroups for one token and matrices larger than
@@ -568,6 +825,43 @@ hipError_t dispatch(int64_t M, const Args& a, hipStream_t stream) {
     }
 }
 
+// The one-token fused kernel for N < 16384 rows when ceil(N / 1024) rows per
+// wave fit one register set; hipErrorNotSupported otherwise (the caller falls
+// back to decode_kernel).  RB = ceil(N / 1024) rows per wave over ceil(N / RB)
+// waves: one workgroup per CU, or a few CUs idle.
+template <int CH, int RB>
+hipError_t launch_decode1_rb(const Args& a, hipStream_t stream) {
+    const int64_t waves = (a.N + RB - 1) / RB;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (a.gain != nullptr) return launch_kernel((decode1_kernel<CH, RB, true>), grid, dim3(256), 0, stream, a);
+    return launch_kernel((decode1_kernel<CH, RB, false>), grid, dim3(256), 0, stream, a);
+}
+
+template <int CH>
+hipError_t launch_decode1_ch(const Args& a, hipStream_t stream) {
+    const int64_t rpw = (a.N + 1023) / 1024;
+    if (a.N >= 16384 || rpw > 16 / CH) return hipErrorNotSupported;
+#define BITNET_DECODE1_RB(R) \
+    if constexpr (R * CH <= 16) \
+        if (rpw == R) return launch_decode1_rb<CH, R>(a, stream);
+    BITNET_DECODE1_RB(1) BITNET_DECODE1_RB(2) BITNET_DECODE1_RB(3) BITNET_DECODE1_RB(4)
+    BITNET_DECODE1_RB(5) BITNET_DECODE1_RB(6) BITNET_DECODE1_RB(7) BITNET_DECODE1_RB(8)
+    BITNET_DECODE1_RB(9) BITNET_DECODE1_RB(10) BITNET_DECODE1_RB(11) BITNET_DECODE1_RB(12)
+    BITNET_DECODE1_RB(13) BITNET_DECODE1_RB(14) BITNET_DECODE1_RB(15) BITNET_DECODE1_RB(16)
+#undef BITNET_DECODE1_RB
+    return hipErrorNotSupported;
+}
+
+hipError_t dispatch_decode1(const Args& a, hipStream_t stream) {
+    switch (chunks_per_lane(a.K)) {
+        case 1: return launch_decode1_ch<1>(a, stream);
+        case 2: return launch_decode1_ch<2>(a, stream);
+        case 3: return launch_decode1_ch<3>(a, stream);
+        case 4: return launch_decode1_ch<4>(a, stream);
+        default: return hipErrorNotSupported;
+    }
+}
+
 }  // namespace
 
 bool gemv_supported(int64_t M, int64_t K) {
@@ -593,6 +887,10 @@ hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
     a.x = x, a.gain = gain, a.eps = eps, a.packed = packed, a.scales = scales;
     a.N = (int)N, a.K = (int)K, a.y = y, a.xq_out = xq, a.x_scale_out = x_scale;
     a.x_qsum_out = x_qsum, a.acc = acc;
+    if (M == 1 && N >= 1) {
+        const hipError_t e = dispatch_decode1(a, stream);
+        if (e != hipErrorNotSupported) return e;
+    }
     return dispatch<true>(M, a, stream);
 }
 

@@ -310,6 +310,13 @@ FUSED_CASES = [
     (1, 20000, 16384, False),                          # 4 chunks, 10 rows per wave
     (2, 6000, 12288, False),                           # 2 tokens x 3 chunks: one-row sets
     (4, 9000, 8192, True),                             # 4 tokens x 2 chunks: one-row sets
+    # one-token kernel with exact rows per wave (N < 16384, ceil(N / 1024) rows):
+    (1, 16383, 4096, True),                            # 16 rows per wave, last wave ragged
+    (1, 5000, 8192, False),                            # 2 chunks, 5 rows per wave
+    (1, 3000, 12288, True),                            # 3 chunks, 3 rows per wave
+    (1, 1025, 192, False),                             # 2 rows per wave, one chunk of three lanes
+    (1, 700, 16384, True),                             # 4 chunks, one row per wave, 700 waves
+    (1, 8193, 8192, False),                            # 2 chunks past one register set: decode_kernel
 ]
 
 
