@@ -70,6 +70,10 @@ def load(path: str):
     lib.oracle_pack_base3.restype = i32
     lib.oracle_unpack_base3.argtypes = [p, i64, i64, i64, p]
     lib.oracle_unpack_base3.restype = i64
+    lib.oracle_warmup_lambda.argtypes = [i64, i64]
+    lib.oracle_warmup_lambda.restype = ctypes.c_double
+    lib.oracle_linear_forward_blend.argtypes = [p, p, f32, i64, i64, p, i64, ctypes.c_double, p]
+    lib.oracle_linear_forward_blend.restype = i32
     return lib
 
 
@@ -248,6 +252,25 @@ class Oracle:
         q = np.empty((N, K), np.int8)
         bad = self.lib.oracle_unpack_base3(_ptr(packed3), N, K, row_bytes, _ptr(q))
         return q, int(bad)
+
+    def warmup_lambda(self, step: int, total: int) -> float:
+        """min(step / total, 1), 0 for step <= 0, 1 for total <= 0."""
+        return float(self.lib.oracle_warmup_lambda(int(step), int(total)))
+
+    def linear_forward_blend(self, x_bits, W, lam: float, gain=None, eps: float = 1e-5) -> np.ndarray:
+        """float64 y [M][N] of the layer at warm-up blend factor lam (oracle_linear_forward_blend)."""
+        x_bits = _c(x_bits, np.uint16)
+        W = _c(W, np.float32)
+        M, K = x_bits.shape
+        N = W.shape[0]
+        g = None if gain is None else _c(gain, np.float32)
+        y = np.empty((M, N), np.float64)
+        rc = self.lib.oracle_linear_forward_blend(_ptr(x_bits), _ptr(g), ctypes.c_float(eps), M, K, _ptr(W), N,
+                                                  ctypes.c_double(lam), _ptr(y))
+        if rc != 0:
+            raise ValueError(f"oracle_linear_forward_blend rejected M={M} N={N} K={K}")
+        return y
+
 
 _DEFAULT = None
 

@@ -55,7 +55,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_VERSION 2
+#define ORACLE_VERSION 3
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -550,4 +550,85 @@ int64_t oracle_unpack_base3(const uint8_t* packed3, int64_t N, int64_t K, int64_
         }
     }
     return bad;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Warm-up blend ([FT] "동적 워밍업 양자화"): lambda = min(step / total, 1)  */
+/* scales the difference between the original and the quantised values, so  */
+/* a value v enters as v + lambda (Q(v) - v): lambda = 0 is the full-        */
+/* precision layer, lambda = 1 the BitLinear layer.                          */
+/* ------------------------------------------------------------------------- */
+
+/* min(step / total, 1), and 0 for step <= 0; total <= 0 means no warm-up (1). */
+double oracle_warmup_lambda(int64_t step, int64_t total) {
+    if (total <= 0) return 1.0;
+    if (step <= 0) return 0.0;
+    if (step >= total) return 1.0;
+    return (double)step / (double)total;
+}
+
+/*
+ * The layer at blend factor lambda, in float64:
+ *   n[m][k]  = u[m][k] * rstd[m]      the RMSNorm output (u = float32 x * gain as
+ *                                      in O2, rstd = 1 / sqrt(mean x^2 + eps))
+ *   n~[m][k] = d_x[m] * q[m][k]        its dequantised int8 codes (O2)
+ *   W~[o][k] = d_w * q_w[o][k]         the dequantised ternary weights (O1)
+ *   a = n + lambda (n~ - n),  b = W + lambda (W~ - W)
+ *   y[m][o]  = sum_k a[m][k] b[o][k]   (k ascending)
+ * x: bf16 bits [M][K]; gain [K] or NULL; W float32 [N][K]; y float64 [M][N].
+ */
+int oracle_linear_forward_blend(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
+                                const float* W, int64_t N, double lambda, double* y) {
+    if (M < 0 || N < 0 || K < 16 || K % 16 != 0) return -1;
+    int8_t* q = (int8_t*)malloc((size_t)(M > 0 ? M : 1) * (size_t)K);
+    float* d_x = (float*)malloc(sizeof(float) * (size_t)(M > 0 ? M : 1));
+    int32_t* qsum = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M > 0 ? M : 1));
+    double* a = (double*)malloc(sizeof(double) * (size_t)(M > 0 ? M : 1) * (size_t)K);
+    uint8_t* packed = (uint8_t*)malloc((size_t)(N > 0 ? N : 1) * (size_t)(K / 4));
+    int8_t* qw = (int8_t*)malloc((size_t)(N > 0 ? N : 1) * (size_t)K);
+    float w_scale[2];
+    int rc = 0;
+    if (!q || !d_x || !qsum || !a || !packed || !qw) rc = -1;
+    if (rc == 0 && M > 0) rc = oracle_quant_act(x, gain, eps, M, K, q, d_x, qsum);
+    if (rc == 0 && N > 0) rc = oracle_pack_weights(W, N, K, 0, packed, w_scale, qw);
+    if (rc == 0) {
+        for (int64_t m = 0; m < M; m++) {
+            double sum_sq = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                const double xk = (double)bf16_bits_to_float(x[m * K + k]);
+                sum_sq += xk * xk;
+            }
+            const double rstd = 1.0 / sqrt(sum_sq / (double)K + (double)eps);
+            for (int64_t k = 0; k < K; k++) {
+                const float xk = bf16_bits_to_float(x[m * K + k]);
+                const float u = gain ? xk * gain[k] : xk;
+                const double n = (double)u * rstd;
+                const double nt = (double)d_x[m] * (double)q[m * K + k];
+                a[m * K + k] = n + lambda * (nt - n);
+            }
+        }
+        const double d_w = (double)w_scale[0];
+#pragma omp parallel for schedule(static)
+        for (int64_t o = 0; o < N; o++) {
+            double* b = (double*)malloc(sizeof(double) * (size_t)K);
+            for (int64_t k = 0; k < K; k++) {
+                const double w = (double)W[o * K + k];
+                const double wt = d_w * (double)qw[o * K + k];
+                b[k] = w + lambda * (wt - w);
+            }
+            for (int64_t m = 0; m < M; m++) {
+                double s = 0.0;
+                for (int64_t k = 0; k < K; k++) s += a[m * K + k] * b[k];
+                y[m * N + o] = s;
+            }
+            free(b);
+        }
+    }
+    free(q);
+    free(d_x);
+    free(qsum);
+    free(a);
+    free(packed);
+    free(qw);
+    return rc;
 }

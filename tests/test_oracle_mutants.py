@@ -13,6 +13,8 @@ import pytest
 import oracle
 from oracle import build as oracle_build
 import test_oracle_backward_pins as bpins
+import test_oracle_base3_pins as b3pins
+import test_oracle_blend_pins as blpins
 import test_oracle_pins as pins
 
 MUTANTS = {
@@ -67,6 +69,19 @@ MUTANTS = {
                                                   "(double)bf16_bits_to_float(x[m * K + k]);"),
     "rmsnorm backward: eps dropped": ("r[m] = 1.0 / sqrt(ss / (double)K + (double)eps);",
                                       "r[m] = 1.0 / sqrt(ss / (double)K);"),
+    "base3: offset code not added": ("c = v + 1;", "c = v;"),
+    "base3: base 4 places": ("place *= 3;", "place *= 4;"),
+    "base3: padding weights as digit 1": ("int c = 0;\n                if (k < K) {", "int c = 1;\n                if (k < K) {"),
+    "base3 unpack: offset not removed": ("q[n * K + k] = (int8_t)(byte % 3 - 1);", "q[n * K + k] = (int8_t)(byte % 3);"),
+    "base3 unpack: wrong digit divisor": ("byte /= 3;", "byte /= 4;"),
+    "blend: weights not blended": ("b[k] = w + lambda * (wt - w);", "b[k] = wt;"),
+    "blend: activations not blended": ("a[m * K + k] = n + lambda * (nt - n);", "a[m * K + k] = n;"),
+    "blend: lambda and 1 - lambda swapped": ("a[m * K + k] = n + lambda * (nt - n);",
+                                             "a[m * K + k] = nt + lambda * (n - nt);"),
+    "blend: RMSNorm factor dropped": ("const double n = (double)u * rstd;", "const double n = (double)u;"),
+    "blend: dequantised weights without d_w": ("const double wt = d_w * (double)qw[o * K + k];",
+                                               "const double wt = (double)qw[o * K + k];"),
+    "schedule: no clamp at 1": ("if (step >= total) return 1.0;\n", "\n"),
 }
 
 # Pins run against every mutant (the parametrised ones at a representative size).
@@ -102,6 +117,14 @@ PIN_CALLS = [
     (bpins.test_backward_weight_single_token_is_an_outer_product, {}),
     (bpins.test_rmsnorm_backward_matches_finite_differences, {}),
     (bpins.test_rmsnorm_backward_is_orthogonal_to_x_without_eps, {}),
+    (b3pins.test_hand_computed_bytes, {}),
+    (b3pins.test_five_digits_to_a_byte_is_a_bijection, {}),
+    (b3pins.test_round_trip_and_padding, {"N": 4, "K": 333, "row_bytes": 80}),
+    (b3pins.test_same_codes_as_the_two_bit_packing, {}),
+    (blpins.test_lambda_schedule, {}),
+    (blpins.test_lambda_one_is_the_bitlinear_layer, {"gain": True}),
+    (blpins.test_lambda_zero_is_the_dense_layer, {"gain": True}),
+    (blpins.test_blend_is_quadratic_in_lambda_over_both_operands, {"lam": 0.5}),
 ]
 
 

@@ -262,8 +262,16 @@ def test_folded_rstd_changes_only_near_ties(orc):
     q, _, _ = orc.quant_act(x, eps=1e-5)
     u = synth.bf16_to_float(x).astype(np.float64)
     xn = u / np.sqrt((u ** 2).mean(1, keepdims=True) + 1e-5)
-    literal = np.clip(np.rint(xn * 127 / np.abs(xn).max(1, keepdims=True)), -128, 127)
-    assert np.mean(literal != q) < 1e-3
+    v = xn * 127 / np.abs(xn).max(1, keepdims=True)
+    literal = np.clip(np.rint(v), -128, 127)
+    differ = literal != q
+    # The two orders agree except where the exact value is a rounding tie (the
+    # float64 literal lands within 1e-9 of a half-integer): there the folded
+    # float32 product and the float64 quotient may round to the two neighbours.
+    assert differ.sum() <= 4                           # 2 of 65536 at this seed
+    assert (np.abs(literal[differ] - q[differ]) == 1).all()
+    frac = v[differ] - np.floor(v[differ])
+    assert (np.abs(frac - 0.5) < 1e-9).all()
 
 
 # ---------------------------------------------------------------------------
