@@ -42,6 +42,9 @@ region measures the GPU, not Python or per-launch host overhead, whatever
                    int TOPS
   backward         STE backward of the prefill layer: grad_n and grad_w on the bf16
                    matrix cores, RMSNorm backward, packed-weight transpose
+  blend            the warm-up blend of the prefill layer (lambda = 0.5): the
+                   float32 contraction of blended operands, TFLOP/s against the
+                   fp32 matrix-core peak
   pack             offline weight preparation (absmean scale, ternarise, pack;
                    with the Hadamard pre-rotation for the H-BitLinear weight):
                    time per matrix and GB/s of its two passes over W
@@ -77,6 +80,7 @@ INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix-core peak, 5.0 POP/s
 PEAK_CLOCK_GHZ = 2.4        # the engine clock that peak is quoted at
 FP6_PEAK_TOPS = 10100.0     # MI355X dense fp6 / fp4 matrix-core peak, 10.1 PFLOP/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, 2.5 PFLOP/s
+FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak
 ROTATE_BYTES = 1 << 30      # > 4 x the 256 MB Infinity Cache
 METRIC = "BitLinear decode GEMV weight GB/s (%HBM peak); prefill int8 TOPS (%MFMA peak)"
 
@@ -100,7 +104,7 @@ def parse_args():
     ap.add_argument("--block-steps", type=int, default=200, help="timed steps per token count of the block leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES, ten times (HBM counter calibration)")
-    ap.add_argument("--legs", default="decode,decode_sizes,base3,prefill,hadamard,block,backward,pack",
+    ap.add_argument("--legs", default="decode,decode_sizes,base3,prefill,hadamard,block,backward,blend,pack",
                     help="comma-separated legs to run (the headline needs decode)")
     ap.add_argument("--cpu-one-core-seconds", type=float, default=5.0,
                     help="wall time budget of the one-core CPU-oracle sample")
@@ -743,6 +747,29 @@ def backward_bench(args, dev, bt, torch, synth):
     }
 
 
+def blend_bench(args, dev, bt, torch, synth):
+    """The warm-up blend (lambda = 0.5) of the prefill layer (M 2048, K 4096,
+    N 14336): quantisation, blended activations and the float32 contraction
+    with the weights blended in its stage loads, one call."""
+    layer = synth.workload("prefill")[0]
+    M, K, N = layer.M, layer.K, layer.N
+    W = torch.from_numpy(layer.weights()).to(dev)
+    packed, w_scale = bt.pack_weights(W)
+    x = torch.from_numpy(layer.activations().view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(bt.lib().bitnet_linear_forward_blend_workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    call = lambda: bt.linear_forward_blend(x, W, packed, w_scale, 0.5, out=y, workspace=ws)
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ms, _ = timed(lambda n: [call() for _ in range(n)], max(3, args.prefill_iters // 3), torch)
+    flops = 2.0 * M * N * K
+    tf = flops / (ms * 1e-3) / 1e12
+    del W, packed, x, y, ws
+    return {"workload": f"warm-up blend lambda=0.5, M={M} K={K} N={N}", "us": round(ms * 1e3, 1),
+            "TFLOPs": round(tf, 1), "frac_fp32_peak": round(tf / FP32_PEAK_TFLOPS, 4)}
+
+
 def pack_bench(args, dev, bt, torch, synth):
     """Offline weight preparation (absmean scale, ternarise, pack; and the
     Hadamard pre-rotation) of the prefill and H-BitLinear weight matrices."""
@@ -915,7 +942,7 @@ def main():
         for name, fn in (("decode_sizes", decode_sizes_bench), ("base3", base3_bench),
                          ("prefill", prefill_bench), ("hadamard", hadamard_bench),
                          ("block", block_bench), ("backward", backward_bench),
-                         ("pack", pack_bench)):
+                         ("blend", blend_bench), ("pack", pack_bench)):
             if name in legs:
                 secondary[name] = fn(args, dev, bt, torch, synth)
                 torch.cuda.empty_cache()
@@ -934,7 +961,7 @@ def main():
         for name, fn in (("decode_sizes", decode_sizes_bench), ("base3", base3_bench),
                          ("prefill", prefill_bench), ("hadamard", hadamard_bench),
                          ("block", block_bench), ("backward", backward_bench),
-                         ("pack", pack_bench)):
+                         ("blend", blend_bench), ("pack", pack_bench)):
             if name in legs:
                 secondary[name] = fn(args, dev, bt, torch, synth)
                 log(f"{name}: {secondary[name]}")

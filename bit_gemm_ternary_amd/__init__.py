@@ -96,6 +96,10 @@ def lib() -> ctypes.CDLL:
     L.bitnet_last_error.restype = ctypes.c_char_p
     L.bitnet_version.argtypes = []
     L.bitnet_version.restype = i32
+    L.bitnet_linear_forward_blend_workspace_bytes.argtypes = [i64, i64]
+    L.bitnet_linear_forward_blend_workspace_bytes.restype = sz
+    L.bitnet_linear_forward_blend.argtypes = [p, p, f32, p, p, p, f32, i64, i64, i64, p, p, sz, p]
+    L.bitnet_linear_forward_blend.restype = i32
     L.bitnet_stream_read.argtypes = [p, sz, p, p]
     L.bitnet_stream_read.restype = i32
     L.bitnet_set_kernel_events.argtypes = [p, p]
@@ -427,6 +431,34 @@ def bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5, out=None
                                           _ptr(w_scale), M, N, K, _ptr(xq), _ptr(x_scale),
                                           _ptr(x_qsum), _ptr(out), _ptr(acc_out), _stream(dev)))
     return (out, acc_out) if acc_out is not None else out
+
+
+def linear_forward_blend(x, W, packed, w_scale, lam: float, gain=None, eps: float = 1e-5, out=None,
+                         workspace=None):
+    """The layer at warm-up blend factor ``lam`` in [0, 1] (bitnet_linear_forward_blend):
+    bf16 x [M][K], float32 master weights W [N][K] with their packing (packed,
+    w_scale) -> y float32 [M][N]; lam = 0 is the dense layer, lam = 1 BitLinear."""
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    M, K = x.shape
+    _require(W, "W", torch.float32, 2, dev)
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError(f"W is {list(W.shape)}, x has K={K}")
+    _require_shape(packed, "packed", torch.uint8, (N, K // 4), dev)
+    _require_at_least(w_scale, "w_scale", torch.float32, 1, dev)
+    _gain(gain, K, dev)
+    out = _output(out, "out", torch.float32, (M, N), dev)
+    need = int(lib().bitnet_linear_forward_blend_workspace_bytes(M, K))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1, dev)
+    _check(lib().bitnet_linear_forward_blend(_ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(W), _ptr(packed),
+                                             _ptr(w_scale), ctypes.c_float(lam), M, N, K, _ptr(out),
+                                             _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
 
 
 # --- base-3 packing ---------------------------------------------------------

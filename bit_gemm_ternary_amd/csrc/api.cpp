@@ -446,6 +446,39 @@ int bitnet_rmsnorm_backward(const uint16_t* x, const float* gain, float eps, con
                       fn);
 }
 
+size_t bitnet_linear_forward_blend_workspace_bytes(int64_t M, int64_t K) {
+    if (M < 1 || M > kMaxRows || K < kMinK || K > kMaxK || K % 64 != 0) return 0;
+    return bitnet::blend_workspace_bytes(M, K);
+}
+
+int bitnet_linear_forward_blend(const uint16_t* x, const float* gain, float eps, const float* W,
+                                const uint8_t* packed, const float* w_scale, float lambda, int64_t M, int64_t N,
+                                int64_t K, float* y, void* workspace, size_t workspace_bytes, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_linear_forward_blend";
+    if (M < 0 || M > kMaxRows || N < 0 || N > kMaxRows)
+        return fail(BITNET_ERR_SHAPE, "%s: M=%lld or N=%lld out of range", fn, (long long)M, (long long)N);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if ((s = check_eps(eps, fn)) != BITNET_OK) return s;
+    if (!std::isfinite(lambda) || lambda < 0.f || lambda > 1.f)
+        return fail(BITNET_ERR_VALUE, "%s: lambda must be in [0, 1]", fn);
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!x || !W || !packed || !w_scale || !y || !workspace)
+        return fail(BITNET_ERR_NULL, "%s: only gain may be NULL", fn);
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(packed, 16) || !aligned(workspace, 16) ||
+        (gain && !aligned(gain, 16)))
+        return fail(BITNET_ERR_ALIGN, "%s: x, gain, W, packed and workspace must be 16-byte aligned", fn);
+    if (!aligned(w_scale, 4) || !aligned(y, 4))
+        return fail(BITNET_ERR_ALIGN, "%s: w_scale and y must be 4-byte aligned", fn);
+    const size_t need = bitnet::blend_workspace_bytes(M, K);
+    if (workspace_bytes < need)
+        return fail(BITNET_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    return hip_status(bitnet::launch_linear_forward_blend(x, gain, eps, W, packed, w_scale, lambda, M, N, K, y,
+                                                          workspace, (hipStream_t)stream),
+                      fn);
+}
+
 int bitnet_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
     DisarmEvents disarm;
     const char* fn = "bitnet_stream_read";

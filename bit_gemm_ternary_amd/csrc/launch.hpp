@@ -143,6 +143,14 @@ hipError_t launch_rmsnorm_backward(const uint16_t* x, const float* gain, float e
                                    int64_t M, int64_t K, float* grad_x, float* grad_gain, void* workspace,
                                    hipStream_t stream);
 
+// The layer at warm-up blend factor lambda (blend.hip): workspace of
+// blend_workspace_bytes(M, K) bytes, 16-byte aligned (blended activations,
+// int8 codes, scales and sums).
+size_t blend_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_linear_forward_blend(const uint16_t* x, const float* gain, float eps, const float* W,
+                                       const uint8_t* packed, const float* w_scale, float lambda, int64_t M,
+                                       int64_t N, int64_t K, float* y, void* workspace, hipStream_t stream);
+
 // Plain read of `bytes` bytes (a multiple of 16) of device memory; a word is
 // written to sink only on a data pattern that does not occur in practice.
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);

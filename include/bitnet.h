@@ -389,6 +389,34 @@ int bitnet_linear_forward_base3(const int8_t* xq, const float* x_scale, const in
                                 int64_t K, float* y, int32_t* acc, void* stream);
 
 /*
+ * The layer during the warm-up of quantisation ([FT] "동적 워밍업 양자화"):
+ * with lambda = min(step / total_steps, 1), each operand is moved from its
+ * full-precision value toward its quantised value by lambda, v + lambda
+ * (Q(v) - v), so lambda = 0 is the dense layer and lambda = 1 the BitLinear
+ * layer:
+ *   a[m][k] = n + lambda (d_x[m] q_x[m][k] - n),  n = x[m][k] gain[k] rstd[m]
+ *             (RMSNorm output; q_x, d_x the int8 codes and scale of
+ *             bitnet_quant_act, rstd = 1 / sqrt(mean_k x^2 + eps))
+ *   b[o][k] = W[o][k] + lambda (d_w q_w[o][k] - W[o][k])
+ *   y[m][o] = sum_k a[m][k] b[o][k]
+ * computed in float32 (operands blended in float32, float32 matrix-core sums).
+ *
+ *   x        in   bf16 [M][K], 16-byte aligned; gain [K] or NULL, eps >= 0.
+ *   W        in   float32 [N][K] full-precision weights, 16-byte aligned.
+ *   packed, w_scale  in  bitnet_pack_weights(W) outputs (hadamard = 0).
+ *   lambda        in [0, 1] (BITNET_ERR_VALUE otherwise).
+ *   y        out  float32 [M][N], 4-byte aligned.
+ *   workspace     at least bitnet_linear_forward_blend_workspace_bytes(M, K)
+ *                 bytes, 16-byte aligned (blended activations, int8 codes,
+ *                 scales); contents undefined afterwards.
+ * M = 0 or N = 0 is a no-op.
+ */
+size_t bitnet_linear_forward_blend_workspace_bytes(int64_t M, int64_t K);
+int bitnet_linear_forward_blend(const uint16_t* x, const float* gain, float eps, const float* W,
+                                const uint8_t* packed, const float* w_scale, float lambda, int64_t M, int64_t N,
+                                int64_t K, float* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement reference, no passage of the pages: one plain read of `bytes`
  * bytes of device memory at `buf` (16-byte aligned, bytes a multiple of 16 and
  * >= 16), each byte once with 16-byte loads over the whole chip.  Its rate is

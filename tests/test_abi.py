@@ -321,3 +321,30 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define BITNET_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == bt.NOALLOC_SCRATCH_BYTES
+
+
+def test_blend_argument_errors(L):
+    f = L.bitnet_linear_forward_blend
+    v = ctypes.c_void_p
+    ws = L.bitnet_linear_forward_blend_workspace_bytes(4, 256)
+    assert ws >= 4 * 256 * 5
+    ok = dict(x=v(A16), gain=None, eps=1e-5, W=v(A16), packed=v(A16), w=v(A4), lam=0.5, M=4, N=8, K=256,
+              y=v(A4), ws=v(A16), wsb=ws)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["gain"], ctypes.c_float(a["eps"]), a["W"], a["packed"], a["w"],
+                 ctypes.c_float(a["lam"]), a["M"], a["N"], a["K"], a["y"], a["ws"], a["wsb"], None)
+
+    assert call(lam=-0.1) == 7
+    assert call(lam=1.5) == 7
+    assert call(lam=float("nan")) == 7
+    assert call(K=100) == 2
+    assert call(M=-1) == 2
+    assert call(eps=-1.0) == 7
+    assert call(W=None) == 1
+    assert call(ws=None) == 1
+    assert call(x=v(A4)) == 4
+    assert call(gain=v(A4)) == 4
+    assert call(wsb=ws - 1) == 5
+    assert call(M=0, x=None, W=None) == 0
