@@ -70,6 +70,10 @@ def load(path: str):
     lib.oracle_pack_base3.restype = i32
     lib.oracle_unpack_base3.argtypes = [p, i64, i64, i64, p]
     lib.oracle_unpack_base3.restype = i64
+    lib.oracle_pack_nibbles.argtypes = [p, i64, i64, p]
+    lib.oracle_pack_nibbles.restype = i32
+    lib.oracle_unpack_nibbles.argtypes = [p, i64, i64, p]
+    lib.oracle_unpack_nibbles.restype = i32
     lib.oracle_warmup_lambda.argtypes = [i64, i64]
     lib.oracle_warmup_lambda.restype = ctypes.c_double
     lib.oracle_linear_forward_blend.argtypes = [p, p, f32, i64, i64, p, i64, ctypes.c_double, p]
@@ -252,6 +256,25 @@ class Oracle:
         q = np.empty((N, K), np.int8)
         bad = self.lib.oracle_unpack_base3(_ptr(packed3), N, K, row_bytes, _ptr(q))
         return q, int(bad)
+
+    def pack_nibbles(self, q: np.ndarray) -> np.ndarray:
+        """int4 codes int8 [M][K] -> uint8 [M][K/2], code 2j in the low nibble
+        of byte j (two's complement)."""
+        q = _c(q, np.int8)
+        M, K = q.shape
+        out = np.empty((M, K // 2), np.uint8)
+        if self.lib.oracle_pack_nibbles(_ptr(q), M, K, _ptr(out)) != 0:
+            raise ValueError(f"oracle_pack_nibbles rejected K={K} or a code outside [-8, 7]")
+        return out
+
+    def unpack_nibbles(self, packed: np.ndarray) -> np.ndarray:
+        """uint8 [M][K/2] -> int4 codes int8 [M][K]."""
+        packed = _c(packed, np.uint8)
+        M, half = packed.shape
+        q = np.empty((M, 2 * half), np.int8)
+        if self.lib.oracle_unpack_nibbles(_ptr(packed), M, 2 * half, _ptr(q)) != 0:
+            raise ValueError("oracle_unpack_nibbles rejected its arguments")
+        return q
 
     def warmup_lambda(self, step: int, total: int) -> float:
         """min(step / total, 1), 0 for step <= 0, 1 for total <= 0."""

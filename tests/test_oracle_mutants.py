@@ -15,6 +15,7 @@ from oracle import build as oracle_build
 import test_oracle_backward_pins as bpins
 import test_oracle_base3_pins as b3pins
 import test_oracle_blend_pins as blpins
+import test_oracle_nibble_pins as nbpins
 import test_oracle_pins as pins
 
 MUTANTS = {
@@ -82,6 +83,13 @@ MUTANTS = {
     "blend: dequantised weights without d_w": ("const double wt = d_w * (double)qw[o * K + k];",
                                                "const double wt = (double)qw[o * K + k];"),
     "schedule: no clamp at 1": ("if (step >= total) return 1.0;\n", "\n"),
+    "nibbles: code pair swapped": ("out[m * (K / 2) + j] = (uint8_t)((lo & 15) | ((hi & 15) << 4));",
+                                   "out[m * (K / 2) + j] = (uint8_t)((hi & 15) | ((lo & 15) << 4));"),
+    "nibbles: unpack without sign extension": ("q[m * K + 2 * j] = (int8_t)(lo >= 8 ? lo - 16 : lo);",
+                                               "q[m * K + 2 * j] = (int8_t)(lo);"),
+    "nibbles: range check dropped": ("if (lo < -8 || lo > 7 || hi < -8 || hi > 7) bad = 1;", ""),
+    "nibbles: high nibble taken from the low bits": ("const int lo = b & 15, hi = b >> 4;",
+                                                     "const int lo = b & 15, hi = b & 15;"),
 }
 
 # Pins run against every mutant (the parametrised ones at a representative size).
@@ -125,6 +133,11 @@ PIN_CALLS = [
     (blpins.test_lambda_one_is_the_bitlinear_layer, {"gain": True}),
     (blpins.test_lambda_zero_is_the_dense_layer, {"gain": True}),
     (blpins.test_blend_is_quadratic_in_lambda_over_both_operands, {"lam": 0.5}),
+    (nbpins.test_hand_computed_bytes, {}),
+    (nbpins.test_code_pairs_to_a_byte_is_a_bijection, {}),
+    (nbpins.test_unpack_against_a_sign_extension_formula, {}),
+    (nbpins.test_codes_outside_int4_are_rejected, {}),
+    (nbpins.test_hadamard_codes_round_trip, {"M": 3, "K": 256}),
 ]
 
 
