@@ -258,13 +258,14 @@ class Oracle:
         return q, int(bad)
 
     def pack_nibbles(self, q: np.ndarray) -> np.ndarray:
-        """int4 codes int8 [M][K] -> uint8 [M][K/2], code 2j in the low nibble
-        of byte j (two's complement)."""
+        """int4 codes int8 [M][K] -> uint8 [M][K/2]: in each group g of 16 codes,
+        byte 8g + j holds code 16g + j (low nibble) and 16g + 8 + j (high
+        nibble), two's complement."""
         q = _c(q, np.int8)
         M, K = q.shape
         out = np.empty((M, K // 2), np.uint8)
         if self.lib.oracle_pack_nibbles(_ptr(q), M, K, _ptr(out)) != 0:
-            raise ValueError(f"oracle_pack_nibbles rejected K={K} or a code outside [-8, 7]")
+            raise ValueError(f"oracle_pack_nibbles rejected K={K} (a multiple of 16) or a code outside [-8, 7]")
         return out
 
     def unpack_nibbles(self, packed: np.ndarray) -> np.ndarray:

@@ -41,8 +41,9 @@
  *   - The Hadamard transform is the unnormalised Sylvester-order transform,
  *     computed by butterflies with the stage distance ascending 1, 2, 4, ...;
  *     its 1/sqrt(K) normalisation is folded into the float scales.
- *   - Packed int4 storage: two codes per byte in natural order, 4-bit two's
- *     complement, code 2j in the low nibble of byte j.
+ *   - Packed int4 storage: two codes per byte, 4-bit two's complement; in
+ *     each group of 16 codes, byte j holds code j in its low nibble and code
+ *     8 + j in its high nibble (the slot order of the 2-bit weight packing).
  *   - Packed layout: row n of the [N][K] weight matrix owns K/4 bytes; the
  *     32-bit little-endian word g of the row holds weights 16g .. 16g+15, and
  *     weight 16g + 4i + b lives in bits 2i..2i+1 of byte b of that word.  The
@@ -312,21 +313,25 @@ int oracle_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, i
 
 /*
  * Packed storage of the int4 codes ([V2] "방법론": the 4-bit activations take
- * half a byte each).  The pages fix no byte layout; the one used here is
- * natural order, two's complement, code 2j in the low nibble of byte j and
- * code 2j+1 in its high nibble:
- *   out[m][j] = (q[m][2j] & 15) | ((q[m][2j+1] & 15) << 4).
- * q [M][K] (K even) -> out [M][K/2].  Returns -1 on a bad shape or on a code
- * outside [-8, 7] (such a code has no 4-bit two's complement form).
+ * half a byte each).  The pages fix no byte layout.  The one used here packs
+ * each group of 16 consecutive codes into 8 bytes the way the 2-bit weight
+ * packing places its fields: nibble slot i (0 low, 1 high) of byte j holds
+ * code 16g + 8i + j, in 4-bit two's complement:
+ *   out[m][8g + j] = (q[m][16g + j] & 15) | ((q[m][16g + 8 + j] & 15) << 4).
+ * q [M][K] (K a multiple of 16) -> out [M][K/2].  Returns -1 on a bad shape or
+ * on a code outside [-8, 7] (such a code has no 4-bit two's complement form).
  */
 int oracle_pack_nibbles(const int8_t* q, int64_t M, int64_t K, uint8_t* out) {
-    if (M < 0 || K < 2 || K % 2 != 0) return -1;
+    if (M < 0 || K < 16 || K % 16 != 0) return -1;
     int bad = 0;
     for (int64_t m = 0; m < M; m++) {
-        for (int64_t j = 0; j < K / 2; j++) {
-            const int lo = q[m * K + 2 * j], hi = q[m * K + 2 * j + 1];
-            if (lo < -8 || lo > 7 || hi < -8 || hi > 7) bad = 1;
-            out[m * (K / 2) + j] = (uint8_t)((lo & 15) | ((hi & 15) << 4));
+        for (int64_t g = 0; g < K / 16; g++) {
+            for (int64_t j = 0; j < 8; j++) {
+                const int lo = q[m * K + 16 * g + j];
+                const int hi = q[m * K + 16 * g + 8 + j];
+                if (lo < -8 || lo > 7 || hi < -8 || hi > 7) bad = 1;
+                out[m * (K / 2) + 8 * g + j] = (uint8_t)((lo & 15) | ((hi & 15) << 4));
+            }
         }
     }
     return bad ? -1 : 0;
@@ -334,13 +339,15 @@ int oracle_pack_nibbles(const int8_t* q, int64_t M, int64_t K, uint8_t* out) {
 
 /* The inverse: nibble v in 0..15 is the code v - 16 if v >= 8, else v. */
 int oracle_unpack_nibbles(const uint8_t* packed, int64_t M, int64_t K, int8_t* q) {
-    if (M < 0 || K < 2 || K % 2 != 0) return -1;
+    if (M < 0 || K < 16 || K % 16 != 0) return -1;
     for (int64_t m = 0; m < M; m++) {
-        for (int64_t j = 0; j < K / 2; j++) {
-            const int b = packed[m * (K / 2) + j];
-            const int lo = b & 15, hi = b >> 4;
-            q[m * K + 2 * j] = (int8_t)(lo >= 8 ? lo - 16 : lo);
-            q[m * K + 2 * j + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+        for (int64_t g = 0; g < K / 16; g++) {
+            for (int64_t j = 0; j < 8; j++) {
+                const int b = packed[m * (K / 2) + 8 * g + j];
+                const int lo = b & 15, hi = b >> 4;
+                q[m * K + 16 * g + j] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+                q[m * K + 16 * g + 8 + j] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+            }
         }
     }
     return 0;

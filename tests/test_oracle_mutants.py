@@ -83,10 +83,12 @@ MUTANTS = {
     "blend: dequantised weights without d_w": ("const double wt = d_w * (double)qw[o * K + k];",
                                                "const double wt = (double)qw[o * K + k];"),
     "schedule: no clamp at 1": ("if (step >= total) return 1.0;\n", "\n"),
-    "nibbles: code pair swapped": ("out[m * (K / 2) + j] = (uint8_t)((lo & 15) | ((hi & 15) << 4));",
-                                   "out[m * (K / 2) + j] = (uint8_t)((hi & 15) | ((lo & 15) << 4));"),
-    "nibbles: unpack without sign extension": ("q[m * K + 2 * j] = (int8_t)(lo >= 8 ? lo - 16 : lo);",
-                                               "q[m * K + 2 * j] = (int8_t)(lo);"),
+    "nibbles: code pair swapped": ("out[m * (K / 2) + 8 * g + j] = (uint8_t)((lo & 15) | ((hi & 15) << 4));",
+                                   "out[m * (K / 2) + 8 * g + j] = (uint8_t)((hi & 15) | ((lo & 15) << 4));"),
+    "nibbles: high nibble from the next code": ("const int hi = q[m * K + 16 * g + 8 + j];",
+                                                "const int hi = q[m * K + 16 * g + 2 * j + 1];"),
+    "nibbles: unpack without sign extension": ("q[m * K + 16 * g + j] = (int8_t)(lo >= 8 ? lo - 16 : lo);",
+                                               "q[m * K + 16 * g + j] = (int8_t)(lo);"),
     "nibbles: range check dropped": ("if (lo < -8 || lo > 7 || hi < -8 || hi > 7) bad = 1;", ""),
     "nibbles: high nibble taken from the low bits": ("const int lo = b & 15, hi = b >> 4;",
                                                      "const int lo = b & 15, hi = b & 15;"),
@@ -134,10 +136,11 @@ PIN_CALLS = [
     (blpins.test_lambda_zero_is_the_dense_layer, {"gain": True}),
     (blpins.test_blend_is_quadratic_in_lambda_over_both_operands, {"lam": 0.5}),
     (nbpins.test_hand_computed_bytes, {}),
+    (nbpins.test_single_code_positions, {}),
     (nbpins.test_code_pairs_to_a_byte_is_a_bijection, {}),
     (nbpins.test_unpack_against_a_sign_extension_formula, {}),
     (nbpins.test_codes_outside_int4_are_rejected, {}),
-    (nbpins.test_hadamard_codes_round_trip, {"M": 3, "K": 256}),
+    (nbpins.test_hadamard_codes_round_trip, {}),
 ]
 
 
