@@ -647,22 +647,39 @@ def hadamard_bench(args, dev, bt, torch, synth):
         qs = torch.empty(M, dtype=torch.int32, device=dev)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         xq6 = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=dev)
+        xq4 = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
         hq = lambda: bt.hadamard_quant_act(x, None, 1e-5, out=(xq, xs, qs))
         gemm = lambda: bt.linear_forward(xq, xs, qs, packed, w_scale, out=y)
         hq6 = lambda: bt.hadamard_quant_act_f6(x, None, 1e-5, out=(xq6, xs, qs))
         gemm6 = lambda: bt.linear_forward_f6(xq6, xs, qs, packed, w_scale, out=y)
+        hq4 = lambda: bt.hadamard_quant_act_i4(x, None, 1e-5, out=(xq4, xs, qs))
+        gemm4 = lambda: bt.linear_forward_i4(xq4, xs, qs, packed, w_scale, out=y)
+        # one token of the same layer: the GEMVs on int8 and on packed 4-bit codes
+        y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
+        gemv = lambda: bt.linear_forward(xq[:1], xs[:1], qs[:1], packed, w_scale, out=y1)
+        gemv4 = lambda: bt.linear_forward_i4(xq4[:1], xs[:1], qs[:1], packed, w_scale, out=y1)
         for _ in range(5):
             hq()
             gemm()
             hq6()
             gemm6()
+            hq4()
+            gemm4()
+            gemv()
+            gemv4()
         torch.cuda.synchronize()
         hq_us = time_launches(hq, args.prefill_iters, bt)
         gemm_us = time_launches(gemm, args.prefill_iters, bt)
         hq6_us = time_launches(hq6, args.prefill_iters, bt)
         gemm6_us = time_launches(gemm6, args.prefill_iters, bt)
+        hq4_us = time_launches(hq4, args.prefill_iters, bt)
+        gemm4_us = time_launches(gemm4, args.prefill_iters, bt)
+        gemv_us = time_launches(gemv, args.prefill_iters, bt)
+        gemv4_us = time_launches(gemv4, args.prefill_iters, bt)
         hq_bytes = M * K * 2 + M * K + 8 * M
         hq6_bytes = M * K * 2 + M * K // 4 * 3 + 8 * M
+        hq4_bytes = M * K * 2 + M * K // 2 + 8 * M
+        gemv_bytes = N * K // 4 + K + 4 * N
         ops = 2.0 * M * N * K
         out.append({"M": M, "K": K, "N": N,
                     "fwht_int4_us": round(hq_us, 2),
@@ -674,7 +691,15 @@ def hadamard_bench(args, dev, bt, torch, synth):
                            "fwht_e3m2_GB_s": round(hq6_bytes / hq6_us / 1e3, 1),
                            "gemm_fp4xfp6_us": round(gemm6_us, 2),
                            "gemm_fp4xfp6_TOPS": round(ops / (gemm6_us * 1e-6) / 1e12, 1),
-                           "gemm_fp4xfp6_frac_fp6_peak": round(ops / (gemm6_us * 1e-6) / 1e12 / FP6_PEAK_TOPS, 4)}})
+                           "gemm_fp4xfp6_frac_fp6_peak": round(ops / (gemm6_us * 1e-6) / 1e12 / FP6_PEAK_TOPS, 4)},
+                    "i4": {"fwht_nibble_us": round(hq4_us, 2),
+                           "fwht_nibble_GB_s": round(hq4_bytes / hq4_us / 1e3, 1),
+                           "fwht_nibble_frac_hbm": round(hq4_bytes / hq4_us / 1e3 / HBM_PEAK_GBS, 4),
+                           "gemm_nibble_us": round(gemm4_us, 2),
+                           "gemm_nibble_TOPS": round(ops / (gemm4_us * 1e-6) / 1e12, 1),
+                           "gemv_m1_int8_us": round(gemv_us, 2),
+                           "gemv_m1_nibble_us": round(gemv4_us, 2),
+                           "gemv_m1_nibble_GB_s": round((gemv_bytes - K // 2) / gemv4_us / 1e3, 1)}})
     return out
 
 

@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
     L.bitnet_hadamard_quant_act_f6.restype = i32
     L.bitnet_linear_forward_f6.argtypes = [p, p, p, p, p, i64, i64, i64, p, p, p]
     L.bitnet_linear_forward_f6.restype = i32
+    L.bitnet_hadamard_quant_act_i4.argtypes = [p, p, f32, i64, i64, p, p, p, p]
+    L.bitnet_hadamard_quant_act_i4.restype = i32
+    L.bitnet_linear_forward_i4.argtypes = [p, p, p, p, p, i64, i64, i64, p, p, p]
+    L.bitnet_linear_forward_i4.restype = i32
     L.bitnet_bitlinear_forward.argtypes = [p, p, f32, p, p, i64, i64, i64, p, p, p, p, p, p]
     L.bitnet_bitlinear_forward.restype = i32
     L.bitnet_bitlinear_forward_grouped.argtypes = [p, p, f32, p, p, p, i32, i64, i64, p, p, p, p,
@@ -352,6 +356,23 @@ def hadamard_quant_act_f6(x, gain=None, eps: float = 1e-5, out=None):
     return xq6, x_scale, x_qsum
 
 
+def hadamard_quant_act_i4(x, gain=None, eps: float = 1e-5, out=None):
+    """bf16 [M][K] -> (xq4 uint8 [M][K/2] packed 4-bit codes, x_scale float32 [M],
+    x_qsum int32 [M]) (bitnet_hadamard_quant_act_i4)."""
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    M, K = x.shape
+    _gain(gain, K, dev)
+    xq4, x_scale, x_qsum = (None, None, None) if out is None else out
+    xq4 = _output(xq4, "xq4", torch.uint8, (M, K // 2), dev)
+    x_scale = _output(x_scale, "x_scale", torch.float32, (M,), dev)
+    x_qsum = _output(x_qsum, "x_qsum", torch.int32, (M,), dev)
+    _check(lib().bitnet_hadamard_quant_act_i4(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K,
+                                              _ptr(xq4), _ptr(x_scale), _ptr(x_qsum), _stream(dev)))
+    return xq4, x_scale, x_qsum
+
+
 def _contraction_args(x_scale, x_qsum, packed, w_scale, M, K, dev):
     torch = _torch()
     _require_shape(x_scale, "x_scale", torch.float32, (M,), dev)
@@ -380,6 +401,26 @@ def linear_forward_f6(xq6, x_scale, x_qsum, packed, w_scale, return_acc: bool = 
     if return_acc or acc_out is not None:
         acc_out = _output(acc_out, "acc_out", torch.int32, (M, N), dev)
     _check(lib().bitnet_linear_forward_f6(_ptr(xq6), _ptr(x_scale), _ptr(x_qsum), _ptr(packed),
+                                          _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out),
+                                          _stream(dev)))
+    return (out, acc_out) if acc_out is not None else out
+
+
+def linear_forward_i4(xq4, x_scale, x_qsum, packed, w_scale, return_acc: bool = False, out=None,
+                      acc_out=None):
+    """Contraction + dequantisation on packed 4-bit codes (bitnet_linear_forward_i4);
+    returns y float32 [M][N], or (y, acc int32 [M][N]) when return_acc or acc_out
+    is given."""
+    torch = _torch()
+    _require(xq4, "xq4", torch.uint8, 2)
+    dev = xq4.device
+    M = xq4.shape[0]
+    K = xq4.shape[1] * 2
+    N = _contraction_args(x_scale, x_qsum, packed, w_scale, M, K, dev)
+    out = _output(out, "out", torch.float32, (M, N), dev)
+    if return_acc or acc_out is not None:
+        acc_out = _output(acc_out, "acc_out", torch.int32, (M, N), dev)
+    _check(lib().bitnet_linear_forward_i4(_ptr(xq4), _ptr(x_scale), _ptr(x_qsum), _ptr(packed),
                                           _ptr(w_scale), M, N, K, _ptr(out), _ptr(acc_out),
                                           _stream(dev)))
     return (out, acc_out) if acc_out is not None else out

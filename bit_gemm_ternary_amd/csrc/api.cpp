@@ -204,6 +204,45 @@ int bitnet_hadamard_quant_act_f6(const uint16_t* x, const float* gain, float eps
                       fn);
 }
 
+int bitnet_hadamard_quant_act_i4(const uint16_t* x, const float* gain, float eps, int64_t M,
+                                 int64_t K, uint8_t* xq4, float* x_scale, int32_t* x_qsum,
+                                 void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_hadamard_quant_act_i4";
+    int s = validate_quant(x, gain, eps, M, K, reinterpret_cast<int8_t*>(xq4), x_scale, x_qsum,
+                           true, fn);
+    if (s != BITNET_OK || M == 0) return s;
+    return hip_status(bitnet::launch_hadamard_quant_act_i4(x, gain, eps, M, K, std::sqrt((double)K),
+                                                           xq4, x_scale, x_qsum,
+                                                           (hipStream_t)stream),
+                      fn);
+}
+
+int bitnet_linear_forward_i4(const uint8_t* xq4, const float* x_scale, const int32_t* x_qsum,
+                             const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, float* y, int32_t* acc, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_linear_forward_i4";
+    if (M < 0 || M > kMaxRows || N < 0 || N > kMaxRows)
+        return fail(BITNET_ERR_SHAPE, "%s: M=%lld or N=%lld out of range", fn, (long long)M, (long long)N);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK) return s;
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!xq4 || !x_scale || !x_qsum || !packed || !w_scale || !y)
+        return fail(BITNET_ERR_NULL, "%s: only acc may be NULL", fn);
+    if (!aligned(xq4, 16) || !aligned(packed, 16))
+        return fail(BITNET_ERR_ALIGN, "%s: xq4 and packed must be 16-byte aligned", fn);
+    if (!aligned(x_scale, 4) || !aligned(x_qsum, 4) || !aligned(w_scale, 4) || !aligned(y, 4) ||
+        (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "%s: scales, sums, y and acc must be 4-byte aligned", fn);
+    hipStream_t st = (hipStream_t)stream;
+    const bitnet::RowScales scales = bitnet::single_group(w_scale, N);
+    hipError_t e = bitnet::gemv_supported(M, K)
+                       ? bitnet::launch_gemv_i4(xq4, x_scale, x_qsum, packed, scales, M, N, K, y, acc, st)
+                       : bitnet::launch_gemm_i4(xq4, x_scale, x_qsum, packed, scales, M, N, K, y, acc, st);
+    return hip_status(e, fn);
+}
+
 int bitnet_linear_forward_f6(const uint8_t* xq6, const float* x_scale, const int32_t* x_qsum,
                              const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
                              int64_t K, float* y, int32_t* acc, void* stream) {

@@ -63,7 +63,10 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int BN_, int BM_, int WN_, int WM_, int OCC_, int S_ = 2, bool F6_ = false, int KS_ = 1>
+// Activation formats of the tiled kernel.
+constexpr int kXInt8 = 0, kXE3M2 = 1, kXNibble = 2;
+
+template <int BN_, int BM_, int WN_, int WM_, int OCC_, int S_ = 2, int XF_ = kXInt8, int KS_ = 1>
 struct GemmCfg {
     static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
     static constexpr int S = S_;                    // LDS stage buffers (S - 1 stages in flight)
@@ -72,11 +75,13 @@ struct GemmCfg {
     // are added through LDS at the end.  With small tiles a single group runs
     // one wave per SIMD, whose stage work (LDS reads, unpacking, dependent
     // MFMAs) has nothing to overlap with; a second group fills that gap.
-    // Activation format: int8 codes, or 6-bit E3M2 codes (F6: 192 bytes per
+    // Activation format: int8 codes, 6-bit E3M2 codes (F6: 192 bytes per
     // row per stage, padded to 208 in LDS so 16-byte reads of 16 consecutive
-    // rows fall in distinct bank groups).
-    static constexpr bool F6 = F6_;
-    static constexpr int X_ROW = F6 ? 208 : kBK;     // LDS bytes per activation row
+    // rows fall in distinct bank groups), or packed 4-bit codes (I4: 128 bytes
+    // per row per stage, eight 16-byte slots stored at s ^ (r & 7)).
+    static constexpr bool F6 = XF_ == kXE3M2;
+    static constexpr bool I4 = XF_ == kXNibble;
+    static constexpr int X_ROW = F6 ? 208 : (I4 ? kBK / 2 : kBK);   // LDS bytes per activation row
     static constexpr int X_ROW_SLOTS = X_ROW / 16;
     static constexpr int STEPS = F6 ? 4 : 8;         // MFMA K steps per stage (64 or 32 K each)
     static constexpr int OCC = OCC_;                // workgroups per CU the tile is sized for
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
     // Buffer resources cover only this block's valid rows.
     const int x_rows = (int)min((int64_t)C::BM, (int64_t)M - m0);
     const int w_rows = (int)min((int64_t)C::BN, (int64_t)N - n0);
-    const int x_row_bytes = C::F6 ? K / 4 * 3 : K;   // activation bytes per token in HBM
+    const int x_row_bytes = C::F6 ? K / 4 * 3 : (C::I4 ? K / 2 : K);   // activation bytes per token in HBM
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(X + m0 * x_row_bytes), (short)0, x_rows * x_row_bytes, (int)kBufferWord3);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
@@ -210,6 +215,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
                     const int r = p / C::X_ROW_SLOTS, s = p % C::X_ROW_SLOTS;
                     const int b = k0 / 4 * 3 + 16 * s;             // byte in the token's row
                     off = (live && s < 12 && b < x_row_bytes) ? (uint32_t)(r * x_row_bytes + b) : kOutOfRange;
+                } else if constexpr (C::I4) {
+                    const int r = p >> 3, s = (p & 7) ^ (r & 7);
+                    const int b = k0 / 2 + 16 * s;
+                    off = (live && b < x_row_bytes) ? (uint32_t)(r * x_row_bytes + b) : kOutOfRange;
                 } else {
                     const int r = p >> 4, s = (p & 15) ^ (r & 15);
                     const int k = k0 + 16 * s;
@@ -250,6 +259,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
         const int8_t* xs = &lds[buf][0];
         const int8_t* ws = &lds[buf][C::X_STAGE];
         v4u wv[C::FN][2];
+        v4u xr[C::FM];   // I4: the 16-byte slot holding two K steps' codes
 #pragma unroll
         for (int i = 0; i < C::FN; ++i) {
             const int r = wn * C::TN + i * 32 + fr;
@@ -299,7 +309,21 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
 #pragma unroll
                 for (int j = 0; j < C::FM; ++j) {
                     const int r = wm * C::TM + j * 32 + fr;
-                    b[j] = *reinterpret_cast<const v4i*>(&xs[r * kBK + 16 * ((8 * fh + st) ^ (r & 15))]);
+                    if constexpr (C::I4) {
+                        // Group 8 fh + st of the stage (16 codes in 8 bytes): byte i
+                        // holds codes i and 8 + i, so masking the high nibbles of
+                        // the two dwords (and of the dwords shifted up by 4) gives
+                        // 16 q in natural order, as int8.  The sums are 16 times
+                        // the codes' and are scaled back in the epilogue.
+                        if (st % 2 == 0)
+                            xr[j] = *reinterpret_cast<const v4u*>(
+                                &xs[r * C::X_ROW + 16 * ((4 * fh + st / 2) ^ (r & 7))]);
+                        const uint32_t lo = xr[j][2 * (st % 2)], hi = xr[j][2 * (st % 2) + 1];
+                        b[j] = v4i{(int)((lo << 4) & 0xF0F0F0F0u), (int)((hi << 4) & 0xF0F0F0F0u),
+                                   (int)(lo & 0xF0F0F0F0u), (int)(hi & 0xF0F0F0F0u)};
+                    } else {
+                        b[j] = *reinterpret_cast<const v4i*>(&xs[r * kBK + 16 * ((8 * fh + st) ^ (r & 15))]);
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < C::FN; ++i) {
@@ -399,9 +423,10 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
                         const int nl = i * 32 + 8 * q + 4 * fh;   // wave-local output column
                         const int64_t ng = n0 + wn * C::TN + nl;   // its global column
                         // (the FP4 x FP6 sums are exact integers in float32)
-                        const v4i a = v4i{(int)acc[i][j][4 * q], (int)acc[i][j][4 * q + 1],
-                                          (int)acc[i][j][4 * q + 2], (int)acc[i][j][4 * q + 3]} -
-                                      v4i{qs, qs, qs, qs};
+                        v4i a = v4i{(int)acc[i][j][4 * q], (int)acc[i][j][4 * q + 1],
+                                    (int)acc[i][j][4 * q + 2], (int)acc[i][j][4 * q + 3]};
+                        if constexpr (C::I4) a = a >> 4;   // exact: the sums are multiples of 16
+                        a -= v4i{qs, qs, qs, qs};
                         // Columns past N read row N-1's scale; they are never stored.
                         float4 v;
                         v.x = ((float)a[0] * sx) * scales.of(min(ng, (int64_t)N - 1), dw0);
@@ -586,15 +611,15 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_q
 
 // Tile configurations (weight rows x tokens, waves along N x along M,
 // workgroups per CU, stage buffers, 6-bit activations, K groups).
-template <bool F6>
+template <int XF>
 struct Tiles {
-    using Large = GemmCfg<448, 128, 7, 2, 1, 2, F6>;        // 14 waves, wave tile 64 x 64
-    using Mid = GemmCfg<256, 128, 4, 2, 1, 2, F6>;          // 8 waves, wave tile 64 x 64
-    using Wide = GemmCfg<256, 64, 4, 1, 1, 2, F6>;          // 4 waves, wave tile 64 x 64
-    using TallK3 = GemmCfg<128, 64, 2, 2, 1, 2, F6, 3>;     // 3 K groups of 4 waves (64 x 32)
-    using Tiny = GemmCfg<64, 64, 2, 2, 2, 2, F6>;           // 4 waves, wave tile 32 x 32
-    using TinyK2 = GemmCfg<64, 64, 2, 2, 2, 2, F6, 2>;      // 2 K groups of 4 waves
-    using TinyK4 = GemmCfg<64, 64, 2, 2, 1, 2, F6, 4>;      // 4 K groups of 4 waves
+    using Large = GemmCfg<448, 128, 7, 2, 1, 2, XF>;        // 14 waves, wave tile 64 x 64
+    using Mid = GemmCfg<256, 128, 4, 2, 1, 2, XF>;          // 8 waves, wave tile 64 x 64
+    using Wide = GemmCfg<256, 64, 4, 1, 1, 2, XF>;          // 4 waves, wave tile 64 x 64
+    using TallK3 = GemmCfg<128, 64, 2, 2, 1, 2, XF, 3>;     // 3 K groups of 4 waves (64 x 32)
+    using Tiny = GemmCfg<64, 64, 2, 2, 2, 2, XF>;           // 4 waves, wave tile 32 x 32
+    using TinyK2 = GemmCfg<64, 64, 2, 2, 2, 2, XF, 2>;      // 2 K groups of 4 waves
+    using TinyK4 = GemmCfg<64, 64, 2, 2, 1, 2, XF, 4>;      // 4 K groups of 4 waves
 };
 
 constexpr int64_t kCus = 256;
@@ -606,11 +631,11 @@ constexpr int64_t kCus = 256;
 // a stage's LDS reads and dependent MFMAs with: K groups add waves that work
 // on other stages of the same tile, the more the longer K.  Measured on the
 // prefill, H-BitLinear (M 512) and Llama-block (M 256) shapes.
-template <bool F6>
+template <int XF>
 hipError_t launch_tiled(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                         const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                         int64_t K, float* y, int32_t* acc, hipStream_t stream) {
-    using T = Tiles<F6>;
+    using T = Tiles<XF>;
     if (tiles_of<typename T::Large>(M, N) >= 2 * kCus)
         return launch_cfg<typename T::Large>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     if (tiles_of<typename T::Mid>(M, N) >= kCus)
@@ -647,15 +672,23 @@ hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_
             return launch_skinny<8, 2>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
         return launch_skinny<8, 1>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     }
-    return launch_tiled<false>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    return launch_tiled<kXInt8>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
 }
 
 hipError_t launch_gemm_f6(const uint8_t* xq6, const float* x_scale, const int32_t* x_qsum,
                           const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                           int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
-    return launch_tiled<true>(reinterpret_cast<const int8_t*>(xq6), x_scale, x_qsum, packed, scales, M,
-                              N, K, y, acc, stream);
+    return launch_tiled<kXE3M2>(reinterpret_cast<const int8_t*>(xq6), x_scale, x_qsum, packed, scales, M,
+                                N, K, y, acc, stream);
+}
+
+hipError_t launch_gemm_i4(const uint8_t* xq4, const float* x_scale, const int32_t* x_qsum,
+                          const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    return launch_tiled<kXNibble>(reinterpret_cast<const int8_t*>(xq4), x_scale, x_qsum, packed, scales,
+                                  M, N, K, y, acc, stream);
 }
 
 }  // namespace bitnet

@@ -63,10 +63,17 @@ namespace {
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer descriptor word 3 (gfx9 family)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // offset past every buffer used here: loads 0
 constexpr int kMaxRecords = 0x7fffffff;         // buffer size used for the weight batches
-constexpr int kMaxXRegsChunks = 8;              // MT * CH limit: 16 * MT * CH code VGPRs
+constexpr int kMaxXRegsChunks = 8;
+// Where decode_kernel's codes come from: int8 codes in memory, the fused
+// quantisation of bf16 tokens, or packed 4-bit codes in memory.
+constexpr int kInt8Codes = 0, kFused = 1, kNibbleCodes = 2;              // MT * CH limit: 16 * MT * CH code VGPRs
 
 __device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+// Signed 4-bit dot product of eight nibble lanes, accumulated (v_dot8_i32_i4).
+__device__ __forceinline__ int dot8(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
 }
 __device__ __forceinline__ int dot4_first(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_sdot4((int)a, (int)b, 0, true);
@@ -158,6 +165,7 @@ struct Args {
     const float* gain;       // fused: [K] or NULL
     float eps;
     const int8_t* xq;        // standalone: codes [MT][K]
+    const uint8_t* xq4;      // standalone, nibbles: codes [MT][K/2]
     const float* x_scale;    // standalone: d_x [MT]
     const int32_t* x_qsum;   // standalone: sum of codes [MT]
     const uint8_t* packed;   // [N][K/4]
@@ -172,8 +180,11 @@ struct Args {
 
 // MT tokens, CH 16-byte chunks per lane per row (K <= CH * 4096), NT threads,
 // RB rows per batch, MULTI: more than RB rows per wave.
-template <int MT, int CH, int NT, int RB, bool MULTI, bool FUSED>
+template <int MT, int CH, int NT, int RB, bool MULTI, int MODE>
 __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
+    constexpr bool FUSED = MODE == kFused;
+    constexpr bool I4 = MODE == kNibbleCodes;
+    constexpr int XD = I4 ? 8 : 16;                // code dwords per chunk per token
     constexpr int NW = NT / kWave;
     constexpr int MTP = MT == 3 ? 4 : MT;  // tokens per row in the reduction (a power of 2)
     constexpr int NV = MTP * RB;
@@ -227,7 +238,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     // hold both sets, the token and the codes at once.
     constexpr bool kLateSecondSet = MT * CH >= 6;
 
-    uint32_t xv[MT][CH][16];  // codes of my chunks: chunk c covers x[64c .. 64c+63]
+    uint32_t xv[MT][CH][XD];  // codes of my chunks: chunk c covers x[64c .. 64c+63]
     int tok_sum[MT];
     float tok_scale[MT];
     uint4 w0[RB][CH], w1[RB][CH];
@@ -393,6 +404,33 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
                 }
             }
         }
+    } else if constexpr (I4) {
+        // Nibble codes of my chunks (32 bytes per chunk) from memory, ahead of
+        // the weights: dwords 2d and 2d + 1 of a chunk hold the 16-code group d.
+        const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)a.xq4, (short)0, MT * (K / 2), (int)kBufferWord3);
+#pragma unroll
+        for (int tok = 0; tok < MT; ++tok)
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int c = lane + kWave * j;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint4 v = load16(qres, c < nchunk ? (uint32_t)(tok * (K / 2) + 32 * c + 16 * q)
+                                                            : kOutOfRange);
+                    xv[tok][j][4 * q] = v.x;
+                    xv[tok][j][4 * q + 1] = v.y;
+                    xv[tok][j][4 * q + 2] = v.z;
+                    xv[tok][j][4 * q + 3] = v.w;
+                }
+            }
+#pragma unroll
+        for (int tok = 0; tok < MT; ++tok) {
+            tok_sum[tok] = a.x_qsum[tok];
+            tok_scale[tok] = a.x_scale[tok];
+        }
+        load(w0, 0);
+        if constexpr (MULTI) load(w1, RB);
     } else {
         // Codes of my chunks straight from memory, ahead of the weights.
         const __amdgpu_buffer_rsrc_t qres = __builtin_amdgcn_make_buffer_rsrc(
@@ -431,20 +469,39 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
             if (has_row(i0 + rb)) {  // wave-uniform
 #pragma unroll
                 for (int tok = 0; tok < MT; ++tok) {
-                    int s03 = 0, s1 = 0, s2 = 0;
+                    if constexpr (I4) {
+                        // Fields of slots 0 and 2 (w & 0x33333333) and of slots 1
+                        // and 3 ((w >> 2) & 0x33333333) are 4-bit lanes holding
+                        // q + 1 for the weights 16g + j, 16g + 8 + j and
+                        // 16g + 4 + j, 16g + 12 + j: the nibble order of the
+                        // group's two code dwords.
+                        int s = 0;
 #pragma unroll
-                    for (int j = 0; j < CH; ++j) {
-                        const uint32_t ws[4] = {w[rb][j].x, w[rb][j].y, w[rb][j].z, w[rb][j].w};
+                        for (int j = 0; j < CH; ++j) {
+                            const uint32_t ws[4] = {w[rb][j].x, w[rb][j].y, w[rb][j].z, w[rb][j].w};
 #pragma unroll
-                        for (int d = 0; d < 4; ++d) {
-                            const uint32_t word = ws[d];
-                            s03 = dot4(word & 0x03030303u, xv[tok][j][4 * d + 0], s03);
-                            s1 = dot4(word & 0x0C0C0C0Cu, xv[tok][j][4 * d + 1], s1);
-                            s2 = dot4(word & 0x30303030u, xv[tok][j][4 * d + 2], s2);
-                            s03 = dot4((word >> 6) & 0x03030303u, xv[tok][j][4 * d + 3], s03);
+                            for (int d = 0; d < 4; ++d) {
+                                s = dot8(ws[d] & 0x33333333u, xv[tok][j][2 * d], s);
+                                s = dot8((ws[d] >> 2) & 0x33333333u, xv[tok][j][2 * d + 1], s);
+                            }
                         }
+                        p[rb * MTP + tok] = s;
+                    } else {
+                        int s03 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+                        for (int j = 0; j < CH; ++j) {
+                            const uint32_t ws[4] = {w[rb][j].x, w[rb][j].y, w[rb][j].z, w[rb][j].w};
+#pragma unroll
+                            for (int d = 0; d < 4; ++d) {
+                                const uint32_t word = ws[d];
+                                s03 = dot4(word & 0x03030303u, xv[tok][j][4 * d + 0], s03);
+                                s1 = dot4(word & 0x0C0C0C0Cu, xv[tok][j][4 * d + 1], s1);
+                                s2 = dot4(word & 0x30303030u, xv[tok][j][4 * d + 2], s2);
+                                s03 = dot4((word >> 6) & 0x03030303u, xv[tok][j][4 * d + 3], s03);
+                            }
+                        }
+                        p[rb * MTP + tok] = s03 + (s1 >> 2) + (s2 >> 4);
                     }
-                    p[rb * MTP + tok] = s03 + (s1 >> 2) + (s2 >> 4);
                 }
             }
         }
@@ -743,35 +800,35 @@ int chunks_per_lane(int64_t K) { return (int)((K / 64 + kWave - 1) / kWave); }
 // The chunk counts instantiated: 1, 2, 3, 4, 6, 8 (larger counts are not supported).
 int rounded_ch(int ch) { return ch <= 4 ? ch : (ch <= 6 ? 6 : (ch <= 8 ? 8 : ch)); }
 
-template <int MT, int CH, int NT, int RB, bool MULTI, bool FUSED>
+template <int MT, int CH, int NT, int RB, bool MULTI, int MODE>
 hipError_t launch_shape(const Args& a, int64_t waves, hipStream_t stream) {
     constexpr int NW = NT / kWave;
     const int64_t blocks = (waves + NW - 1) / NW;
-    return launch_kernel((decode_kernel<MT, CH, NT, RB, MULTI, FUSED>), dim3((unsigned)blocks),
+    return launch_kernel((decode_kernel<MT, CH, NT, RB, MULTI, MODE>), dim3((unsigned)blocks),
                          dim3(NT), 0, stream, a);
 }
 
 // Pick RB (and MULTI) for a wave owning up to rpw rows.
-template <int MT, int CH, int NT, bool FUSED>
+template <int MT, int CH, int NT, int MODE>
 hipError_t launch_rb(const Args& a, int64_t rpw, int64_t waves, hipStream_t stream) {
     constexpr int CAP = max_batch<CH>();
     constexpr int MTP = MT == 3 ? 4 : MT;
     constexpr int CAP_MT = MTP * CAP <= kWave ? CAP : kWave / MTP;
-    if (rpw <= 2 && CAP_MT >= 2) return launch_shape<MT, CH, NT, 2, false, FUSED>(a, waves, stream);
+    if (rpw <= 2 && CAP_MT >= 2) return launch_shape<MT, CH, NT, 2, false, MODE>(a, waves, stream);
     if constexpr (CAP_MT >= 4)
-        if (rpw <= 4) return launch_shape<MT, CH, NT, 4, false, FUSED>(a, waves, stream);
+        if (rpw <= 4) return launch_shape<MT, CH, NT, 4, false, MODE>(a, waves, stream);
     if constexpr (CAP_MT >= 8)
-        if (rpw <= 8) return launch_shape<MT, CH, NT, 8, false, FUSED>(a, waves, stream);
+        if (rpw <= 8) return launch_shape<MT, CH, NT, 8, false, MODE>(a, waves, stream);
     if constexpr (CAP_MT >= 16)
-        if (rpw <= 16) return launch_shape<MT, CH, NT, 16, false, FUSED>(a, waves, stream);
+        if (rpw <= 16) return launch_shape<MT, CH, NT, 16, false, MODE>(a, waves, stream);
     // Two alternating register sets: with 6 or more chunks per lane, two sets
     // of two rows next to the codes exceed the register file (the compiler
     // spilled 129 registers at 8 chunks), so each set holds one row.
     constexpr int MRB = MT * CH >= 6 ? 1 : CAP_MT;
-    return launch_shape<MT, CH, NT, MRB, true, FUSED>(a, waves, stream);
+    return launch_shape<MT, CH, NT, MRB, true, MODE>(a, waves, stream);
 }
 
-template <int MT, int CH, bool FUSED>
+template <int MT, int CH, int MODE>
 hipError_t launch_ch(const Args& a, hipStream_t stream) {
     const int64_t N = a.N;
     // 512-thread workgroups (2048 waves) for single tokens and matrices larger
@@ -785,22 +842,22 @@ hipError_t launch_ch(const Args& a, hipStream_t stream) {
         // N = 16384).
         if (CH <= 2 && N >= 16384 && N <= 4096 * max_batch<CH>()) {
             const int64_t rpw = (N + 4095) / 4096;
-            return launch_rb<MT, CH, 512, FUSED>(a, rpw, (N + rpw - 1) / rpw, stream);
+            return launch_rb<MT, CH, 512, MODE>(a, rpw, (N + rpw - 1) / rpw, stream);
         }
         if (N >= 4096 && (N > 4096 || a.K > 4096)) {
             const int64_t rpw = (N + 2047) / 2048;
-            return launch_rb<MT, CH, 512, FUSED>(a, rpw, (N + rpw - 1) / rpw, stream);
+            return launch_rb<MT, CH, 512, MODE>(a, rpw, (N + rpw - 1) / rpw, stream);
         }
     }
     const int64_t rpw = (N + 1023) / 1024;
-    return launch_rb<MT, CH, 256, FUSED>(a, rpw, (N + rpw - 1) / rpw, stream);
+    return launch_rb<MT, CH, 256, MODE>(a, rpw, (N + rpw - 1) / rpw, stream);
 }
 
-template <int MT, bool FUSED>
+template <int MT, int MODE>
 hipError_t dispatch_ch(int ch, const Args& a, hipStream_t stream) {
 #define BITNET_GEMV_CH(C)                                                          \
     if (ch <= C) {                                                                 \
-        if constexpr (MT * C <= kMaxXRegsChunks) return launch_ch<MT, C, FUSED>(a, stream); \
+        if constexpr (MT * C <= kMaxXRegsChunks) return launch_ch<MT, C, MODE>(a, stream); \
         return hipErrorInvalidValue;                                               \
     }
     BITNET_GEMV_CH(1)
@@ -813,14 +870,14 @@ hipError_t dispatch_ch(int ch, const Args& a, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-template <bool FUSED>
+template <int MODE>
 hipError_t dispatch(int64_t M, const Args& a, hipStream_t stream) {
     const int ch = chunks_per_lane(a.K);
     switch (M) {
-        case 1: return dispatch_ch<1, FUSED>(ch, a, stream);
-        case 2: return dispatch_ch<2, FUSED>(ch, a, stream);
-        case 3: return dispatch_ch<3, FUSED>(ch, a, stream);
-        case 4: return dispatch_ch<4, FUSED>(ch, a, stream);
+        case 1: return dispatch_ch<1, MODE>(ch, a, stream);
+        case 2: return dispatch_ch<2, MODE>(ch, a, stream);
+        case 3: return dispatch_ch<3, MODE>(ch, a, stream);
+        case 4: return dispatch_ch<4, MODE>(ch, a, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -876,7 +933,17 @@ hipError_t launch_gemv(const int8_t* xq, const float* x_scale, const int32_t* x_
     Args a{};
     a.xq = xq, a.x_scale = x_scale, a.x_qsum = x_qsum, a.packed = packed, a.scales = scales;
     a.N = (int)N, a.K = (int)K, a.y = y, a.acc = acc;
-    return dispatch<false>(M, a, stream);
+    return dispatch<kInt8Codes>(M, a, stream);
+}
+
+hipError_t launch_gemv_i4(const uint8_t* xq4, const float* x_scale, const int32_t* x_qsum,
+                          const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc, hipStream_t stream) {
+    if (N == 0) return hipSuccess;
+    Args a{};
+    a.xq4 = xq4, a.x_scale = x_scale, a.x_qsum = x_qsum, a.packed = packed, a.scales = scales;
+    a.N = (int)N, a.K = (int)K, a.y = y, a.acc = acc;
+    return dispatch<kNibbleCodes>(M, a, stream);
 }
 
 hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
@@ -891,7 +958,7 @@ hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
         const hipError_t e = dispatch_decode1(a, stream);
         if (e != hipErrorNotSupported) return e;
     }
-    return dispatch<true>(M, a, stream);
+    return dispatch<kFused>(M, a, stream);
 }
 
 }  // namespace bitnet

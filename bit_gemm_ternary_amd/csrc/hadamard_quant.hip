@@ -123,11 +123,17 @@ __device__ __forceinline__ uint32_t e3m2_of_int(int v) {
     return (v < 0 ? 0x20u : 0u) | ((uint32_t)(l + 3) << 2) | m;
 }
 
-// F6 = false: int8 codes, xq [M][K].  F6 = true: 6-bit E3M2 codes, xq
+// Output formats of the codes.
+enum CodeFormat { kInt8 = 0, kE3M2 = 1, kNibble = 2 };
+
+// kInt8: one int8 per code, xq [M][K].  kE3M2: 6-bit E3M2 codes, xq
 // [M][K/4*3] bytes, 32 values per 24-byte group; value p of a group is the
 // code at K offset 16 (p % 2) + 4 (p / 8) + (p % 8) / 2 (the order in which the
-// FP4 x FP6 contraction unpacks the weights).
-template <int P, int E, bool F6>
+// FP4 x FP6 contraction unpacks the weights).  kNibble: two codes per byte in
+// 4-bit two's complement, xq [M][K/2]; in each group g of 16 codes, byte
+// 8g + j holds code 16g + j in its low nibble and code 16g + 8 + j in its high
+// nibble (the slot order of the 2-bit weight packing).
+template <int P, int E, int FMT>
 __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps, double sqrt_k,
     int8_t* __restrict__ xq, float* __restrict__ x_scale, int32_t* __restrict__ x_qsum) {
@@ -194,7 +200,7 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
     qs = wave_sum_dpp(qs);
     if (lane == 0) red_i[wave] = qs;
     __syncthreads();
-    if constexpr (F6) {
+    if constexpr (FMT == kE3M2) {
         uint2* row = reinterpret_cast<uint2*>(xq + m * (K / 4 * 3));
         for (int g = t; g < K / 32; g += F::B) {
             const uint4 c0 = reinterpret_cast<const uint4*>(lds8 + 32 * g)[0];
@@ -213,17 +219,27 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
             row[3 * g + 1] = make_uint2(out[2], out[3]);
             row[3 * g + 2] = make_uint2(out[4], out[5]);
         }
+    } else if constexpr (FMT == kNibble) {
+        // Group g of 16 codes -> 8 bytes: byte j holds code j (low nibble) and
+        // code 8 + j (high nibble), so the dwords are (bytes 0..3 | 8..11 << 4)
+        // and (bytes 4..7 | 12..15 << 4) of the group's codes.
+        uint2* row = reinterpret_cast<uint2*>(xq + m * (K / 2));
+        for (int g = t; g < K / 16; g += F::B) {
+            const uint4 c = reinterpret_cast<const uint4*>(lds8)[g];
+            row[g] = make_uint2((c.x & 0x0F0F0F0Fu) | ((c.z & 0x0F0F0F0Fu) << 4),
+                                (c.y & 0x0F0F0F0Fu) | ((c.w & 0x0F0F0F0Fu) << 4));
+        }
     } else {
-    int8_t* dst = xq + m * K + (int64_t)t * E;
-    if constexpr (E >= 16) {
+        int8_t* dst = xq + m * K + (int64_t)t * E;
+        if constexpr (E >= 16) {
 #pragma unroll
-        for (int q = 0; q < E / 16; ++q)
-            reinterpret_cast<uint4*>(dst)[q] = reinterpret_cast<const uint4*>(lds8 + t * E)[q];
-    } else if constexpr (E == 8) {
-        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(lds8 + t * E);
-    } else {
-        *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds8 + t * E);
-    }
+            for (int q = 0; q < E / 16; ++q)
+                reinterpret_cast<uint4*>(dst)[q] = reinterpret_cast<const uint4*>(lds8 + t * E)[q];
+        } else if constexpr (E == 8) {
+            *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(lds8 + t * E);
+        } else {
+            *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(lds8 + t * E);
+        }
     }
 
     if (t == 0) {
@@ -283,28 +299,28 @@ int log2_exact(int64_t k) {
     return p;
 }
 
-template <int P, bool F6>
+template <int P, int FMT>
 hipError_t launch_hq(const uint16_t* x, const float* gain, float eps, int64_t M, double sqrt_k,
                      int8_t* xq, float* x_scale, int32_t* x_qsum, hipStream_t stream) {
     constexpr int E = elems_per_thread<P>();
-    return launch_kernel((hadamard_quant_kernel<P, E, F6>), dim3((unsigned)M),
+    return launch_kernel((hadamard_quant_kernel<P, E, FMT>), dim3((unsigned)M),
                          dim3(Fwht<P, E>::B), 0, stream, x, gain, eps, sqrt_k, xq, x_scale, x_qsum);
 }
 
-template <bool F6>
+template <int FMT>
 hipError_t launch_hq_k(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
                        double sqrt_k, int8_t* xq, float* x_scale, int32_t* x_qsum,
                        hipStream_t stream) {
     if (M == 0) return hipSuccess;
     switch (log2_exact(K)) {
-        case 8: return launch_hq<8, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 9: return launch_hq<9, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 10: return launch_hq<10, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 11: return launch_hq<11, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 12: return launch_hq<12, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 13: return launch_hq<13, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 14: return launch_hq<14, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
-        case 15: return launch_hq<15, F6>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 8: return launch_hq<8, FMT>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 9: return launch_hq<9, FMT>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 10: return launch_hq<10, FMT>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 11: return launch_hq<11, FMT>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 12: return launch_hq<12, FMT>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 13: return launch_hq<13, FMT>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 14: return launch_hq<14, FMT>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
+        case 15: return launch_hq<15, FMT>(x, gain, eps, M, sqrt_k, xq, x_scale, x_qsum, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -322,14 +338,21 @@ hipError_t launch_rows(const float* src, float* dst, int64_t N, hipStream_t stre
 hipError_t launch_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
                                      int64_t K, double sqrt_k, int8_t* xq, float* x_scale,
                                      int32_t* x_qsum, hipStream_t stream) {
-    return launch_hq_k<false>(x, gain, eps, M, K, sqrt_k, xq, x_scale, x_qsum, stream);
+    return launch_hq_k<kInt8>(x, gain, eps, M, K, sqrt_k, xq, x_scale, x_qsum, stream);
 }
 
 hipError_t launch_hadamard_quant_act_f6(const uint16_t* x, const float* gain, float eps,
                                         int64_t M, int64_t K, double sqrt_k, uint8_t* xq6,
                                         float* x_scale, int32_t* x_qsum, hipStream_t stream) {
-    return launch_hq_k<true>(x, gain, eps, M, K, sqrt_k, reinterpret_cast<int8_t*>(xq6), x_scale,
-                             x_qsum, stream);
+    return launch_hq_k<kE3M2>(x, gain, eps, M, K, sqrt_k, reinterpret_cast<int8_t*>(xq6), x_scale,
+                              x_qsum, stream);
+}
+
+hipError_t launch_hadamard_quant_act_i4(const uint16_t* x, const float* gain, float eps,
+                                        int64_t M, int64_t K, double sqrt_k, uint8_t* xq4,
+                                        float* x_scale, int32_t* x_qsum, hipStream_t stream) {
+    return launch_hq_k<kNibble>(x, gain, eps, M, K, sqrt_k, reinterpret_cast<int8_t*>(xq4), x_scale,
+                                x_qsum, stream);
 }
 
 hipError_t launch_fwht_rows_f32(const float* src, float* dst, int64_t N, int64_t K,

@@ -57,6 +57,12 @@ hipError_t launch_hadamard_quant_act(const uint16_t* x, const float* gain, float
 hipError_t launch_hadamard_quant_act_f6(const uint16_t* x, const float* gain, float eps,
                                         int64_t M, int64_t K, double sqrt_k, uint8_t* xq6,
                                         float* x_scale, int32_t* x_qsum, hipStream_t stream);
+// The same codes as packed 4-bit two's complement, two per byte
+// (xq4: [M][K / 2] bytes; byte 8g + j holds code 16g + j in its low nibble and
+// code 16g + 8 + j in its high nibble).
+hipError_t launch_hadamard_quant_act_i4(const uint16_t* x, const float* gain, float eps,
+                                        int64_t M, int64_t K, double sqrt_k, uint8_t* xq4,
+                                        float* x_scale, int32_t* x_qsum, hipStream_t stream);
 // Row-wise unnormalised Walsh-Hadamard transform of float32 [N][K] (K = 2^p,
 // 256 <= K <= 32768), used for the weight pre-rotation.
 hipError_t launch_fwht_rows_f32(const float* src, float* dst, int64_t N, int64_t K,
@@ -106,6 +112,15 @@ hipError_t launch_fused_decode(const uint16_t* x, const float* gain, float eps,
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                        const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                        int64_t K, float* y, int32_t* acc, hipStream_t stream);
+// The contraction with packed 4-bit codes (launch_hadamard_quant_act_i4
+// layout): the register-resident GEMV on v_dot8_i32_i4 when gemv_supported(M,
+// K), and the int8 matrix-core tiles (codes expanded to 16 q) for any M.
+hipError_t launch_gemv_i4(const uint8_t* xq4, const float* x_scale, const int32_t* x_qsum,
+                          const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc, hipStream_t stream);
+hipError_t launch_gemm_i4(const uint8_t* xq4, const float* x_scale, const int32_t* x_qsum,
+                          const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
+                          int64_t K, float* y, int32_t* acc, hipStream_t stream);
 // The contraction with 6-bit E3M2 activation codes (bitnet_hadamard_quant_act_f6
 // layout) on the FP4 x FP6 matrix core; any M.
 hipError_t launch_gemm_f6(const uint8_t* xq6, const float* x_scale, const int32_t* x_qsum,

@@ -198,6 +198,39 @@ int bitnet_hadamard_quant_act_f6(const uint16_t* x, const float* gain, float eps
                                  void* stream);
 
 /*
+ * H-BitLinear activations stored at half a byte per value ([V2] "방법론":
+ * 4-bit activations).  Same computation and codes as bitnet_hadamard_quant_act,
+ * packed two per byte in 4-bit two's complement:
+ *
+ *   xq4   out  uint8 [M][K/2], 16-byte aligned (x_scale, x_qsum as before).
+ *              In each group g of 16 consecutive codes, byte 8g + j holds code
+ *              16g + j in its low nibble and code 16g + 8 + j in its high
+ *              nibble (j = 0..7), the slot order of the packed weights.
+ *
+ * Consumed by bitnet_linear_forward_i4.  K a power of two in [256, 32768].
+ */
+int bitnet_hadamard_quant_act_i4(const uint16_t* x, const float* gain, float eps, int64_t M,
+                                 int64_t K, uint8_t* xq4, float* x_scale, int32_t* x_qsum,
+                                 void* stream);
+
+/*
+ * Contraction + dequantisation reading the packed 4-bit codes of
+ * bitnet_hadamard_quant_act_i4 directly ([V2] "방법론"; [FT] "계산 패러다임").
+ * M <= 4 tokens run a GEMV on signed 4-bit dot products (the fields of two
+ * weight slots per nibble lane against the code dwords, no unpacking of the
+ * codes); larger M run the int8 matrix-core GEMM with the codes expanded to
+ * 16 q in registers and the sums divided by 16.  acc and y are bit-identical
+ * to bitnet_linear_forward on the same codes stored one per int8.
+ *
+ *   xq4, x_scale, x_qsum  in  outputs of bitnet_hadamard_quant_act_i4; xq4
+ *                             [M][K/2], 16-byte aligned.
+ *   other arguments           as bitnet_linear_forward (K a multiple of 64).
+ */
+int bitnet_linear_forward_i4(const uint8_t* xq4, const float* x_scale, const int32_t* x_qsum,
+                             const uint8_t* packed, const float* w_scale, int64_t M, int64_t N,
+                             int64_t K, float* y, int32_t* acc, void* stream);
+
+/*
  * Ternary integer contraction + dequantisation ([FT] "계산 패러다임",
  * "추론 최적화 및 커스텀 커널", "양자화 메커니즘" rescale; [QP] dequantise).
  *

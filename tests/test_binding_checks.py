@@ -105,6 +105,24 @@ def test_linear_forward_and_f6():
     raises(lambda: bt.linear_forward_f6(xq6, xs, qs, D((N, K // 8), u8), w, out=out), "packed")
 
 
+def test_i4_calls():
+    x = D((M, K), bf16)
+    i4 = (D((M, K // 2), u8), D((M,), f32), D((M,), i32))
+    raises(lambda: bt.hadamard_quant_act_i4(x, gain=D((K // 2,), f32), out=i4), "gain")
+    raises(lambda: bt.hadamard_quant_act_i4(x, out=(D((M, K), u8), D((M,), f32), D((M,), i32))), "xq4")
+    raises(lambda: bt.hadamard_quant_act_i4(x, out=(D((M, K // 2), u8), D((M + 1,), f32), D((M,), i32))),
+           "x_scale")
+    xq4, xs, qs = i4
+    p, w = D((N, K // 4), u8), D((2,), f32)
+    out = D((M, N), f32)
+    raises(lambda: bt.linear_forward_i4(xq4, xs, qs, D((N, K // 2), u8), w, out=out), "packed")
+    raises(lambda: bt.linear_forward_i4(xq4, D((M - 1,), f32), qs, p, w, out=out), "x_scale")
+    raises(lambda: bt.linear_forward_i4(xq4, xs, qs, p, w, out=D((M, N - 1), f32)), "out")
+    raises(lambda: bt.linear_forward_i4(xq4, xs, qs, p, w, out=out, acc_out=D((M, N + 4), i32)), "acc_out")
+    with pytest.raises(TypeError, match="xq4"):
+        bt.linear_forward_i4(D((M, K // 2), i8), xs, qs, p, w, out=out)
+
+
 def test_base3_calls():
     p = D((N, K // 4), u8)
     rb = bt.base3_row_bytes(K)
