@@ -78,7 +78,7 @@ struct GemmCfg {
     // Activation format: int8 codes, 6-bit E3M2 codes (F6: 192 bytes per
     // row per stage, padded to 208 in LDS so 16-byte reads of 16 consecutive
     // rows fall in distinct bank groups), or packed 4-bit codes (I4: 128 bytes
-    // per row per stage, eight 16-byte slots stored at s ^ (r & 7)).
+    // per row per stage, eight 16-byte slots stored at s ^ x4_swizzle(r)).
     static constexpr bool F6 = XF_ == kXE3M2;
     static constexpr bool I4 = XF_ == kXNibble;
     static constexpr int X_ROW = F6 ? 208 : (I4 ? kBK / 2 : kBK);   // LDS bytes per activation row
@@ -140,6 +140,12 @@ __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
 // Any 8 consecutive rows (and any 16 rows of a 16-row block) then hit distinct
 // 16-byte bank groups when a lane group reads the same piece of each row.
 __device__ __forceinline__ int w_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Nibble activation rows (128 bytes, eight 16-byte slots): slot s of row r is
+// stored at s ^ x4_swizzle(r).  LDS serves 256 bytes per cycle, so two rows
+// cover its banks; pairing the row's parity with three more row bits gives 16
+// consecutive rows distinct banks for a 16-byte read of the same slot.
+__device__ __forceinline__ int x4_swizzle(int r) { return (r >> 1) & 7; }
 
 // All of this wave's loads into LDS have landed and its LDS reads are done,
 // then the workgroup barrier.  Written as one asm statement with a memory
@@ -216,7 +222,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
                     const int b = k0 / 4 * 3 + 16 * s;             // byte in the token's row
                     off = (live && s < 12 && b < x_row_bytes) ? (uint32_t)(r * x_row_bytes + b) : kOutOfRange;
                 } else if constexpr (C::I4) {
-                    const int r = p >> 3, s = (p & 7) ^ (r & 7);
+                    const int r = p >> 3, s = (p & 7) ^ x4_swizzle(r);
                     const int b = k0 / 2 + 16 * s;
                     off = (live && b < x_row_bytes) ? (uint32_t)(r * x_row_bytes + b) : kOutOfRange;
                 } else {
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
                         // the codes' and are scaled back in the epilogue.
                         if (st % 2 == 0)
                             xr[j] = *reinterpret_cast<const v4u*>(
-                                &xs[r * C::X_ROW + 16 * ((4 * fh + st / 2) ^ (r & 7))]);
+                                &xs[r * C::X_ROW + 16 * ((4 * fh + st / 2) ^ x4_swizzle(r))]);
                         const uint32_t lo = xr[j][2 * (st % 2)], hi = xr[j][2 * (st % 2) + 1];
                         b[j] = v4i{(int)((lo << 4) & 0xF0F0F0F0u), (int)((hi << 4) & 0xF0F0F0F0u),
                                    (int)(lo & 0xF0F0F0F0u), (int)(hi & 0xF0F0F0F0u)};

@@ -41,17 +41,37 @@ struct Fwht {
     // Index held in register r of thread t during phase J: the low w bits of r
     // are the phase's index bits [b0, b0 + w); the remaining bits of r (short
     // last phase only) are index bits [0, xb); the thread id fills the rest,
-    // low bits first.
+    // low bits first.  The thread's bits and the register's bits are disjoint,
+    // so the index is base<J>(t) + offset<J>(r), and (the padding adds the
+    // index shifted down by 5, which keeps disjoint bits disjoint) the padded
+    // LDS slot is pad(base) + pad(offset): one address per thread and phase,
+    // with the register's part a compile-time offset.
     template <int J>
-    __device__ static __forceinline__ int index(int t, int r) {
+    __device__ static __forceinline__ int base(int t) {
         constexpr int b0 = J * LOG_E;
         constexpr int w = (P - b0 < LOG_E) ? (P - b0) : LOG_E;
         constexpr int xb = LOG_E - w;
         constexpr int nlow = b0 - xb;
-        const int r_lo = r & ((1 << w) - 1);
-        const int r_hi = r >> w;
-        const int base = ((t & ((1 << nlow) - 1)) << xb) | ((t >> nlow) << (b0 + w));
-        return base | (r_lo << b0) | r_hi;
+        return ((t & ((1 << nlow) - 1)) << xb) | ((t >> nlow) << (b0 + w));
+    }
+    template <int J>
+    __device__ static constexpr int offset(int r) {
+        constexpr int b0 = J * LOG_E;
+        constexpr int w = (P - b0 < LOG_E) ? (P - b0) : LOG_E;
+        return ((r & ((1 << w) - 1)) << b0) | (r >> w);
+    }
+    template <int J>
+    __device__ static __forceinline__ int index(int t, int r) {
+        return base<J>(t) | offset<J>(r);
+    }
+    static constexpr int pad_c(int i) { return i + (i >> 5); }
+    // Index bits [0, xbits) of the last phase come from the register number
+    // (r >> w): the 2^xbits registers that differ only there hold adjacent
+    // indices.
+    template <int J>
+    static constexpr int xbits() {
+        constexpr int w = (P - J * LOG_E < LOG_E) ? (P - J * LOG_E) : LOG_E;
+        return LOG_E - w;
     }
 
     template <int J>
@@ -77,11 +97,13 @@ struct Fwht {
     __device__ static __forceinline__ void run(float (&v)[E], float* lds, int t) {
         stages<J>(v);
         if constexpr (J + 1 < NPH) {
+            float* wr = lds + pad(base<J>(t));
+            float* rd = lds + pad(base<J + 1>(t));
 #pragma unroll
-            for (int r = 0; r < E; ++r) lds[pad(index<J>(t, r))] = v[r];
+            for (int r = 0; r < E; ++r) wr[pad_c(offset<J>(r))] = v[r];
             __syncthreads();
 #pragma unroll
-            for (int r = 0; r < E; ++r) v[r] = lds[pad(index<J + 1>(t, r))];
+            for (int r = 0; r < E; ++r) v[r] = rd[pad_c(offset<J + 1>(r))];
             __syncthreads();
             run<J + 1>(v, lds, t);
         }
@@ -149,9 +171,12 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
 
     float v[E];
     load_bf16<E>(x + m * K + (int64_t)t * E, v);
-    double ss = 0.0;
+    // Sum of squares: each square of a bf16 value is exact in float32; four
+    // float32 chains, combined in float64.
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < E; ++r) ss += (double)v[r] * (double)v[r];
+    for (int r = 0; r < E; ++r) sq[r % 4] = __fmaf_rn(v[r], v[r], sq[r % 4]);
+    double ss = ((double)sq[0] + (double)sq[1]) + ((double)sq[2] + (double)sq[3]);
     if (gain != nullptr) {
         const float4* g4 = reinterpret_cast<const float4*>(gain + t * E);
 #pragma unroll
@@ -187,15 +212,50 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void hadamard_quant_kernel(
 
     // Codes go through LDS (as bytes) back to natural order for wide stores;
     // each wave's code sum rides along and is added up after the same barrier.
+    // |t| <= amax, so |t * rn(7 / amax)| < 7.5 and the clamp to [-8, 7] never
+    // acts: adding 1.5 * 2^23 rounds the product to an integer (ties to even,
+    // the rint of the definition) and leaves it, two's complement, in the low
+    // byte of the float's bits.  A token below the tiny absmax has scale 0 and
+    // all-zero codes.
     const bool zero = amax < kTinyAbsmax;
     const float scale = zero ? 0.f : 7.0f / amax;
     int8_t* lds8 = reinterpret_cast<int8_t*>(lds);
-    int qs = 0;
+    uint32_t b[E];
 #pragma unroll
-    for (int r = 0; r < E; ++r) {
-        const int q = zero ? 0 : round_clamp(v[r] * scale, -8.f, 7.f);
-        qs += q;
-        lds8[F::template index<F::NPH - 1>(t, r)] = (int8_t)q;
+    for (int r = 0; r < E; ++r) b[r] = __float_as_uint(__fadd_rn(__fmul_rn(v[r], scale), 12582912.0f));
+    auto pack4 = [](uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+        return __builtin_amdgcn_perm(__builtin_amdgcn_perm(b3, b2, 0x0c0c0400u),
+                                     __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u), 0x05040100u);
+    };
+    constexpr int J = F::NPH - 1;
+    constexpr int G = 1 << F::template xbits<J>();   // adjacent codes per register group
+    constexpr int W = E / G;
+    constexpr int B0 = J * F::LOG_E;
+    int8_t* cdst = lds8 + F::template base<J>(t);
+    int qs = 0;
+    if constexpr (G >= 4) {
+#pragma unroll
+        for (int rl = 0; rl < W; ++rl)
+#pragma unroll
+            for (int q = 0; q < G / 4; ++q) {
+                const uint32_t word = pack4(b[rl + (4 * q) * W], b[rl + (4 * q + 1) * W],
+                                            b[rl + (4 * q + 2) * W], b[rl + (4 * q + 3) * W]);
+                qs = __builtin_amdgcn_sdot4((int)word, 0x01010101, qs, false);
+                *reinterpret_cast<uint32_t*>(cdst + (rl << B0) + 4 * q) = word;
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i)
+            qs = __builtin_amdgcn_sdot4((int)pack4(b[4 * i], b[4 * i + 1], b[4 * i + 2], b[4 * i + 3]),
+                                        0x01010101, qs, false);
+#pragma unroll
+        for (int rl = 0; rl < W; ++rl) {
+            if constexpr (G == 2)
+                *reinterpret_cast<uint16_t*>(cdst + (rl << B0)) =
+                    (uint16_t)__builtin_amdgcn_perm(b[rl + W], b[rl], 0x0c0c0400u);
+            else
+                cdst[rl << B0] = (int8_t)b[rl];
+        }
     }
     qs = wave_sum_dpp(qs);
     if (lane == 0) red_i[wave] = qs;
@@ -275,8 +335,9 @@ __global__ __launch_bounds__((Fwht<P, E>::B)) void fwht_rows_kernel(const float*
     }
     F::template run<0>(v, lds, t);
     // Back to natural order through LDS, then contiguous float4 stores.
+    float* wr = lds + F::pad(F::template base<F::NPH - 1>(t));
 #pragma unroll
-    for (int r = 0; r < E; ++r) lds[F::pad(F::template index<F::NPH - 1>(t, r))] = v[r];
+    for (int r = 0; r < E; ++r) wr[F::pad_c(F::template offset<F::NPH - 1>(r))] = v[r];
     __syncthreads();
     float4* d4 = reinterpret_cast<float4*>(dst + n * K + (int64_t)t * E);
 #pragma unroll
