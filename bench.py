@@ -114,7 +114,7 @@ def parse_args():
 COPY_BYTES = 256 << 20
 READ_REF_BYTES = 2 << 30
 CSRC = os.path.join(ROOT, "bit_gemm_ternary_amd", "csrc")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_kernel.decode_M1.hbm_traffic.md")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode1_kernel.decode_M1.hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("gemv.hip", "common.hpp")]
 GEMM_SUMMARY = os.path.join(ROOT, "profiles", "gemm_kernel.prefill_M2048_K4096_N14336.counters.md")
 GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "common.hpp")]
@@ -1033,7 +1033,7 @@ def main():
             "frac_of_read_reference": round(achieved / read_ref, 4),
             "traffic": None if traffic is None else traffic["hbm_bytes_per_step"],
             "traffic_per_launch": None if traffic is None else traffic["hbm_bytes_per_launch"],
-            "kernel": "decode_kernel, fused (3 launches per step)",
+            "kernel": "decode1_kernel, fused (3 launches per step)",
             "bytes_per_step": dec["kernel_bytes"],
             "us_per_step": round(dec["kernel_us"], 3),
             "per_launch": dec["per_layer"],
