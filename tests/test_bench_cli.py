@@ -42,9 +42,14 @@ def test_no_gpu_no_number():
 
 def test_committed_summaries_carry_bench_data():
     # the counter summaries bench.py reads exist and hold a parseable data line
-    for name in ("decode_kernel.decode_M1.hbm_traffic.md", "gemm_kernel.prefill_M2048_K4096_N14336.counters.md"):
-        with open(os.path.join(ROOT, "profiles", name)) as f:
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_paths", BENCH)
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for path in (bench.TRAFFIC_SUMMARY, bench.GEMM_SUMMARY):
+        with open(path) as f:
             lines = [ln for ln in f if ln.startswith("bench-data: ")]
-        assert len(lines) == 1, name
+        assert len(lines) == 1, path
         data = json.loads(lines[0][len("bench-data: "):])
         assert len(data["source_sha256"]) == 64
