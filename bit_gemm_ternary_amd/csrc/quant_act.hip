@@ -5,12 +5,19 @@
 // [-128, 127] after normalisation) with the factor 127/absmax of the
 // quantization primer (endplan.ai, section 그러면 크기를 더 못줄이나요?).
 //
-// One 256-thread workgroup per token.  Each thread owns CH chunks of 16
-// consecutive bf16 values (chunk c = thread + 256*j), kept in registers as raw
-// bf16 between the two passes:
-//   pass 1: u = x * gain, absmax |u| and sum x^2 (float64) -> workgroup reduce
-//           (DPP within waves, one LDS exchange);
-//   pass 2: codes rint(u * float32(127/absmax)), stored 16 bytes at a time.
+// One workgroup per token (256 threads, 1024 from K = 16384 up, so that a
+// thread holds at most 8 vectors).  Thread t owns the 16-byte vectors
+// (8 consecutive bf16 values) t, t + NT, t + 2 NT, ..., so every load and
+// store instruction of a wave covers one contiguous stretch of the token; the
+// raw bf16 stay in registers between the two passes:
+//   pass 1: u = x * gain, absmax |u|, and sum x^2 (each square of a bf16 value
+//           exact in float32, four float32 chains combined in float64)
+//           -> workgroup reduce (DPP within waves, one LDS exchange);
+//   pass 2: codes rint(u * float32(127/absmax)), 8 bytes per vector.
+// |u| <= absmax, so |u * rn(127/absmax)| < 127.5 and the clamp to [-128, 127]
+// never acts: adding 1.5 * 2^23 rounds the product to an integer (ties to
+// even, the rint of the definition) and leaves it, two's complement, in the
+// low byte of the float's bits.
 // HBM-bound: 2K bytes read, K bytes written per token.
 #include "common.hpp"
 #include "launch.hpp"
@@ -18,76 +25,64 @@
 namespace bitnet {
 namespace {
 
-constexpr int kQuantThreads = 256;
-
-template <int CH>
-__global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
+template <int XV, int NT>
+__global__ __launch_bounds__(NT) void quant_act_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ gain, float eps, int K,
     int8_t* __restrict__ xq, float* __restrict__ x_scale, int32_t* __restrict__ x_qsum) {
-    __shared__ float red_f[kQuantThreads / kWave];
-    __shared__ double red_d[kQuantThreads / kWave];
-    __shared__ int red_i[kQuantThreads / kWave];
+    __shared__ float red_f[NT / kWave];
+    __shared__ double red_d[NT / kWave];
+    __shared__ int red_i[NT / kWave];
 
     const int64_t m = blockIdx.x;
     const int t = threadIdx.x;
-    const int nchunk = K / 16;
+    const int nvec = K / 8;
     const uint4* xr = reinterpret_cast<const uint4*>(x + m * K);
 
-    uint4 raw[CH][2];
+    uint4 raw[XV];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        const int c = t + j * kQuantThreads;
-        if (c < nchunk) {
-            raw[j][0] = xr[2 * c];
-            raw[j][1] = xr[2 * c + 1];
-        } else {
-            raw[j][0] = make_uint4(0, 0, 0, 0);
-            raw[j][1] = make_uint4(0, 0, 0, 0);
-        }
+    for (int j = 0; j < XV; ++j) {
+        const int v = t + j * NT;
+        raw[j] = v < nvec ? xr[v] : make_uint4(0, 0, 0, 0);
     }
 
-    // Unpack 16 bf16 of chunk j into float32.
-    auto unpack = [&](int j, float (&v)[16]) {
-        const uint32_t w[8] = {raw[j][0].x, raw[j][0].y, raw[j][0].z, raw[j][0].w,
-                               raw[j][1].x, raw[j][1].y, raw[j][1].z, raw[j][1].w};
+    // The 8 values of vector j, times the gain when there is one.
+    auto values = [&](int j, float (&u)[8], bool with_gain, bool reload) {
+        const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[2 * i] = bf16_lo(w[i]);
-            v[2 * i + 1] = bf16_hi(w[i]);
+        for (int i = 0; i < 4; ++i) {
+            u[2 * i] = bf16_lo(w[i]);
+            u[2 * i + 1] = bf16_hi(w[i]);
         }
-    };
-    auto apply_gain = [&](int c, float (&v)[16]) {
-        if (gain != nullptr) {
-            const float4* g4 = reinterpret_cast<const float4*>(gain + 16 * c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 g = g4[i];
-                v[4 * i] *= g.x;
-                v[4 * i + 1] *= g.y;
-                v[4 * i + 2] *= g.z;
-                v[4 * i + 3] *= g.w;
-            }
+        const int v = t + j * NT;
+        if (with_gain && gain != nullptr && v < nvec) {
+            // Read again in the second pass (volatile: not kept in registers
+            // across the reduction, which would double the registers per vector).
+            typedef float f4v __attribute__((ext_vector_type(4)));
+            const f4v* g4 = reinterpret_cast<const f4v*>(gain + 8 * v);
+            const f4v g0 = reload ? *reinterpret_cast<const volatile f4v*>(g4) : g4[0];
+            const f4v g1 = reload ? *reinterpret_cast<const volatile f4v*>(g4 + 1) : g4[1];
+            u[0] *= g0[0]; u[1] *= g0[1]; u[2] *= g0[2]; u[3] *= g0[3];
+            u[4] *= g1[0]; u[5] *= g1[1]; u[6] *= g1[2]; u[7] *= g1[3];
         }
     };
 
+    // Vectors past K were loaded as zeros and change neither sum.
     float amax = 0.f;
-    double ss = 0.0;
+    float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        const int c = t + j * kQuantThreads;
-        if (c < nchunk) {
-            float v[16];
-            unpack(j, v);
+    for (int j = 0; j < XV; ++j) {
+        float u[8];
+        values(j, u, false, false);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) ss += (double)v[i] * (double)v[i];
-            apply_gain(c, v);
+        for (int i = 0; i < 8; ++i) sq[i % 4] = __fmaf_rn(u[i], u[i], sq[i % 4]);
+        values(j, u, true, false);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
-        }
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(u[i]));
     }
+    double ss = ((double)sq[0] + (double)sq[1]) + ((double)sq[2] + (double)sq[3]);
     // Absmax and sum of squares reduced together: DPP within each wave, one
     // LDS exchange across the four waves.
-    constexpr int NW = kQuantThreads / kWave;
+    constexpr int NW = NT / kWave;
     const int lane = t % kWave, wave = t / kWave;
     amax = wave_max_dpp(amax);
     ss = wave_sum_dpp(ss);
@@ -104,25 +99,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     const float scale = zero ? 0.f : 127.0f / amax;
     int qs = 0;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-        const int c = t + j * kQuantThreads;
-        if (c < nchunk) {
-            float v[16];
-            unpack(j, v);
-            apply_gain(c, v);
-            uint32_t word[4];
+    for (int j = 0; j < XV; ++j) {
+        const int v = t + j * NT;
+        float u[8];
+        values(j, u, true, true);
+        uint32_t b[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t wv = 0;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int q = zero ? 0 : round_clamp(v[4 * i + b] * scale, -128.f, 127.f);
-                    qs += q;
-                    wv |= (uint32_t)(q & 0xff) << (8 * b);
-                }
-                word[i] = wv;
-            }
-            *reinterpret_cast<uint4*>(xq + m * K + 16 * c) = make_uint4(word[0], word[1], word[2], word[3]);
+        for (int i = 0; i < 8; ++i) b[i] = __float_as_uint(__fadd_rn(__fmul_rn(u[i], scale), 12582912.0f));
+        const uint32_t lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
+        if (v < nvec) {
+            qs = __builtin_amdgcn_sdot4((int)lo, 0x01010101, qs, false);
+            qs = __builtin_amdgcn_sdot4((int)hi, 0x01010101, qs, false);
+            *reinterpret_cast<uint2*>(xq + m * K + 8 * v) = make_uint2(lo, hi);
         }
     }
     qs = wave_sum_dpp(qs);
@@ -142,11 +133,23 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(
     }
 }
 
-template <int CH>
-hipError_t launch_ch(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
+template <int XV, int NT>
+hipError_t launch_xv(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
                      int8_t* xq, float* x_scale, int32_t* x_qsum, hipStream_t stream) {
-    return launch_kernel(quant_act_kernel<CH>, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, x,
-                       gain, eps, (int)K, xq, x_scale, x_qsum);
+    return launch_kernel(quant_act_kernel<XV, NT>, dim3((unsigned)M), dim3(NT), 0, stream, x, gain,
+                         eps, (int)K, xq, x_scale, x_qsum);
+}
+
+template <int NT>
+hipError_t launch_nt(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
+                     int8_t* xq, float* x_scale, int32_t* x_qsum, hipStream_t stream) {
+    const int64_t xv = (K / 8 + NT - 1) / NT;
+    if (xv <= 1) return launch_xv<1, NT>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
+    if (xv <= 2) return launch_xv<2, NT>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
+    if (xv <= 3) return launch_xv<3, NT>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
+    if (xv <= 4) return launch_xv<4, NT>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
+    if (xv <= 6) return launch_xv<6, NT>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
+    return launch_xv<8, NT>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
 }
 
 }  // namespace
@@ -154,16 +157,9 @@ hipError_t launch_ch(const uint16_t* x, const float* gain, float eps, int64_t M,
 hipError_t launch_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
                             int8_t* xq, float* x_scale, int32_t* x_qsum, hipStream_t stream) {
     if (M == 0) return hipSuccess;
-    const int64_t chunks = K / 16;
-    const int64_t ch = (chunks + kQuantThreads - 1) / kQuantThreads;  // 1 .. 16 for K <= 65536
-    if (ch <= 1) return launch_ch<1>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
-    if (ch <= 2) return launch_ch<2>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
-    if (ch <= 3) return launch_ch<3>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
-    if (ch <= 4) return launch_ch<4>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
-    if (ch <= 6) return launch_ch<6>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
-    if (ch <= 8) return launch_ch<8>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
-    if (ch <= 12) return launch_ch<12>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
-    return launch_ch<16>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
+    // K <= 16384: 256 threads, at most 8 vectors each; K <= 65536: 1024 threads.
+    if (K <= 16384) return launch_nt<256>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
+    return launch_nt<1024>(x, gain, eps, M, K, xq, x_scale, x_qsum, stream);
 }
 
 }  // namespace bitnet

@@ -100,6 +100,7 @@ def _activation(M, K, seed, dist="normal", frac=0.01, factor=20.0):
 QUANT_CASES = [
     (4, 256, False), (1, 4096, False), (1, 11008, False), (3, 14336, True), (2048, 4096, False),
     (17, 65536, True), (5, 64, False), (33, 192, True),
+    (3, 32768, False), (2, 20480, True), (6, 16384, True), (4, 16448, False),   # 256 / 1024 threads
 ]
 
 
