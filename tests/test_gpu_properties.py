@@ -87,6 +87,11 @@ def test_every_entry_point_is_deterministic(dev):
     ph, wh = bt.pack_weights(W, hadamard=True)
     q6, dx6, qs6 = bt.hadamard_quant_act_f6(x512)
     _runs_identical(lambda: bt.linear_forward_f6(q6, dx6, qs6, ph, wh, return_acc=True))
+    _runs_identical(lambda: bt.hadamard_quant_act_i4(x512))
+    q4, dx4, qs4 = bt.hadamard_quant_act_i4(x512)
+    for m in (1, 4, 16, 512):  # nibble GEMV, nibble tiles
+        _runs_identical(lambda: bt.linear_forward_i4(q4[:m], dx4[:m], qs4[:m], ph, wh, return_acc=True))
+    _runs_identical(lambda: (bt.linear_forward_blend(x16, W, packed, ws, 0.5),))
     gy = bf16_to_dev(synth.bf16_bits(np.random.default_rng(807).standard_normal((512, N)).astype(np.float32)), dev)
     pt = bt.transpose_packed(packed, K)
     q, dx, _ = bt.quant_act(x512)
@@ -115,6 +120,26 @@ def test_token_counts_across_kernels_agree(dev):
             _, acc = bt.linear_forward(q[:M].contiguous(), dx[:M].contiguous(), qs[:M].contiguous(),
                                        packed, ws, return_acc=True)
             np.testing.assert_array_equal(host(acc), ref[:M])
+
+
+def test_nibble_token_counts_across_kernels_agree(dev):
+    # packed 4-bit codes: the first rows through the dot8 GEMV (M <= 4) and the
+    # tile configurations equal the M = 512 result row for row, and all equal
+    # the int8-container path on the same codes
+    K, N = 4096, 4096
+    W = to_dev(synth.weights(N, K, seed=815), dev)
+    ph, wh = bt.pack_weights(W, hadamard=True)
+    x = tokens_on(dev, 512, K, 816)
+    q4, dx, qs = bt.hadamard_quant_act_i4(x)
+    q8, _, _ = bt.hadamard_quant_act(x)
+    _, ref = bt.linear_forward_i4(q4, dx, qs, ph, wh, return_acc=True)
+    ref = host(ref)
+    _, ref8 = bt.linear_forward(q8, dx, qs, ph, wh, return_acc=True)
+    np.testing.assert_array_equal(ref, host(ref8))
+    for M in (1, 2, 3, 4, 5, 16, 17, 64, 300):
+        _, acc = bt.linear_forward_i4(q4[:M].contiguous(), dx[:M].contiguous(), qs[:M].contiguous(),
+                                      ph, wh, return_acc=True)
+        np.testing.assert_array_equal(host(acc), ref[:M])
 
 
 def test_fused_and_standalone_decode_agree(dev):
@@ -247,13 +272,34 @@ def test_random_small_shapes_match_the_oracle(orc, dev, M, N, k64, seed):
 
 
 @settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
-@given(M=st.integers(5, 700), N=st.integers(1, 4000), k64=st.integers(1, 260), f6=st.booleans(),
+@given(M=st.integers(1, 4), N=st.integers(1, 12000), k64=st.integers(1, 200), seed=st.integers(0, 10 ** 6))
+def test_random_nibble_gemv_shapes_match_the_oracle(orc, dev, M, N, k64, seed):
+    K = 64 * k64
+    rng = np.random.default_rng(seed)
+    W = synth.weights(N, K, seed=seed)
+    packed, d_w, _, _ = orc.pack_weights(W)
+    codes = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    d_x = rng.uniform(1e-3, 1e-2, M).astype(np.float32)
+    qsum = codes.astype(np.int64).sum(axis=1).astype(np.int32)
+    want_acc, want_y = orc.linear_forward(codes, d_x, packed, d_w, K)
+    y, acc = bt.linear_forward_i4(to_dev(orc.pack_nibbles(codes), dev), to_dev(d_x, dev), to_dev(qsum, dev),
+                                  to_dev(packed, dev), to_dev(np.array([d_w, 0], np.float32), dev),
+                                  return_acc=True)
+    np.testing.assert_array_equal(host(acc), want_acc)
+    got = host(y).astype(np.float64)
+    assert np.all(np.abs(got - want_y) <= 1e-5 * np.abs(want_y))
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(M=st.integers(5, 700), N=st.integers(1, 4000), k64=st.integers(1, 260), fmt=st.sampled_from(["i8", "f6", "i4"]),
        seed=st.integers(0, 10 ** 6))
-def test_random_tiled_shapes_match_the_oracle(orc, dev, M, N, k64, f6, seed):
+def test_random_tiled_shapes_match_the_oracle(orc, dev, M, N, k64, fmt, seed):
     # The tiled paths at random shapes: skinny (M <= 16), the 64 x 64 tiles in
     # one, two or four K groups, 128 x 64 tiles in three, the 256-row tiles;
-    # ragged M, N and K (K need not fill the last 256-deep stage).
+    # ragged M, N and K (K need not fill the last 256-deep stage); int8, E3M2
+    # and packed 4-bit codes.
     K = 64 * k64
+    f6 = fmt != "i8"
     assume(M * N * K <= 2_500_000_000)
     rng = np.random.default_rng(seed)
     W = synth.weights(N, K, seed=seed)
@@ -265,8 +311,10 @@ def test_random_tiled_shapes_match_the_oracle(orc, dev, M, N, k64, f6, seed):
     want_acc, want_y = orc.linear_forward(codes, d_x, packed, d_w, K)
     args = (to_dev(d_x, dev), to_dev(qsum, dev), to_dev(packed, dev),
             to_dev(np.array([d_w, 0], np.float32), dev))
-    if f6:
+    if fmt == "f6":
         y, acc = bt.linear_forward_f6(to_dev(f6_layout.encode(codes), dev), *args, return_acc=True)
+    elif fmt == "i4":
+        y, acc = bt.linear_forward_i4(to_dev(orc.pack_nibbles(codes), dev), *args, return_acc=True)
     else:
         y, acc = bt.linear_forward(to_dev(codes, dev), *args, return_acc=True)
     np.testing.assert_array_equal(host(acc), want_acc)
