@@ -318,6 +318,12 @@ FUSED_CASES = [
     (1, 1025, 192, False),                             # 2 rows per wave, one chunk of three lanes
     (1, 700, 16384, True),                             # 4 chunks, one row per wave, 700 waves
     (1, 8193, 8192, False),                            # 2 chunks past one register set: decode_kernel
+    (1, 28672, 4096, False),                           # Llama-3-8B gate|up: decode_kernel
+    (1, 32767, 4096, True),                            # decode_kernel, last wave ragged
+    (1, 20000, 8192, False),                           # 2 chunks, 20 rows per wave: decode_kernel
+    (1, 12000, 8192, True),                            # 2 chunks, 12 rows per wave: decode_kernel
+    (1, 9000, 14336, False),                           # 4 chunks, 9 rows per wave: decode_kernel
+    (1, 8000, 14336, True),                            # 4 chunks, 8 rows per wave: decode_kernel
 ]
 
 
