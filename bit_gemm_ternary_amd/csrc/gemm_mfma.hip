@@ -112,20 +112,25 @@ struct GemmCfg {
 };
 
 // Two packed words (32 offset codes c = q + 1, weights 0..15 in w and 16..31
-// in w2) -> 32 FP4 (E2M1) values 2 c / 2 = c, i.e. nibble 2 c: code c of
-// weight 4 d + b of w goes to nibble 2 b of dword d, that of w2 to nibble
-// 2 b + 1.  FP4 holds 0, 1 and 2 exactly.
+// in w2) -> 32 FP4 (E2M1) values: code c of weight 4 d + b of w goes to
+// nibble 2 b of dword d, that of w2 to nibble 2 b + 1.  The nibble is the code
+// itself, the E2M1 value c / 2 (0, 0.5 and 1 are exact: 0.5 is the subnormal),
+// and the operand's block scale 2^1 makes it c again.  Per dword: the code
+// fields of w masked in place and those of w2 shifted into the high nibble,
+// merged by one and-or.
 __device__ __forceinline__ v8i unpack_fp4(uint32_t w, uint32_t w2) {
     v8i r = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-        r[d] = (int)((((w >> (2 * d)) & 0x03030303u) << 1) | (((w2 >> (2 * d)) & 0x03030303u) << 5));
+    r[0] = (int)((w & 0x03030303u) | ((w2 << 4) & 0x30303030u));
+    r[1] = (int)(((w >> 2) & 0x03030303u) | ((w2 << 2) & 0x30303030u));
+    r[2] = (int)(((w >> 4) & 0x03030303u) | (w2 & 0x30303030u));
+    r[3] = (int)(((w >> 6) & 0x03030303u) | ((w2 >> 2) & 0x30303030u));
     return r;
 }
 
 constexpr int kFmtFp4 = 4;      // MFMA operand format selector: FP4 E2M1
 constexpr int kFmtE3M2 = 3;     // MFMA operand format selector: 6-bit E3M2
 constexpr int kScaleOne = 127;  // E8M0 block scale 2^0
+constexpr int kScaleTwo = 128;  // E8M0 block scale 2^1 (the FP4 weight operand: nibble c means c / 2)
 
 __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
     v4i r;
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gemm_kernel(
 #pragma unroll
                     for (int j = 0; j < C::FM; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            a, b[j], acc[i][j], kFmtFp4, kFmtE3M2, 0, kScaleOne, 0, kScaleOne);
+                            a, b[j], acc[i][j], kFmtFp4, kFmtE3M2, 0, kScaleTwo, 0, kScaleOne);
                 }
             } else {
                 v4i b[C::FM];
