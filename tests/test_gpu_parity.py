@@ -263,6 +263,18 @@ def test_empty_inputs(dev):
     y = bt.linear_forward(xq, torch.ones(3, device=dev), torch.zeros(3, dtype=torch.int32, device=dev),
                           torch.empty((0, 64), dtype=torch.uint8, device=dev), ws)
     assert tuple(y.shape) == (3, 0)
+    # packed 4-bit codes and the warm-up blend
+    q4, dx4, qs4 = bt.hadamard_quant_act_i4(torch.empty((0, 256), dtype=torch.bfloat16, device=dev))
+    assert tuple(q4.shape) == (0, 128) and dx4.shape[0] == 0 and qs4.shape[0] == 0
+    y = bt.linear_forward_i4(q4, dx4, qs4, packed, ws)
+    assert tuple(y.shape) == (0, 8)
+    y = bt.linear_forward_i4(torch.zeros((2, 128), dtype=torch.uint8, device=dev), torch.ones(2, device=dev),
+                             torch.zeros(2, dtype=torch.int32, device=dev),
+                             torch.empty((0, 64), dtype=torch.uint8, device=dev), ws)
+    assert tuple(y.shape) == (2, 0)
+    W = torch.zeros((8, 256), dtype=torch.float32, device=dev)
+    y = bt.linear_forward_blend(torch.empty((0, 256), dtype=torch.bfloat16, device=dev), W, packed, ws, 0.5)
+    assert tuple(y.shape) == (0, 8)
 
 
 # ---------------------------------------------------------------------------
