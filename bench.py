@@ -36,7 +36,9 @@ region measures the GPU, not Python or per-launch host overhead, whatever
                    (committed counter summary)
   hadamard         H-BitLinear M=512: FWHT + int4 quantisation GB/s and GEMM TOPS,
                    for int8 codes (int8 matrix core) and for 6-bit E3M2 codes (FP4 x
-                   FP6 matrix core, against the 10.1 PFLOP/s fp6 peak)
+                   FP6 matrix core, against the 10.1 PFLOP/s fp6 peak), packed 4-bit
+                   codes; one token through the layer as two kernels and as the
+                   single fused launch
   block            the seven BitLinear projections of a Llama-3-8B block at
                    M = 1, 16 and 256 tokens: time per block, packed weight GB/s,
                    int TOPS
@@ -658,6 +660,11 @@ def hadamard_bench(args, dev, bt, torch, synth):
         y1 = torch.empty((1, N), dtype=torch.float32, device=dev)
         gemv = lambda: bt.linear_forward(xq[:1], xs[:1], qs[:1], packed, w_scale, out=y1)
         gemv4 = lambda: bt.linear_forward_i4(xq4[:1], xs[:1], qs[:1], packed, w_scale, out=y1)
+        # one token through the whole layer: the quantisation kernel then the
+        # GEMV, against the single fused launch
+        hq4_1 = lambda: bt.hadamard_quant_act_i4(x[:1], None, 1e-5, out=(xq4[:1], xs[:1], qs[:1]))
+        hfused = lambda: bt.hadamard_bitlinear_forward(x[:1], packed, w_scale, codes=(xq4[:1], xs[:1], qs[:1]),
+                                                       out=y1)
         for _ in range(5):
             hq()
             gemm()
@@ -667,6 +674,8 @@ def hadamard_bench(args, dev, bt, torch, synth):
             gemm4()
             gemv()
             gemv4()
+            hq4_1()
+            hfused()
         torch.cuda.synchronize()
         hq_us = time_launches(hq, args.prefill_iters, bt)
         gemm_us = time_launches(gemm, args.prefill_iters, bt)
@@ -676,6 +685,8 @@ def hadamard_bench(args, dev, bt, torch, synth):
         gemm4_us = time_launches(gemm4, args.prefill_iters, bt)
         gemv_us = time_launches(gemv, args.prefill_iters, bt)
         gemv4_us = time_launches(gemv4, args.prefill_iters, bt)
+        hq4_1_us = time_launches(hq4_1, args.prefill_iters, bt)
+        hfused_us = time_launches(hfused, args.prefill_iters, bt)
         hq_bytes = M * K * 2 + M * K + 8 * M
         hq6_bytes = M * K * 2 + M * K // 4 * 3 + 8 * M
         hq4_bytes = M * K * 2 + M * K // 2 + 8 * M
@@ -699,7 +710,11 @@ def hadamard_bench(args, dev, bt, torch, synth):
                            "gemm_nibble_TOPS": round(ops / (gemm4_us * 1e-6) / 1e12, 1),
                            "gemv_m1_int8_us": round(gemv_us, 2),
                            "gemv_m1_nibble_us": round(gemv4_us, 2),
-                           "gemv_m1_nibble_GB_s": round((gemv_bytes - K // 2) / gemv4_us / 1e3, 1)}})
+                           "gemv_m1_nibble_GB_s": round((gemv_bytes - K // 2) / gemv4_us / 1e3, 1),
+                           "layer_m1_two_kernels_us": round(hq4_1_us + gemv4_us, 2),
+                           "layer_m1_fused_us": round(hfused_us, 2),
+                           "layer_m1_fused_GB_s": round((N * K // 4 + 2 * K + K // 2 + 4 * N) / hfused_us / 1e3,
+                                                        1)}})
     return out
 
 

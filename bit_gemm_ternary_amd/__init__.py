@@ -20,6 +20,7 @@ __all__ = [
     "BitnetError", "lib", "library_path", "pack_weights", "pack_weights_workspace_bytes",
     "base3_row_bytes", "pack_base3", "linear_forward_base3",
     "quant_act", "hadamard_quant_act", "linear_forward", "bitlinear", "bitlinear_forward",
+    "hadamard_quant_act_i4", "linear_forward_i4", "hadamard_bitlinear_forward",
     "BitLinear",
     "STATUS", "set_kernel_events",
 ]
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.bitnet_linear_forward_i4.restype = i32
     L.bitnet_bitlinear_forward.argtypes = [p, p, f32, p, p, i64, i64, i64, p, p, p, p, p, p]
     L.bitnet_bitlinear_forward.restype = i32
+    L.bitnet_hadamard_bitlinear_forward.argtypes = [p, p, f32, p, p, i64, i64, i64, p, p, p, p, p, p]
+    L.bitnet_hadamard_bitlinear_forward.restype = i32
     L.bitnet_bitlinear_forward_grouped.argtypes = [p, p, f32, p, p, p, i32, i64, i64, p, p, p, p,
                                                    p, p]
     L.bitnet_bitlinear_forward_grouped.restype = i32
@@ -471,6 +474,38 @@ def bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5, out=None
     _check(lib().bitnet_bitlinear_forward(_ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(packed),
                                           _ptr(w_scale), M, N, K, _ptr(xq), _ptr(x_scale),
                                           _ptr(x_qsum), _ptr(out), _ptr(acc_out), _stream(dev)))
+    return (out, acc_out) if acc_out is not None else out
+
+
+def hadamard_bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5, out=None, codes=None,
+                               acc_out=None):
+    """Fused H-BitLinear forward (bitnet_hadamard_bitlinear_forward): bf16 [M][K]
+    -> y float32 [M][N], with weights packed with ``hadamard=True``.
+
+    ``codes`` may hold preallocated (xq4 uint8 [M][K/2], x_scale, x_qsum) for
+    the intermediate 4-bit codes (they are written); ``out`` / ``acc_out``
+    preallocated outputs.  Returns y, or (y, acc) when ``acc_out`` is given.
+    """
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    M, K = x.shape
+    _require(packed, "packed", torch.uint8, 2, dev)
+    N = packed.shape[0]
+    if packed.shape[1] * 4 != K:
+        raise ValueError(f"packed is [{N}][{packed.shape[1]}], expected [{N}][{K // 4}] for K={K}")
+    _require_at_least(w_scale, "w_scale", torch.float32, 1, dev)
+    _gain(gain, K, dev)
+    xq4, x_scale, x_qsum = (None, None, None) if codes is None else codes
+    xq4 = _output(xq4, "xq4", torch.uint8, (M, K // 2), dev)
+    x_scale = _output(x_scale, "x_scale", torch.float32, (M,), dev)
+    x_qsum = _output(x_qsum, "x_qsum", torch.int32, (M,), dev)
+    out = _output(out, "out", torch.float32, (M, N), dev)
+    if acc_out is not None:
+        _require_shape(acc_out, "acc_out", torch.int32, (M, N), dev)
+    _check(lib().bitnet_hadamard_bitlinear_forward(_ptr(x), _ptr(gain), ctypes.c_float(eps), _ptr(packed),
+                                                   _ptr(w_scale), M, N, K, _ptr(xq4), _ptr(x_scale),
+                                                   _ptr(x_qsum), _ptr(out), _ptr(acc_out), _stream(dev)))
     return (out, acc_out) if acc_out is not None else out
 
 

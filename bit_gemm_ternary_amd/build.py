@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitnet_hip.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "pack.hip", "quant_act.hip", "hadamard_quant.hip", "gemv.hip", "gemm_mfma.hip",
+SOURCES = ["api.cpp", "pack.hip", "quant_act.hip", "hadamard_quant.hip", "hadamard_decode.hip", "gemv.hip", "gemm_mfma.hip",
            "backward.hip", "base3.hip", "stream_read.hip", "blend.hip"]
 
 FLAGS = [

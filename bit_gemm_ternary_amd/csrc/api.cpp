@@ -331,6 +331,40 @@ int bitnet_bitlinear_forward(const uint16_t* x, const float* gain, float eps,
                                   xq, x_scale, x_qsum, y, acc, st, fn);
 }
 
+int bitnet_hadamard_bitlinear_forward(const uint16_t* x, const float* gain, float eps,
+                                      const uint8_t* packed, const float* w_scale, int64_t M,
+                                      int64_t N, int64_t K, uint8_t* xq4, float* x_scale,
+                                      int32_t* x_qsum, float* y, int32_t* acc, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_hadamard_bitlinear_forward";
+    int s = validate_quant(x, gain, eps, M, K, reinterpret_cast<int8_t*>(xq4), x_scale, x_qsum, true, fn);
+    if (s != BITNET_OK) return s;
+    if (N < 0 || N > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: N=%lld out of range", fn, (long long)N);
+    if (M == 0) return BITNET_OK;
+    hipStream_t st = (hipStream_t)stream;
+    const double sqrt_k = std::sqrt((double)K);
+    if (N == 0)
+        return hip_status(bitnet::launch_hadamard_quant_act_i4(x, gain, eps, M, K, sqrt_k, xq4, x_scale,
+                                                               x_qsum, st),
+                          fn);
+    if (!packed || !w_scale || !y) return fail(BITNET_ERR_NULL, "%s: packed, w_scale and y must not be NULL", fn);
+    if (!aligned(packed, 16)) return fail(BITNET_ERR_ALIGN, "%s: packed must be 16-byte aligned", fn);
+    if (!aligned(w_scale, 4) || !aligned(y, 4) || (acc && !aligned(acc, 4)))
+        return fail(BITNET_ERR_ALIGN, "%s: w_scale, y and acc must be 4-byte aligned", fn);
+    if (M == 1 && bitnet::hadamard_decode_supported(N, K))
+        return hip_status(bitnet::launch_hadamard_decode(x, gain, eps, sqrt_k, packed, w_scale, N, K, y, xq4,
+                                                         x_scale, x_qsum, acc, st),
+                          fn);
+    hipError_t e = bitnet::launch_hadamard_quant_act_i4(x, gain, eps, M, K, sqrt_k, xq4, x_scale, x_qsum, st);
+    if (e == hipSuccess) {
+        const bitnet::RowScales scales = bitnet::single_group(w_scale, N);
+        e = bitnet::gemv_supported(M, K)
+                ? bitnet::launch_gemv_i4(xq4, x_scale, x_qsum, packed, scales, M, N, K, y, acc, st)
+                : bitnet::launch_gemm_i4(xq4, x_scale, x_qsum, packed, scales, M, N, K, y, acc, st);
+    }
+    return hip_status(e, fn);
+}
+
 int bitnet_bitlinear_forward_grouped(const uint16_t* x, const float* gain, float eps,
                                      const uint8_t* packed, const float* w_scales,
                                      const int64_t* group_rows, int groups, int64_t M, int64_t K,

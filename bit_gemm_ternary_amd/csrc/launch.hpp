@@ -63,6 +63,18 @@ hipError_t launch_hadamard_quant_act_f6(const uint16_t* x, const float* gain, fl
 hipError_t launch_hadamard_quant_act_i4(const uint16_t* x, const float* gain, float eps,
                                         int64_t M, int64_t K, double sqrt_k, uint8_t* xq4,
                                         float* x_scale, int32_t* x_qsum, hipStream_t stream);
+// One token through the H-BitLinear layer in one launch (hadamard_decode.hip):
+// the codes of launch_hadamard_quant_act_i4 (xq4 [K/2], x_scale, x_qsum,
+// written by the first workgroup) and the contraction of launch_gemv_i4 with
+// one weight group (y, acc [N]).  K a power of two in [1024, 16384] and
+// ceil(N / V) * ceil(K / 4096) <= 16 for N >= 1, with V = 1024 waves up to
+// K = 4096 and 2048 above; hipErrorNotSupported outside that domain
+// (hadamard_decode_supported), launching nothing.
+bool hadamard_decode_supported(int64_t N, int64_t K);
+hipError_t launch_hadamard_decode(const uint16_t* x, const float* gain, float eps, double sqrt_k,
+                                  const uint8_t* packed, const float* w_scale, int64_t N, int64_t K,
+                                  float* y, uint8_t* xq4, float* x_scale, int32_t* x_qsum,
+                                  int32_t* acc, hipStream_t stream);
 // Row-wise unnormalised Walsh-Hadamard transform of float32 [N][K] (K = 2^p,
 // 256 <= K <= 32768), used for the weight pre-rotation.
 hipError_t launch_fwht_rows_f32(const float* src, float* dst, int64_t N, int64_t K,

@@ -313,6 +313,34 @@ int bitnet_bitlinear_forward_grouped(const uint16_t* x, const float* gain, float
                                      int32_t* acc, void* stream);
 
 /*
+ * Fused H-BitLinear forward ([V2] "방법론": the layer's input is Hadamard
+ * transformed and quantised to 4-bit per-token absmax codes, then contracted
+ * with the ternary weights packed with hadamard = 1):
+ * bitnet_hadamard_quant_act_i4 followed by bitnet_linear_forward_i4, with the
+ * same outputs.
+ *
+ *   x, gain, eps            in   as bitnet_hadamard_quant_act_i4 (K a power of
+ *                                two in [256, 32768]).
+ *   packed, w_scale         in   as bitnet_linear_forward_i4 (packed with
+ *                                hadamard = 1 for the layer to mean y = x W^T).
+ *   xq4, x_scale, x_qsum    out  as bitnet_hadamard_quant_act_i4 (the codes the
+ *                                contraction used).
+ *   y, acc                  out  as bitnet_linear_forward_i4 (acc may be NULL).
+ * One token (M = 1) with K in [1024, 16384] and N up to 16384 (8192 at
+ * K = 16384) runs in one launch: every workgroup
+ * transforms and quantises the token while its weight loads are in flight,
+ * then contracts on 4-bit dot products.  Other shapes run the two kernels back
+ * to back.  Codes, x_qsum and acc are bit-identical either way; x_scale (and
+ * so y) may differ from the two-launch path in the last float32 bits, since
+ * the float64 sum of x^2 is added in another order.  N = 0 only quantises;
+ * M = 0 is a no-op; errors as bitnet_bitlinear_forward.
+ */
+int bitnet_hadamard_bitlinear_forward(const uint16_t* x, const float* gain, float eps,
+                                      const uint8_t* packed, const float* w_scale, int64_t M,
+                                      int64_t N, int64_t K, uint8_t* xq4, float* x_scale,
+                                      int32_t* x_qsum, float* y, int32_t* acc, void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * Backward pass under the straight-through estimator ([FT] "Straight-Through
  * Estimator (STE)를 이용한 학습": round() is given the gradient 1, so both

@@ -152,6 +152,36 @@ def test_fused_forward_argument_errors(L):
     assert _fused(L, M=0, x=0, P=0, y=0) == 0
 
 
+def _hfused(L, x=A16, gain=None, eps=1e-5, P=A16, ws=A4, M=1, N=8, K=1024, xq4=A16, sx=A4, qs=A4,
+            y=A4, acc=None):
+    return L.bitnet_hadamard_bitlinear_forward(
+        ctypes.c_void_p(x), None if gain is None else ctypes.c_void_p(gain), ctypes.c_float(eps),
+        ctypes.c_void_p(P), ctypes.c_void_p(ws), M, N, K, ctypes.c_void_p(xq4), ctypes.c_void_p(sx),
+        ctypes.c_void_p(qs), ctypes.c_void_p(y), None if acc is None else ctypes.c_void_p(acc), None)
+
+
+def test_hadamard_fused_forward_argument_errors(L):
+    assert _hfused(L, M=-1) == 2
+    assert _hfused(L, N=-1) == 2
+    assert _hfused(L, K=100) == 2          # not a multiple of 64
+    assert _hfused(L, K=384) == 3          # not a power of two
+    assert _hfused(L, K=128) == 3          # below 256
+    assert _hfused(L, K=65536) == 3        # above 32768
+    assert _hfused(L, eps=-1.0) == 7
+    assert _hfused(L, x=0) == 1
+    assert _hfused(L, xq4=0) == 1
+    assert _hfused(L, P=0) == 1
+    assert _hfused(L, ws=0) == 1
+    assert _hfused(L, y=0) == 1
+    assert _hfused(L, x=BAD) == 4
+    assert _hfused(L, xq4=A4) == 4
+    assert _hfused(L, sx=BAD) == 4
+    assert _hfused(L, P=A4) == 4
+    assert _hfused(L, y=BAD) == 4
+    assert _hfused(L, acc=BAD) == 4
+    assert _hfused(L, M=0, x=0, xq4=0, P=0, y=0) == 0
+
+
 def test_kernel_events_hook_is_exported(L):
     assert L.bitnet_set_kernel_events(None, None) == 0
 

@@ -123,6 +123,25 @@ def test_i4_calls():
         bt.linear_forward_i4(D((M, K // 2), i8), xs, qs, p, w, out=out)
 
 
+def test_hadamard_bitlinear_forward_calls():
+    k = 1024
+    x, p, w = D((1, k), bf16), D((N, k // 4), u8), D((2,), f32)
+    i4 = (D((1, k // 2), u8), D((1,), f32), D((1,), i32))
+    out = D((1, N), f32)
+    f = bt.hadamard_bitlinear_forward
+    raises(lambda: f(x, p, w, gain=D((k // 2,), f32), codes=i4, out=out), "gain")
+    raises(lambda: f(x, p, w, codes=(D((1, k), u8), D((1,), f32), D((1,), i32)), out=out), "xq4")
+    raises(lambda: f(x, p, w, codes=(D((1, k // 2), u8), D((2,), f32), D((1,), i32)), out=out), "x_scale")
+    raises(lambda: f(x, p, w, codes=(D((1, k // 2), u8), D((1,), f32), D((3,), i32)), out=out), "x_qsum")
+    raises(lambda: f(x, p, w, codes=i4, out=D((1, N + 1), f32)), "out")
+    raises(lambda: f(x, p, w, codes=i4, out=out, acc_out=D((2, N), i32)), "acc_out")
+    raises(lambda: f(x, D((N, k // 2), u8), w, codes=i4, out=out), "packed")
+    raises(lambda: f(x, p, D((0,), f32), codes=i4, out=out), "w_scale")
+    raises(lambda: f(x, D((N, k // 4), u8, _OnGpu1), w, codes=i4, out=out), "packed")
+    with pytest.raises(TypeError, match="xq4"):
+        f(x, p, w, codes=(D((1, k // 2), i8), D((1,), f32), D((1,), i32)), out=out)
+
+
 def test_base3_calls():
     p = D((N, K // 4), u8)
     rb = bt.base3_row_bytes(K)
