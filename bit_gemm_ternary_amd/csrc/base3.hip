@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kB3Threads) void base3_gemv_kernel(
     const int32_t qs = x_qsum[0];
     const float sx = x_scale[0], dw = w_scale[0];
 
-    for (int r0 = g; r0 < N; r0 += kB3Batch * W) {
+    for (int64_t r0 = g; r0 < N; r0 += (int64_t)kB3Batch * W) {  // r0 + stride may pass 2^31 - 1
         uint4 w[kB3Batch][CH];
 #pragma unroll
         for (int rb = 0; rb < kB3Batch; ++rb) {
