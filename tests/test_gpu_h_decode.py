@@ -158,3 +158,54 @@ def test_n_zero_only_quantises(orc, dev):
     np.testing.assert_array_equal(host(codes[0]), orc.pack_nibbles(wq))
     np.testing.assert_array_equal(host(codes[2]), wqs)
     assert_close_rel(host(codes[1]), wdx)
+
+
+def _bf16_bits(values, K):
+    x = np.zeros((1, K), np.float32)
+    for i, v in values.items():
+        x[0, i] = v
+    return (x.view(np.uint32) >> 16).astype(np.uint16)   # every value here is exact in bf16
+
+
+@pytest.mark.parametrize("K", [1024, 16384])
+@pytest.mark.parametrize("a,b,half_code", [(7.5, 6.5, 0), (8.5, 5.5, 2)])
+def test_rounding_ties_go_to_even(orc, dev, K, a, b, half_code):
+    """x = a e_0 + b e_1 transforms to a + b and a - b; with absmax a + b = 14
+    the scale is exactly 1/2, so a - b lands on a half-integer code (0.5 or
+    1.5) that rounds to the even neighbour, as in the oracle."""
+    N = 300
+    x = _bf16_bits({0: a, 1: b}, K)
+    packed, d_w, _, _ = orc.pack_weights(synth.weights(N, K, seed=2600))
+    wq, wdx, wqs = orc.hadamard_quant_act(x)
+    assert set(np.unique(wq)) == {7, half_code}
+    want_acc, want_y = orc.linear_forward(wq, wdx, packed, d_w, K)
+    codes = (torch.empty((1, K // 2), dtype=torch.uint8, device=dev),
+             torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    y, acc = bt.hadamard_bitlinear_forward(bf16_to_dev(x, dev), to_dev(packed, dev),
+                                           to_dev(np.array([d_w, 0], np.float32), dev), codes=codes,
+                                           acc_out=torch.empty((1, N), dtype=torch.int32, device=dev))
+    np.testing.assert_array_equal(host(codes[0]), orc.pack_nibbles(wq))
+    np.testing.assert_array_equal(host(codes[2]), wqs)
+    assert_close_rel(host(codes[1]), wdx)
+    np.testing.assert_array_equal(host(acc), want_acc)
+    assert_close_rel(host(y), want_y)
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.25])
+def test_eps_only_scales(orc, dev, eps):
+    K, N = 4096, 2000
+    x = synth.activations(1, K, 2700, 2701, dist="student_t", outlier_frac=0.0)
+    gain = np.random.default_rng(2702).uniform(0.5, 1.5, K).astype(np.float32)
+    packed, d_w, _, _ = orc.pack_weights(synth.weights(N, K, seed=2703))
+    wq, wdx, wqs = orc.hadamard_quant_act(x, gain=gain, eps=eps)
+    want_acc, want_y = orc.linear_forward(wq, wdx, packed, d_w, K)
+    codes = (torch.empty((1, K // 2), dtype=torch.uint8, device=dev),
+             torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.int32, device=dev))
+    y, acc = bt.hadamard_bitlinear_forward(bf16_to_dev(x, dev), to_dev(packed, dev),
+                                           to_dev(np.array([d_w, 0], np.float32), dev),
+                                           gain=to_dev(gain, dev), eps=eps, codes=codes,
+                                           acc_out=torch.empty((1, N), dtype=torch.int32, device=dev))
+    np.testing.assert_array_equal(host(codes[0]), orc.pack_nibbles(wq))
+    assert_close_rel(host(codes[1]), wdx)
+    np.testing.assert_array_equal(host(acc), want_acc)
+    assert_close_rel(host(y), want_y)
