@@ -42,6 +42,11 @@ region measures the GPU, not Python or per-launch host overhead, whatever
   block            the seven BitLinear projections of a Llama-3-8B block at
                    M = 1, 16 and 256 tokens: time per block, packed weight GB/s,
                    int TOPS
+  shard            one device's share of that block split eight ways (M = 1):
+                   q|k|v and gate|up by output features, o and down by input
+                   features (statistics, quantisation with the whole token's
+                   statistics, int32 partial sums, dequantisation); time per
+                   share and per kernel, collectives not run
   backward         STE backward of the prefill layer: grad_n and grad_w on the bf16
                    matrix cores, RMSNorm backward, packed-weight transpose
   blend            the warm-up blend of the prefill layer (lambda = 0.5): the
@@ -106,7 +111,7 @@ def parse_args():
     ap.add_argument("--block-steps", type=int, default=200, help="timed steps per token count of the block leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of COPY_BYTES, ten times (HBM counter calibration)")
-    ap.add_argument("--legs", default="decode,decode_sizes,base3,prefill,hadamard,block,backward,blend,pack",
+    ap.add_argument("--legs", default="decode,decode_sizes,base3,prefill,hadamard,block,shard,backward,blend,pack",
                     help="comma-separated legs to run (the headline needs decode)")
     ap.add_argument("--cpu-one-core-seconds", type=float, default=5.0,
                     help="wall time budget of the one-core CPU-oracle sample")
@@ -261,6 +266,17 @@ def time_region(launch, n, torch, prelude=None):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / n, time.perf_counter() - t0
+
+
+def b2b_us(fn, n, copies, torch, dev, eager=False):
+    """Average duration (us) of fn(r), r = 0, 1, ... on rotation copy r % copies,
+    launched n times back to back in one HIP graph after a cache flush; median
+    of three such regions (each region also carries the graph launch's fixed
+    cost, 12-19 us, spread over the n launches)."""
+    t = StepTimer(fn, n, copies, torch, cache_flush(torch, dev), eager=eager)
+    us = t.median_ms(3) * 1e3
+    t.close()
+    return us
 
 
 class StepTimer:
@@ -661,10 +677,17 @@ def hadamard_bench(args, dev, bt, torch, synth):
         gemv = lambda: bt.linear_forward(xq[:1], xs[:1], qs[:1], packed, w_scale, out=y1)
         gemv4 = lambda: bt.linear_forward_i4(xq4[:1], xs[:1], qs[:1], packed, w_scale, out=y1)
         # one token through the whole layer: the quantisation kernel then the
-        # GEMV, against the single fused launch
-        hq4_1 = lambda: bt.hadamard_quant_act_i4(x[:1], None, 1e-5, out=(xq4[:1], xs[:1], qs[:1]))
-        hfused = lambda: bt.hadamard_bitlinear_forward(x[:1], packed, w_scale, codes=(xq4[:1], xs[:1], qs[:1]),
-                                                       out=y1)
+        # GEMV, against the single fused launch, back to back over rotating
+        # weight copies
+        rot = [packed] + [packed.clone() for _ in range(max(0, math.ceil(ROTATE_BYTES / (N * K // 4)) - 1))]
+        c1 = (xq4[:1], xs[:1], qs[:1])
+
+        def layer_two(r):
+            bt.hadamard_quant_act_i4(x[:1], None, 1e-5, out=c1)
+            bt.linear_forward_i4(*c1, rot[r], w_scale, out=y1)
+
+        def layer_fused(r):
+            bt.hadamard_bitlinear_forward(x[:1], rot[r], w_scale, codes=c1, out=y1)
         for _ in range(5):
             hq()
             gemm()
@@ -674,8 +697,8 @@ def hadamard_bench(args, dev, bt, torch, synth):
             gemm4()
             gemv()
             gemv4()
-            hq4_1()
-            hfused()
+            layer_two(0)
+            layer_fused(0)
         torch.cuda.synchronize()
         hq_us = time_launches(hq, args.prefill_iters, bt)
         gemm_us = time_launches(gemm, args.prefill_iters, bt)
@@ -685,8 +708,9 @@ def hadamard_bench(args, dev, bt, torch, synth):
         gemm4_us = time_launches(gemm4, args.prefill_iters, bt)
         gemv_us = time_launches(gemv, args.prefill_iters, bt)
         gemv4_us = time_launches(gemv4, args.prefill_iters, bt)
-        hq4_1_us = time_launches(hq4_1, args.prefill_iters, bt)
-        hfused_us = time_launches(hfused, args.prefill_iters, bt)
+        two_us = b2b_us(layer_two, 400, len(rot), torch, dev, eager=args.eager)
+        fused_us = b2b_us(layer_fused, 400, len(rot), torch, dev, eager=args.eager)
+        del rot
         hq_bytes = M * K * 2 + M * K + 8 * M
         hq6_bytes = M * K * 2 + M * K // 4 * 3 + 8 * M
         hq4_bytes = M * K * 2 + M * K // 2 + 8 * M
@@ -711,10 +735,11 @@ def hadamard_bench(args, dev, bt, torch, synth):
                            "gemv_m1_int8_us": round(gemv_us, 2),
                            "gemv_m1_nibble_us": round(gemv4_us, 2),
                            "gemv_m1_nibble_GB_s": round((gemv_bytes - K // 2) / gemv4_us / 1e3, 1),
-                           "layer_m1_two_kernels_us": round(hq4_1_us + gemv4_us, 2),
-                           "layer_m1_fused_us": round(hfused_us, 2),
-                           "layer_m1_fused_GB_s": round((N * K // 4 + 2 * K + K // 2 + 4 * N) / hfused_us / 1e3,
-                                                        1)}})
+                           "layer_m1_two_kernels_us": round(two_us, 2),
+                           "layer_m1_fused_us": round(fused_us, 2),
+                           "layer_m1_fused_GB_s": round((N * K // 4 + 2 * K + K // 2 + 4 * N) / fused_us / 1e3, 1),
+                           "layer_m1_timing": "per layer, back to back in one graph over >= 1 GiB of weight "
+                                              "copies"}})
     return out
 
 
@@ -906,6 +931,85 @@ def block_bench(args, dev, bt, torch, synth):
             "by_tokens": out}
 
 
+# Row-parallel projections of the eight-way split block: the whole token's K.
+SHARD_K_TOTAL = {"o/8": 4096, "down/8": 14336}
+
+
+def shard_bench(args, dev, bt, torch, synth):
+    """One device's share of a Llama-3-8B block split eight ways, M = 1: q|k|v
+    and gate|up by output features (the fused decode call on N / 8 rows), o and
+    down by input features (a K / 8 slice: token statistics, quantisation with
+    the whole token's statistics, the contraction to int32 partial sums, the
+    dequantisation).  The collectives between those calls (a maximum and a sum
+    of the statistics, a sum of the partials) are not run: one device's
+    kernels only, on its own statistics.  Weights rotate over > 1 GiB of copies
+    as in the decode leg."""
+    spec = synth.workload("shard")
+    share_bytes = sum(l.N * l.K // 4 for l in spec)
+    copies = max(1, math.ceil(ROTATE_BYTES / share_bytes))
+    layers = [DecodeLayer(l, copies, dev, bt, torch) for l in spec]
+    for L in layers:
+        if L.layer.name in SHARD_K_TOTAL:
+            L.stats = (torch.empty(1, dtype=torch.float32, device=dev),
+                       torch.empty(1, dtype=torch.float64, device=dev))
+            L.acc = torch.empty((1, L.layer.N), dtype=torch.int32, device=dev)
+
+    def stats(L):
+        bt.token_stats(L.x, out=L.stats)
+
+    def quant(L):
+        bt.quant_act_with_stats(L.x, L.stats[0], L.stats[1], SHARD_K_TOTAL[L.layer.name], out=L.codes)
+
+    def contract(L, r):
+        bt.linear_forward(*L.codes, L.packed[r], L.w_scale, out=L.y, acc_out=L.acc)
+
+    def dequant(L):
+        bt.dequant(L.acc, L.codes[1], L.w_scale, out=L.y)
+
+    def step(r):
+        for L in layers:
+            if L.layer.name in SHARD_K_TOTAL:
+                stats(L)
+                quant(L)
+                contract(L, r)
+                dequant(L)
+            else:
+                L.forward(bt, r)
+
+    for s in range(min(args.warmup, 2 * copies)):
+        step(s % copies)
+    torch.cuda.synchronize()
+    t = StepTimer(step, args.block_steps, copies, torch, cache_flush(torch, dev), eager=args.eager)
+    ms = t.median_ms(3)
+    t.close()
+    del t
+    rows = []
+    n = 400
+    for L in layers:
+        if L.layer.name in SHARD_K_TOTAL:
+            us = {"token_stats": b2b_us(lambda r, L=L: stats(L), n, 1, torch, dev, args.eager),
+                  "quant_act_with_stats": b2b_us(lambda r, L=L: quant(L), n, 1, torch, dev, args.eager),
+                  "contraction": b2b_us(lambda r, L=L: contract(L, r), n, copies, torch, dev, args.eager),
+                  "dequant": b2b_us(lambda r, L=L: dequant(L), n, 1, torch, dev, args.eager)}
+            split = "input features (K slice)"
+        else:
+            us = {"fused_decode": b2b_us(lambda r, L=L: L.forward(bt, r), n, copies, torch, dev, args.eager)}
+            split = "output features (N rows)"
+        rows.append({"name": L.layer.name, "K": L.layer.K, "N": L.layer.N, "split_by": split,
+                     "packed_bytes": L.weight_bytes, "kernel_us": {k: round(v, 2) for k, v in us.items()}})
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": "one device's share of the Llama-3-8B block split eight ways, M = 1: q|k|v 4096->768 "
+                        "and gate|up 4096->3584 by output features; o 512->4096 and down 1792->4096 by input "
+                        "features (K slices of 4096 and 14336)",
+            "per_device_packed_bytes": share_bytes, "weight_rotation_copies": copies,
+            "us_per_block": round(ms * 1e3, 2), "packed_GB_s": round(share_bytes / (ms * 1e-3) / 1e9, 1),
+            "collectives": "not run (between the calls of the K-sliced projections)",
+            "kernel_us_note": "average per launch, 400 launches of one kernel back to back in one graph "
+                              "(the contraction and fused decode over the rotating weight copies)",
+            "layers": rows}
+
+
 def cpu_baseline(args, synth):
     import oracle
 
@@ -981,7 +1085,7 @@ def main():
         # Secondary legs only (used for per-kernel counter runs); no headline line.
         for name, fn in (("decode_sizes", decode_sizes_bench), ("base3", base3_bench),
                          ("prefill", prefill_bench), ("hadamard", hadamard_bench),
-                         ("block", block_bench), ("backward", backward_bench),
+                         ("block", block_bench), ("shard", shard_bench), ("backward", backward_bench),
                          ("blend", blend_bench), ("pack", pack_bench)):
             if name in legs:
                 secondary[name] = fn(args, dev, bt, torch, synth)
@@ -1000,7 +1104,7 @@ def main():
     if not args.no_secondary:
         for name, fn in (("decode_sizes", decode_sizes_bench), ("base3", base3_bench),
                          ("prefill", prefill_bench), ("hadamard", hadamard_bench),
-                         ("block", block_bench), ("backward", backward_bench),
+                         ("block", block_bench), ("shard", shard_bench), ("backward", backward_bench),
                          ("blend", blend_bench), ("pack", pack_bench)):
             if name in legs:
                 secondary[name] = fn(args, dev, bt, torch, synth)

@@ -21,6 +21,7 @@ __all__ = [
     "base3_row_bytes", "pack_base3", "linear_forward_base3",
     "quant_act", "hadamard_quant_act", "linear_forward", "bitlinear", "bitlinear_forward",
     "hadamard_quant_act_i4", "linear_forward_i4", "hadamard_bitlinear_forward",
+    "token_stats", "quant_act_with_stats", "dequant",
     "BitLinear",
     "STATUS", "set_kernel_events",
 ]
@@ -82,6 +83,12 @@ def lib() -> ctypes.CDLL:
     L.bitnet_bitlinear_forward.restype = i32
     L.bitnet_hadamard_bitlinear_forward.argtypes = [p, p, f32, p, p, i64, i64, i64, p, p, p, p, p, p]
     L.bitnet_hadamard_bitlinear_forward.restype = i32
+    L.bitnet_token_stats.argtypes = [p, p, i64, i64, p, p, p]
+    L.bitnet_token_stats.restype = i32
+    L.bitnet_quant_act_with_stats.argtypes = [p, p, f32, i64, i64, i64, p, p, p, p, p, p]
+    L.bitnet_quant_act_with_stats.restype = i32
+    L.bitnet_dequant.argtypes = [p, p, p, i64, i64, p, p]
+    L.bitnet_dequant.restype = i32
     L.bitnet_bitlinear_forward_grouped.argtypes = [p, p, f32, p, p, p, i32, i64, i64, p, p, p, p,
                                                    p, p]
     L.bitnet_bitlinear_forward_grouped.restype = i32
@@ -507,6 +514,55 @@ def hadamard_bitlinear_forward(x, packed, w_scale, gain=None, eps: float = 1e-5,
                                                    _ptr(w_scale), M, N, K, _ptr(xq4), _ptr(x_scale),
                                                    _ptr(x_qsum), _ptr(out), _ptr(acc_out), _stream(dev)))
     return (out, acc_out) if acc_out is not None else out
+
+
+# --- row-parallel shards ----------------------------------------------------
+
+def token_stats(x, gain=None, out=None):
+    """Per-token statistics of a K slice (bitnet_token_stats): bf16 [M][K] ->
+    (amax float32 [M], sumsq float64 [M]); combine them over the shards with a
+    maximum and a sum before quant_act_with_stats."""
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    M, K = x.shape
+    _gain(gain, K, dev)
+    amax, sumsq = (None, None) if out is None else out
+    amax = _output(amax, "amax", torch.float32, (M,), dev)
+    sumsq = _output(sumsq, "sumsq", torch.float64, (M,), dev)
+    _check(lib().bitnet_token_stats(_ptr(x), _ptr(gain), M, K, _ptr(amax), _ptr(sumsq), _stream(dev)))
+    return amax, sumsq
+
+
+def quant_act_with_stats(x, amax, sumsq, k_total: int, gain=None, eps: float = 1e-5, out=None):
+    """Codes of a K slice from the whole token's statistics
+    (bitnet_quant_act_with_stats): -> (xq int8 [M][K], x_scale float32 [M],
+    x_qsum int32 [M] of the slice's codes)."""
+    torch = _torch()
+    _require(x, "x", torch.bfloat16, 2)
+    dev = x.device
+    M, K = x.shape
+    _gain(gain, K, dev)
+    _require_shape(amax, "amax", torch.float32, (M,), dev)
+    _require_shape(sumsq, "sumsq", torch.float64, (M,), dev)
+    xq, x_scale, x_qsum = _codes(out, M, K, dev)
+    _check(lib().bitnet_quant_act_with_stats(_ptr(x), _ptr(gain), ctypes.c_float(eps), M, K, int(k_total),
+                                             _ptr(amax), _ptr(sumsq), _ptr(xq), _ptr(x_scale), _ptr(x_qsum),
+                                             _stream(dev)))
+    return xq, x_scale, x_qsum
+
+
+def dequant(acc, x_scale, w_scale, out=None):
+    """y float32 [M][N] = acc * d_x[m] * d_w for int32 accumulators (bitnet_dequant)."""
+    torch = _torch()
+    _require(acc, "acc", torch.int32, 2)
+    dev = acc.device
+    M, N = acc.shape
+    _require_shape(x_scale, "x_scale", torch.float32, (M,), dev)
+    _require_at_least(w_scale, "w_scale", torch.float32, 1, dev)
+    out = _output(out, "out", torch.float32, (M, N), dev)
+    _check(lib().bitnet_dequant(_ptr(acc), _ptr(x_scale), _ptr(w_scale), M, N, _ptr(out), _stream(dev)))
+    return out
 
 
 def linear_forward_blend(x, W, packed, w_scale, lam: float, gain=None, eps: float = 1e-5, out=None,

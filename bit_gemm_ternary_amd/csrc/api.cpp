@@ -365,6 +365,52 @@ int bitnet_hadamard_bitlinear_forward(const uint16_t* x, const float* gain, floa
     return hip_status(e, fn);
 }
 
+int bitnet_token_stats(const uint16_t* x, const float* gain, int64_t M, int64_t K, float* amax,
+                       double* sumsq, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_token_stats";
+    if (M < 0 || M > kMaxRows) return fail(BITNET_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
+    int s = check_k(K, fn);
+    if (s != BITNET_OK || M == 0) return s;
+    if (!x || !amax || !sumsq) return fail(BITNET_ERR_NULL, "%s: x, amax and sumsq must not be NULL", fn);
+    if (!aligned(x, 16) || (gain && !aligned(gain, 16)))
+        return fail(BITNET_ERR_ALIGN, "%s: x and gain must be 16-byte aligned", fn);
+    if (!aligned(amax, 4) || !aligned(sumsq, 8))
+        return fail(BITNET_ERR_ALIGN, "%s: amax must be 4-byte and sumsq 8-byte aligned", fn);
+    return hip_status(bitnet::launch_token_stats(x, gain, M, K, amax, sumsq, (hipStream_t)stream), fn);
+}
+
+int bitnet_quant_act_with_stats(const uint16_t* x, const float* gain, float eps, int64_t M,
+                                int64_t K, int64_t K_total, const float* amax, const double* sumsq,
+                                int8_t* xq, float* x_scale, int32_t* x_qsum, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_quant_act_with_stats";
+    int s = validate_quant(x, gain, eps, M, K, xq, x_scale, x_qsum, false, fn);
+    if (s != BITNET_OK) return s;
+    if (K_total < K || K_total > (int64_t{1} << 24))
+        return fail(BITNET_ERR_SHAPE, "%s: K_total=%lld must lie in [K, 2^24]", fn, (long long)K_total);
+    if (M == 0) return BITNET_OK;
+    if (!amax || !sumsq) return fail(BITNET_ERR_NULL, "%s: amax and sumsq must not be NULL", fn);
+    if (!aligned(amax, 4) || !aligned(sumsq, 8))
+        return fail(BITNET_ERR_ALIGN, "%s: amax must be 4-byte and sumsq 8-byte aligned", fn);
+    return hip_status(bitnet::launch_quant_act_with_stats(x, gain, eps, M, K, K_total, amax, sumsq, xq, x_scale,
+                                                          x_qsum, (hipStream_t)stream),
+                      fn);
+}
+
+int bitnet_dequant(const int32_t* acc, const float* x_scale, const float* w_scale, int64_t M, int64_t N,
+                   float* y, void* stream) {
+    DisarmEvents disarm;
+    const char* fn = "bitnet_dequant";
+    if (M < 0 || M > kMaxRows || N < 0 || N > kMaxRows)
+        return fail(BITNET_ERR_SHAPE, "%s: M=%lld or N=%lld out of range", fn, (long long)M, (long long)N);
+    if (M == 0 || N == 0) return BITNET_OK;
+    if (!acc || !x_scale || !w_scale || !y) return fail(BITNET_ERR_NULL, "%s: no argument may be NULL", fn);
+    if (!aligned(acc, 4) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(y, 4))
+        return fail(BITNET_ERR_ALIGN, "%s: acc, x_scale, w_scale and y must be 4-byte aligned", fn);
+    return hip_status(bitnet::launch_dequant(acc, x_scale, w_scale, M, N, y, (hipStream_t)stream), fn);
+}
+
 int bitnet_bitlinear_forward_grouped(const uint16_t* x, const float* gain, float eps,
                                      const uint8_t* packed, const float* w_scales,
                                      const int64_t* group_rows, int groups, int64_t M, int64_t K,

@@ -49,6 +49,19 @@ hipError_t noalloc_scratch(int device, void** ptr);
 // --- activation quantisation (quant_act.hip, hadamard_quant.hip) ------------
 hipError_t launch_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M, int64_t K,
                             int8_t* xq, float* x_scale, int32_t* x_qsum, hipStream_t stream);
+// Row-parallel shards (quant_act.hip): per token, the absmax of x * gain and
+// the float64 sum of x^2 over this K slice; then the codes of the slice from
+// the whole token's absmax and sum of squares (after the cross-shard maximum
+// and sum), d_x with the mean over k_total values, and the slice's code sum.
+hipError_t launch_token_stats(const uint16_t* x, const float* gain, int64_t M, int64_t K, float* amax,
+                              double* sumsq, hipStream_t stream);
+hipError_t launch_quant_act_with_stats(const uint16_t* x, const float* gain, float eps, int64_t M,
+                                       int64_t K, int64_t k_total, const float* amax,
+                                       const double* sumsq, int8_t* xq, float* x_scale,
+                                       int32_t* x_qsum, hipStream_t stream);
+// y = acc * d_x[m] * d_w for int32 accumulators [M][N] (dequant.hip).
+hipError_t launch_dequant(const int32_t* acc, const float* x_scale, const float* w_scale, int64_t M,
+                          int64_t N, float* y, hipStream_t stream);
 hipError_t launch_hadamard_quant_act(const uint16_t* x, const float* gain, float eps, int64_t M,
                                      int64_t K, double sqrt_k, int8_t* xq, float* x_scale,
                                      int32_t* x_qsum, hipStream_t stream);

@@ -17,6 +17,9 @@ stored [N][K] as in a bias-free linear layer):
 * ``block``    the seven projections of a Llama-3-8B block (q 4096->4096,
                k/v 4096->1024, o 4096->4096, gate/up 4096->14336,
                down 14336->4096) at M in (1, 16, 256); activations N(0, 1).
+* ``shard``    one device's share of that block split eight ways, M = 1:
+               q|k|v and gate|up by output features (4096->768, 4096->3584),
+               o and down by input features (512->4096, 1792->4096).
 
 Seeds: ``seed = 1000 * workload_id + 10 * layer + role`` with role 0 for the
 weights, 1 for the activations and 2 for the choice of outlier channels.
@@ -27,7 +30,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "hadamard": 4, "block": 5}
+WORKLOAD_IDS = {"tiny": 1, "decode": 2, "prefill": 3, "hadamard": 4, "block": 5, "shard": 6}
 
 BLOCK_LAYERS = (  # name, K (in), N (out)
     ("q", 4096, 4096),
@@ -37,6 +40,13 @@ BLOCK_LAYERS = (  # name, K (in), N (out)
     ("gate", 4096, 14336),
     ("up", 4096, 14336),
     ("down", 14336, 4096),
+)
+
+SHARD_LAYERS = (  # name, K (in), N (out): the block cut eight ways
+    ("qkv/8", 4096, 768),
+    ("o/8", 512, 4096),
+    ("gate_up/8", 4096, 3584),
+    ("down/8", 1792, 4096),
 )
 
 
@@ -85,6 +95,9 @@ def workload(name: str, M: int | None = None) -> list[Layer]:
         m = 1 if M is None else M
         return [Layer("block", lname, m, K, N, layer_index=i)
                 for i, (lname, K, N) in enumerate(BLOCK_LAYERS)]
+    if name == "shard":
+        return [Layer("shard", lname, 1, K, N, layer_index=i)
+                for i, (lname, K, N) in enumerate(SHARD_LAYERS)]
     raise KeyError(name)
 
 

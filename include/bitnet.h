@@ -342,6 +342,67 @@ int bitnet_hadamard_bitlinear_forward(const uint16_t* x, const float* gain, floa
 
 /*
  * ---------------------------------------------------------------------------
+ * Row-parallel shards.  When the input features K of a layer are split over G
+ * devices, each holds a K slice of every token and of the packed weights
+ * (columns k0/4 .. (k0 + Ks)/4 of each packed row: slices start at multiples
+ * of 64).  The per-token absmax and mean of x^2 of [FT] "양자화 메커니즘" are
+ * over the whole token, so a shard computes its slice's part, the parts are
+ * combined across devices (a maximum and a sum; the collective itself is the
+ * caller's), and the slice is quantised with the combined values: its codes
+ * are then exactly those an unsharded call writes for those positions.  The
+ * contraction of a slice (bitnet_linear_forward with acc) gives int32 partial
+ * sums whose sum over the shards is the unsharded acc exactly ([FT]
+ * "계산 패러다임": integer additions), and bitnet_dequant applies the scales.
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * Per-token statistics of a K slice.
+ *   x       in   bf16 [M][K] slice (its own row stride K), 16-byte aligned.
+ *   gain    in   float32 [K] (this slice's part of the gain) or NULL; 16-byte aligned.
+ *   amax    out  float32 [M]: max_k |x * gain| over the slice (exact).
+ *   sumsq   out  float64 [M]: sum_k x^2 over the slice (squares exact in
+ *                float32, summed in float32 chains and float64); 8-byte aligned.
+ * K as bitnet_quant_act.  M = 0 is a no-op.
+ */
+int bitnet_token_stats(const uint16_t* x, const float* gain, int64_t M, int64_t K, float* amax,
+                       double* sumsq, void* stream);
+
+/*
+ * Codes of a K slice from the whole token's statistics.
+ *   x, gain, eps, xq    as bitnet_quant_act, for the slice (K values per token).
+ *   K_total             the whole token's K (K <= K_total <= 2^24): the mean of
+ *                       x^2 divides by it.
+ *   amax, sumsq   in    float32 [M], float64 [M]: the maxima and sums of the
+ *                       bitnet_token_stats outputs over all shards.
+ *   x_scale       out   float32 [M]: d_x of the whole token (equal on every
+ *                       shard; equal to the unsharded d_x up to the order of
+ *                       the float64 sum of x^2).
+ *   x_qsum        out   int32 [M]: the sum of this slice's codes (what the
+ *                       slice's contraction subtracts).
+ * Codes q = clamp(rint(u * float32(127 / amax)), -128, 127); with amax the
+ * maximum over all shards the clamp never acts and the codes equal the
+ * unsharded ones.  A token with amax < 2^-120 gets zero codes and d_x = 0.
+ */
+int bitnet_quant_act_with_stats(const uint16_t* x, const float* gain, float eps, int64_t M,
+                                int64_t K, int64_t K_total, const float* amax, const double* sumsq,
+                                int8_t* xq, float* x_scale, int32_t* x_qsum, void* stream);
+
+/*
+ * Dequantisation of int32 accumulators ([FT] "양자화 메커니즘" rescale; [QP]
+ * dequantise): y[m][n] = (acc[m][n] * d_x[m]) * d_w, float32, in the order of
+ * the contraction calls' own epilogue.
+ *   acc      in   int32 [M][N] (e.g. the shards' partial sums added up),
+ *                 4-byte aligned.
+ *   x_scale  in   float32 [M]; w_scale in float32 [2] (d_w at [0]).
+ *   y        out  float32 [M][N], 4-byte aligned.
+ * M = 0 or N = 0 is a no-op.
+ */
+int bitnet_dequant(const int32_t* acc, const float* x_scale, const float* w_scale, int64_t M, int64_t N,
+                   float* y, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
  * Backward pass under the straight-through estimator ([FT] "Straight-Through
  * Estimator (STE)를 이용한 학습": round() is given the gradient 1, so both
  * quantisers pass the gradient through).  Seen by the estimator the forward is

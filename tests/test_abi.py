@@ -182,6 +182,44 @@ def test_hadamard_fused_forward_argument_errors(L):
     assert _hfused(L, M=0, x=0, xq4=0, P=0, y=0) == 0
 
 
+def test_shard_argument_errors(L):
+    p = ctypes.c_void_p
+    A8 = 0x10008
+    st = lambda x=A16, gain=None, M=2, K=256, amax=A4, ss=A8: L.bitnet_token_stats(
+        p(x), None if gain is None else p(gain), M, K, p(amax), p(ss), None)
+    assert st(M=-1) == 2
+    assert st(K=100) == 2
+    assert st(x=0) == 1
+    assert st(ss=0) == 1
+    assert st(x=A4) == 4
+    assert st(gain=A4) == 4
+    assert st(ss=A4) == 4                  # float64 output needs 8-byte alignment
+    assert st(M=0, x=0) == 0
+
+    def qs(x=A16, M=2, K=256, Kt=1024, amax=A4, ss=A8, xq=A16, sx=A4, q=A4, eps=1e-5):
+        return L.bitnet_quant_act_with_stats(p(x), None, ctypes.c_float(eps), M, K, Kt, p(amax), p(ss),
+                                             p(xq), p(sx), p(q), None)
+    assert qs(Kt=128) == 2                 # K_total below K
+    assert qs(Kt=(1 << 24) + 1) == 2
+    assert qs(K=100) == 2
+    assert qs(eps=-1.0) == 7
+    assert qs(amax=0) == 1
+    assert qs(xq=0) == 1
+    assert qs(ss=A4) == 4
+    assert qs(xq=A4) == 4
+    assert qs(M=0, x=0, amax=0) == 0
+
+    dq = lambda acc=A4, sx=A4, ws=A4, M=2, N=8, y=A4: L.bitnet_dequant(p(acc), p(sx), p(ws), M, N, p(y), None)
+    assert dq(M=-1) == 2
+    assert dq(N=-1) == 2
+    assert dq(acc=0) == 1
+    assert dq(y=0) == 1
+    assert dq(acc=BAD) == 4
+    assert dq(y=BAD) == 4
+    assert dq(M=0, acc=0) == 0
+    assert dq(N=0, y=0) == 0
+
+
 def test_kernel_events_hook_is_exported(L):
     assert L.bitnet_set_kernel_events(None, None) == 0
 

@@ -142,6 +142,26 @@ def test_hadamard_bitlinear_forward_calls():
         f(x, p, w, codes=(D((1, k // 2), i8), D((1,), f32), D((1,), i32)), out=out)
 
 
+def test_shard_calls():
+    x = D((M, K), bf16)
+    raises(lambda: bt.token_stats(x, gain=D((K + 8,), f32)), "gain")
+    raises(lambda: bt.token_stats(x, out=(D((M + 1,), f32), D((M,), torch.float64))), "amax")
+    with pytest.raises(TypeError, match="sumsq"):
+        bt.token_stats(x, out=(D((M,), f32), D((M,), f32)))
+    amax, ss = D((M,), f32), D((M,), torch.float64)
+    raises(lambda: bt.quant_act_with_stats(x, D((M - 1,), f32), ss, 4 * K, out=codes()), "amax")
+    with pytest.raises(TypeError, match="sumsq"):
+        bt.quant_act_with_stats(x, amax, D((M,), f32), 4 * K, out=codes())
+    raises(lambda: bt.quant_act_with_stats(x, amax, ss, 4 * K, out=codes(k=K - 64)), "xq")
+    raises(lambda: bt.quant_act_with_stats(x, amax, ss, 4 * K, gain=D((K // 2,), f32), out=codes()), "gain")
+    acc = D((M, N), i32)
+    raises(lambda: bt.dequant(acc, D((M + 1,), f32), D((2,), f32), out=D((M, N), f32)), "x_scale")
+    raises(lambda: bt.dequant(acc, D((M,), f32), D((0,), f32), out=D((M, N), f32)), "w_scale")
+    raises(lambda: bt.dequant(acc, D((M,), f32), D((2,), f32), out=D((M, N - 4), f32)), "out")
+    with pytest.raises(TypeError, match="acc"):
+        bt.dequant(D((M, N), f32), D((M,), f32), D((2,), f32))
+
+
 def test_base3_calls():
     p = D((N, K // 4), u8)
     rb = bt.base3_row_bytes(K)
