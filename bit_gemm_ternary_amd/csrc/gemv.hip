@@ -154,6 +154,25 @@ __device__ __forceinline__ void xreduce(int (&p)[NV], int lane) {
 
 constexpr int log2_of(int v) { return v <= 1 ? 0 : 1 + log2_of(v / 2); }
 
+// The fused kernels' codes in LDS, piece-major: the 16-byte piece q (codes
+// 16q .. 16q + 15) of chunk c sits at q * kPlane + 16 c.  A lane reading piece
+// q of its own chunk then meets its 15 neighbours on 15 other 16-byte bank
+// groups (chunk-major rows, 64 bytes apart, put four lanes on each group: the
+// reads were 4-way bank conflicts), and with the plane stride a multiple of
+// 256 bytes plus 64 the 8-byte code writes of consecutive vectors (one
+// thread's 8 codes) land on distinct banks as well.
+template <int CH>
+struct CodeLds {
+    static constexpr int kPlane = CH * 1024 + 64;
+    static constexpr int kBytes = 4 * kPlane;
+    // Byte address of the codes 8v .. 8v + 7.
+    __device__ static __forceinline__ int of_vector(int v) {
+        return ((v >> 1) & 3) * kPlane + 16 * (v >> 3) + 8 * (v & 1);
+    }
+    // Byte address of piece q of chunk c.
+    __device__ static __forceinline__ int of_piece(int c, int q) { return q * kPlane + 16 * c; }
+};
+
 // Largest batch (rows in flight per register set) for CH chunks per lane.
 template <int CH>
 constexpr int max_batch() {
@@ -192,7 +211,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
     constexpr int XV = (CH * 512 + NT - 1) / NT;  // 8-value bf16 vectors per thread per token
     static_assert(NV <= kWave && (NV & (NV - 1)) == 0, "values per batch: a power of 2, <= 64");
     static_assert(XV * NT == CH * 512, "the fused prologue's vectors tile the code array exactly");
-    __shared__ __align__(16) int8_t codes[MT][FUSED ? CH * 4096 : 16];
+    __shared__ __align__(16) int8_t codes[MT][FUSED ? CodeLds<CH>::kBytes : 16];
     __shared__ float red_f[MT][NW];
     __shared__ double red_d[MT][NW];
     __shared__ int red_i[MT][NW];
@@ -329,10 +348,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
         // The per-token factor d_x = amax * rstd / 127 is computed here too, by
         // every wave, in the same straight-line code as the codes, so its
         // latency overlaps the code work instead of following the second
-        // barrier.  Vectors past K give zero
-        // codes, written to LDS past the token's K codes (the array holds
-        // XV * NT * 8 >= CH * 4096 codes) and never read.  Each thread also sums
-        // its codes; the wave totals go to LDS with the codes.
+        // barrier.  Vectors past K give zero codes, written to the LDS slots
+        // of chunks past K (the array has room for the XV * NT * 8 = CH * 4096
+        // codes of every vector) and never read.  Each thread also sums its
+        // codes; the wave totals go to LDS with the codes.
 #pragma unroll
         for (int tok = 0; tok < MT; ++tok) {
             float amax = red_f[tok][0];
@@ -359,7 +378,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
                 const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
                                                           __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u),
                                                           0x05040100u);
-                *reinterpret_cast<uint2*>(&codes[tok][8 * v]) = make_uint2(lo, hi);
+                *reinterpret_cast<uint2*>(&codes[tok][CodeLds<CH>::of_vector(v)]) = make_uint2(lo, hi);
                 part = dot4(lo, 0x01010101u, part);
                 part = dot4(hi, 0x01010101u, part);
             }
@@ -379,7 +398,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint4 v = make_uint4(0, 0, 0, 0);
-                    if (c < nchunk) v = reinterpret_cast<const uint4*>(&codes[tok][64 * c])[q];
+                    if (c < nchunk) v = *reinterpret_cast<const uint4*>(&codes[tok][CodeLds<CH>::of_piece(c, q)]);
                     xv[tok][j][4 * q] = v.x;
                     xv[tok][j][4 * q + 1] = v.y;
                     xv[tok][j][4 * q + 2] = v.z;
@@ -395,7 +414,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
             for (int tok = 0; tok < MT; ++tok)
                 for (int v = t; v < K / 16; v += NT)
                     reinterpret_cast<uint4*>(a.xq_out + (int64_t)tok * K)[v] =
-                        reinterpret_cast<const uint4*>(codes[tok])[v];
+                        *reinterpret_cast<const uint4*>(&codes[tok][CodeLds<CH>::of_piece(v >> 2, v & 3)]);
             if (t == 0) {
 #pragma unroll
                 for (int tok = 0; tok < MT; ++tok) {
@@ -561,7 +580,7 @@ __global__ __launch_bounds__(256) void decode1_kernel(const Args a) {
     constexpr int LV = log2_of(NV);
     constexpr int XV = CH * 512 / NT;   // 8-value vectors of the token per thread
     static_assert(RB <= 16 && RB * CH <= 16, "one register set of rows");
-    __shared__ __align__(16) int8_t codes[CH * 4096];
+    __shared__ __align__(16) int8_t codes[CodeLds<CH>::kBytes];
     __shared__ float red_f[NW];
     __shared__ double red_d[NW];
     __shared__ int red_i[NW];
@@ -692,7 +711,7 @@ __global__ __launch_bounds__(256) void decode1_kernel(const Args a) {
                                                   __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u), 0x05040100u);
         const uint32_t hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(b[7], b[6], 0x0c0c0400u),
                                                   __builtin_amdgcn_perm(b[5], b[4], 0x0c0c0400u), 0x05040100u);
-        *reinterpret_cast<uint2*>(&codes[8 * v]) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(&codes[CodeLds<CH>::of_vector(v)]) = make_uint2(lo, hi);
         part = dot4(lo, 0x01010101u, part);
         part = dot4(hi, 0x01010101u, part);
     }
@@ -720,7 +739,7 @@ __global__ __launch_bounds__(256) void decode1_kernel(const Args a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < nchunk) v = reinterpret_cast<const uint4*>(&codes[64 * c])[q];
+            if (c < nchunk) v = *reinterpret_cast<const uint4*>(&codes[CodeLds<CH>::of_piece(c, q)]);
             xv[j][4 * q] = v.x;
             xv[j][4 * q + 1] = v.y;
             xv[j][4 * q + 2] = v.z;
@@ -738,7 +757,8 @@ __global__ __launch_bounds__(256) void decode1_kernel(const Args a) {
     // after the rows, where only the storing lanes wait for it.
     if (blockIdx.x == 0) {
         for (int v = t; v < K / 16; v += NT)
-            reinterpret_cast<uint4*>(a.xq_out)[v] = reinterpret_cast<const uint4*>(codes)[v];
+            reinterpret_cast<uint4*>(a.xq_out)[v] =
+                *reinterpret_cast<const uint4*>(&codes[CodeLds<CH>::of_piece(v >> 2, v & 3)]);
         if (t == 0) {
             a.x_scale_out[0] = token_scale(amax, ss, inv_count(K), eps, 1.0 / 127.0);
             a.x_qsum_out[0] = tok_sum;
