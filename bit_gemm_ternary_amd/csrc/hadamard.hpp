@@ -132,15 +132,22 @@ __device__ __forceinline__ void load_bf16(const uint16_t* p, float (&v)[E]) {
     }
 }
 
+// Byte address in LDS of code k for store_codes: natural order.  A layout's
+// addr must be additive over disjoint bits of k (a thread's base index and its
+// register offsets are mapped separately and added).
+struct NaturalCodes {
+    static constexpr int addr(int k) { return k; }
+};
+
 // Integer codes of a thread's transform values after Fwht::run: rint(v * scale)
-// for |v| * scale < 127.5, stored as bytes at their natural index in lds8
-// (K bytes, free LDS).  Adding 1.5 * 2^23 to the product rounds it to an
+// for |v| * scale < 127.5, stored as bytes at L::addr(index) in lds8 (free
+// LDS; K bytes in natural order).  Adding 1.5 * 2^23 to the product rounds it to an
 // integer (ties to even, the rint of the definition) and leaves it, two's
 // complement, in the low byte of the float's bits; with scale = rn(c / amax)
 // and |v| <= amax the product's magnitude stays below c + 0.5, so no clamp is
 // needed for integer c <= 127.  Registers that hold adjacent indices are stored together (a byte,
 // a 16-bit or a 32-bit word per store).  Returns the sum of the thread's codes.
-template <int P, int E>
+template <int P, int E, class L = NaturalCodes>
 __device__ __forceinline__ int store_codes(const float (&v)[E], float scale, int8_t* lds8, int t) {
     using F = Fwht<P, E>;
     uint32_t b[E];
@@ -154,7 +161,7 @@ __device__ __forceinline__ int store_codes(const float (&v)[E], float scale, int
     constexpr int G = 1 << F::template xbits<J>();   // adjacent codes per register group
     constexpr int W = E / G;
     constexpr int B0 = J * F::LOG_E;
-    int8_t* cdst = lds8 + F::template base<J>(t);
+    int8_t* cdst = lds8 + L::addr(F::template base<J>(t));
     int qs = 0;
     if constexpr (G >= 4) {
 #pragma unroll
@@ -164,7 +171,7 @@ __device__ __forceinline__ int store_codes(const float (&v)[E], float scale, int
                 const uint32_t word = pack4(b[rl + (4 * q) * W], b[rl + (4 * q + 1) * W],
                                             b[rl + (4 * q + 2) * W], b[rl + (4 * q + 3) * W]);
                 qs = __builtin_amdgcn_sdot4((int)word, 0x01010101, qs, false);
-                *reinterpret_cast<uint32_t*>(cdst + (rl << B0) + 4 * q) = word;
+                *reinterpret_cast<uint32_t*>(cdst + L::addr((rl << B0) + 4 * q)) = word;
             }
     } else {
 #pragma unroll
@@ -174,10 +181,10 @@ __device__ __forceinline__ int store_codes(const float (&v)[E], float scale, int
 #pragma unroll
         for (int rl = 0; rl < W; ++rl) {
             if constexpr (G == 2)
-                *reinterpret_cast<uint16_t*>(cdst + (rl << B0)) =
+                *reinterpret_cast<uint16_t*>(cdst + L::addr(rl << B0)) =
                     (uint16_t)__builtin_amdgcn_perm(b[rl + W], b[rl], 0x0c0c0400u);
             else
-                cdst[rl << B0] = (int8_t)b[rl];
+                cdst[L::addr(rl << B0)] = (int8_t)b[rl];
         }
     }
     return qs;

@@ -23,7 +23,7 @@
 //   2. sum of x^2 (exact float32 squares in four float32 chains, combined in
 //      float64), the gain, the transform (LDS exchanges between its phases);
 //   3. absmax and sum of squares over the workgroup, one barrier;
-//   4. the codes into LDS at their natural index, with the code sums, one
+//   4. the codes into LDS (piece-major, below), with the code sums, one
 //      barrier;
 //   5. each lane's chunks of codes from LDS as nibble dwords (in a group of
 //      16 codes, byte j holds code j low and code 8 + j high); workgroup 0
@@ -58,6 +58,20 @@ struct HArgs {
     float* x_scale;          // d_x, written by workgroup 0
     int32_t* x_qsum;         // sum of the codes, written by workgroup 0
     int32_t* acc;            // [N] or NULL
+};
+
+// The codes in LDS piece-major: the 16-byte piece q of chunk c (codes
+// 64c + 16q .. 64c + 16q + 15) at q * kPlane + 16 c.  A lane reading piece q
+// of its own chunk then meets its 15 neighbours on 15 other 16-byte bank
+// groups (chunk-major rows 64 bytes apart put four lanes on each group), and
+// a plane stride of K / 4 + 64 bytes keeps the transform's grouped code stores
+// on distinct banks as well (one exception, two-way, for the 8-code groups at
+// K = 8192).  The address is a bit permutation of k plus the plane padding,
+// additive over disjoint bits as store_codes requires.
+template <int P>
+struct PieceMajorCodes {
+    static constexpr int kPlane = (1 << P) / 4 + 64;
+    static constexpr int addr(int k) { return ((k >> 4) & 3) * kPlane + ((k >> 6) << 4) + (k & 15); }
 };
 
 template <int P>
@@ -187,7 +201,9 @@ __global__ __launch_bounds__(threads_for<P>()) void hdecode_kernel(const HArgs a
     // below the tiny absmax has scale 0 and all-zero codes.
     const float scale = amax < kTinyAbsmax ? 0.f : 7.0f / amax;
     int8_t* lds8 = reinterpret_cast<int8_t*>(lds);
-    int qs = hadamard::store_codes<P, E>(v, scale, lds8, t);
+    using CL = PieceMajorCodes<P>;
+    static_assert(4 * CL::kPlane <= 4 * F::LDS_FLOATS, "the codes fit the transform's LDS");
+    int qs = hadamard::store_codes<P, E, CL>(v, scale, lds8, t);
     qs = wave_sum_dpp(qs);
     if (lane == 0) red_i[wave] = qs;
     __syncthreads();
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(threads_for<P>()) void hdecode_kernel(const HArgs a
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             uint4 q = make_uint4(0, 0, 0, 0);
-            if (c < NCH) q = reinterpret_cast<const uint4*>(lds8 + 64 * c)[d];
+            if (c < NCH) q = *reinterpret_cast<const uint4*>(lds8 + d * CL::kPlane + 16 * c);
             xv[j][2 * d] = (q.x & 0x0F0F0F0Fu) | ((q.z & 0x0F0F0F0Fu) << 4);
             xv[j][2 * d + 1] = (q.y & 0x0F0F0F0Fu) | ((q.w & 0x0F0F0F0Fu) << 4);
         }
