@@ -144,3 +144,18 @@ def test_dequant_extreme_accumulators(dev):
     want = (acc.astype(np.float32) * dx[:, None]) * dw    # float32 arithmetic, the same two roundings
     np.testing.assert_array_equal(y, want)
     assert y[0, 0] == 0
+
+
+@pytest.mark.parametrize("M,K,with_gain", [(1, 4096, False), (5, 14336, True), (64, 512, False)])
+def test_one_shard_is_the_unsharded_quantisation(dev, M, K, with_gain):
+    """With a single shard the statistics pass and the quantisation from them
+    reduce in the same order as bitnet_quant_act: codes, sums and d_x are
+    bit-identical to it."""
+    x = bf16_to_dev(synth.activations(M, K, 3100 + M, 3101, outlier_frac=0.01, outlier_factor=20.0), dev)
+    gain = to_dev(np.random.default_rng(3102).uniform(0.5, 1.5, K).astype(np.float32), dev) if with_gain else None
+    amax, sumsq = bt.token_stats(x, gain)
+    q1, d1, s1 = bt.quant_act_with_stats(x, amax, sumsq, K, gain=gain)
+    q0, d0, s0 = bt.quant_act(x, gain)
+    np.testing.assert_array_equal(host(q1), host(q0))
+    np.testing.assert_array_equal(host(s1), host(s0))
+    np.testing.assert_array_equal(host(d1), host(d0))
