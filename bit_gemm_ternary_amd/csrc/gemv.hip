@@ -568,8 +568,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(const Args a) {
 //   3. this thread's share of the codes into LDS, with its code sum and its
 //      part of sum x^2 (exact float32 squares in four float32 chains,
 //      combined in float64), one barrier;
-//   4. the wave's code registers from LDS, the dot products of each row as its
-//      loads land, one transposing reduction over the rows, the stores.
+//   4. the wave's code registers from LDS and the token's d_x, the dot
+//      products of each row as its loads land, one transposing reduction over
+//      the rows, the stores.
 // The arithmetic of every step is that of decode_kernel above.
 // ---------------------------------------------------------------------------
 template <int CH, int RB, bool GAIN>
@@ -731,15 +732,18 @@ __global__ __launch_bounds__(256) void decode1_kernel(const Args a) {
     }
     __syncthreads();
 
-    // 4. Code registers, token scale and sum; the rows.
+    // 4. Code registers, token scale and sum; the rows.  Every chunk slot of
+    // the LDS array holds codes (step 3 writes all XV * NT vectors, zeros past
+    // K) and the weights of chunks past K load as zeros, so the code reads
+    // need no bounds test (a masked read costs a branch and register clears
+    // right where the rows start).
     uint32_t xv[CH][16];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
         const int c = lane + kWave * j;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < nchunk) v = *reinterpret_cast<const uint4*>(&codes[CodeLds<CH>::of_piece(c, q)]);
+            const uint4 v = *reinterpret_cast<const uint4*>(&codes[CodeLds<CH>::of_piece(c, q)]);
             xv[j][4 * q] = v.x;
             xv[j][4 * q + 1] = v.y;
             xv[j][4 * q + 2] = v.z;
@@ -753,14 +757,16 @@ __global__ __launch_bounds__(256) void decode1_kernel(const Args a) {
         tok_sum += red_i[wv];
         ss += red_d[wv];
     }
-    // d_x (float64 chain with a quarter-rate reciprocal square root) is formed
-    // after the rows, where only the storing lanes wait for it.
+    // d_x (a float64 chain with a quarter-rate reciprocal square root) is
+    // formed before the rows, while their loads are still landing: after them
+    // it would lengthen the work left once the last weights arrive.
+    const float tok_scale = token_scale(amax, ss, inv_count(K), eps, 1.0 / 127.0);
     if (blockIdx.x == 0) {
         for (int v = t; v < K / 16; v += NT)
             reinterpret_cast<uint4*>(a.xq_out)[v] =
                 *reinterpret_cast<const uint4*>(&codes[CodeLds<CH>::of_piece(v >> 2, v & 3)]);
         if (t == 0) {
-            a.x_scale_out[0] = token_scale(amax, ss, inv_count(K), eps, 1.0 / 127.0);
+            a.x_scale_out[0] = tok_scale;
             a.x_qsum_out[0] = tok_sum;
         }
     }
@@ -797,7 +803,6 @@ __global__ __launch_bounds__(256) void decode1_kernel(const Args a) {
     if ((lane & ((kWave >> LV) - 1)) == 0 && idx < RB) {
         const int64_t r = (int64_t)g + (int64_t)idx * W;
         if (r < N) {
-            const float tok_scale = token_scale(amax, ss, inv_count(K), eps, 1.0 / 127.0);
             const int acc = p[0] - tok_sum;
             if (acc_out != nullptr) acc_out[r] = acc;
             y_out[r] = ((float)acc * tok_scale) * (groups == 1 ? dw0 : a.scales.of(r, dw0));
