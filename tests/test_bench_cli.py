@@ -53,3 +53,16 @@ def test_committed_summaries_carry_bench_data():
         assert len(lines) == 1, path
         data = json.loads(lines[0][len("bench-data: "):])
         assert len(data["source_sha256"]) == 64
+
+
+def test_committed_summaries_match_the_kernel_sources():
+    # the counters behind roofline.traffic were taken on the sources in the tree:
+    # a kernel change without new counters would leave the benchmark reporting
+    # traffic null
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_paths", BENCH)
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    assert bench.summary_data(bench.TRAFFIC_SUMMARY, bench.KERNEL_SOURCES) is not None
+    assert bench.summary_data(bench.GEMM_SUMMARY, bench.GEMM_SOURCES) is not None
