@@ -122,7 +122,7 @@ COPY_BYTES = 256 << 20
 READ_REF_BYTES = 2 << 30
 CSRC = os.path.join(ROOT, "bit_gemm_ternary_amd", "csrc")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode1_kernel.decode_M1.hbm_traffic.md")
-KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("gemv.hip", "common.hpp")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("gemv.hip", "common.hpp", "xreduce.hpp")]
 GEMM_SUMMARY = os.path.join(ROOT, "profiles", "gemm_kernel.prefill_M2048_K4096_N14336.counters.md")
 GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("gemm_mfma.hip", "common.hpp")]
 

@@ -43,8 +43,12 @@ def test_pack_base3_matches_the_oracle(orc, dev, N, K):
     np.testing.assert_array_equal(got, orc.pack_base3(q, rb))
 
 
+# The shapes reach every batch layout of the GEMV: one to sixteen rows per
+# wave in one register set, and two alternating sets at one to four chunks per
+# lane (40000 x 4096, 20000 x 8192, 9000 x 12800, 5000 x 16384).
 @pytest.mark.parametrize("N,K", [(1, 64), (77, 64), (1000, 320), (4096, 4096), (11008, 4096), (4096, 11008),
-                                 (5000, 16384), (300, 20480), (4099, 8192)])
+                                 (5000, 16384), (300, 20480), (4099, 8192), (40000, 4096), (20000, 8192),
+                                 (9000, 12800), (32768, 4096)])
 def test_linear_forward_base3_matches_the_oracle(orc, dev, N, K):
     W = synth.weights(N, K, seed=610 + N % 89)
     packed, d_w, _, q = orc.pack_weights(W)
