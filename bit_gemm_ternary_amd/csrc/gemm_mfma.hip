@@ -625,8 +625,7 @@ hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const int32_t* x_q
 template <int XF>
 struct Tiles {
     using Large = GemmCfg<448, 128, 7, 2, 1, 2, XF>;        // 14 waves, wave tile 64 x 64
-    using Mid = GemmCfg<256, 128, 4, 2, 1, 2, XF>;          // 8 waves, wave tile 64 x 64
-    using Wide = GemmCfg<256, 64, 4, 1, 1, 2, XF>;          // 4 waves, wave tile 64 x 64
+    using Square = GemmCfg<128, 128, 4, 2, 1, 2, XF>;       // 8 waves, wave tile 32 x 64
     using TallK3 = GemmCfg<128, 64, 2, 2, 1, 2, XF, 3>;     // 3 K groups of 4 waves (64 x 32)
     using Tiny = GemmCfg<64, 64, 2, 2, 2, 2, XF>;           // 4 waves, wave tile 32 x 32
     using TinyK2 = GemmCfg<64, 64, 2, 2, 2, 2, XF, 2>;      // 2 K groups of 4 waves
@@ -635,24 +634,29 @@ struct Tiles {
 
 constexpr int64_t kCus = 256;
 
-// The largest tile that still gives every CU enough work: two rounds of the
-// large tile, one of the mid tile, one of the wide tile (few tokens, many
-// weight rows: each activation stage is read once per 256 rows).  Below that
-// the 64 x 64 tile, whose waves (one 32 x 32 block each) have little to overlap
-// a stage's LDS reads and dependent MFMAs with: K groups add waves that work
-// on other stages of the same tile, the more the longer K.  Measured on the
-// prefill, H-BitLinear (M 512) and Llama-block (M 256) shapes.
+// Tile choice.  The 448 x 128 tile when it gives two or more full rounds of
+// the 256 CUs, or between three quarters of one round and one round; else the
+// 128 x 128 tile when it gives at least 7/8 of a round; below that the 64 x 64
+// tile, whose waves (one 32 x 32 block each) have little to overlap a stage's
+// LDS reads and dependent MFMAs with: K groups add waves that work on other
+// stages of the same tile, the more the longer K.  Measured (graph replays
+// over >= 1 GiB of weight copies) on the prefill, H-BitLinear (M 512) and
+// Llama-block (M 256) shapes and on M 256 ... 2048 at N 8192 ... 28672: the
+// 128 x 128 tile beat the 256 x 128 and 256 x 64 tiles it replaced by 3-15%
+// wherever they were chosen (and the K-group 64 x 64 tiles at K 14336 and
+// 16384 by 11-12% once it has 7/8 of a round), lost to the 448 x 128 tile
+// between 3/4 and one round of that tile (51.1 against 55.4 us at M 768,
+// N 14336) and at two rounds (the prefill FFN shape), and won at 1.5 rounds.
 template <int XF>
 hipError_t launch_tiled(const int8_t* xq, const float* x_scale, const int32_t* x_qsum,
                         const uint8_t* packed, const RowScales& scales, int64_t M, int64_t N,
                         int64_t K, float* y, int32_t* acc, hipStream_t stream) {
     using T = Tiles<XF>;
-    if (tiles_of<typename T::Large>(M, N) >= 2 * kCus)
+    const int64_t large = tiles_of<typename T::Large>(M, N);
+    if (large >= 2 * kCus || (large >= 3 * kCus / 4 && large <= kCus))
         return launch_cfg<typename T::Large>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
-    if (tiles_of<typename T::Mid>(M, N) >= kCus)
-        return launch_cfg<typename T::Mid>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
-    if (tiles_of<typename T::Wide>(M, N) >= kCus)
-        return launch_cfg<typename T::Wide>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    if (tiles_of<typename T::Square>(M, N) >= 7 * kCus / 8)
+        return launch_cfg<typename T::Square>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     const int64_t tiles = tiles_of<typename T::Tiny>(M, N);
     const int64_t stages = (K + kBK - 1) / kBK;
     if (stages >= 48 && tiles >= 2 * kCus)

@@ -75,8 +75,8 @@ I4_FORWARD_CASES = [
     # matrix-core tiles, ragged M, N and K
     (5, 512, 256), (17, 1000, 4096), (100, 333, 192), (33, 65, 64),
     (2100, 14000, 192),   # 448 x 128 tiles
-    (2000, 4100, 64),     # 256 x 128 tiles
-    (250, 16400, 192),    # 256 x 64 tiles
+    (2000, 4100, 64),     # 128 x 128 tiles
+    (250, 16400, 192),    # 128 x 128 tiles (few tokens, many rows)
     (999, 4100, 320),     # 64 x 64 tiles
     (200, 900, 4160),     # 64 x 64 tiles, two K groups, 17 stages
     (100, 333, 12352),    # 64 x 64 tiles, four K groups

@@ -181,11 +181,13 @@ FORWARD_FULL_CASES = [
     (5, 512, 256), (16, 4096, 4096), (17, 1000, 4096), (64, 1024, 4096), (100, 333, 192),
     (128, 128, 128), (256, 1024, 4096), (300, 4099, 1024), (1, 70, 65536), (33, 65, 64),
     # each matrix-core tile size at ragged M, N and K (K not a multiple of the 256-deep stage)
-    (2100, 14000, 192),  # 448 x 128 tiles
-    (2000, 4100, 64),    # 256 x 128 tiles
-    (999, 4100, 320),    # 64 x 64 tiles
+    (2100, 14000, 192),  # 448 x 128 tiles, two or more rounds
+    (900, 14000, 192),   # 448 x 128 tiles, one round
+    (2000, 4100, 64),    # 128 x 128 tiles
+    (999, 4100, 320),    # 128 x 128 tiles, about one round
+    (250, 16400, 192),   # 128 x 128 tiles (few tokens, many rows)
+    (300, 5000, 320),    # 64 x 64 tiles
     (200, 900, 4160),    # 64 x 64 tiles in two K groups (17 stages: one group runs past K)
-    (250, 16400, 192),   # 256 x 64 tiles (few tokens, many rows)
     (100, 333, 12352),   # 64 x 64 tiles in four K groups (49 stages)
     (9, 4100, 576),      # skinny, one row block per workgroup, K split over eight waves
     (16, 9000, 1088),    # skinny, two row blocks
@@ -215,7 +217,7 @@ FORWARD_SAMPLED_CASES = [
     (256, 14336, 4096, False),    # Llama-3-8B block gate/up at M = 256
     (16, 14336, 4096, False),     # ... at M = 16
     (256, 4096, 14336, False),    # down projection at M = 256
-    (256, 28672, 4096, False),    # grouped gate|up at M = 256 (256 x 64 tiles)
+    (256, 28672, 4096, False),    # grouped gate|up at M = 256 (128 x 128 tiles)
     (1000, 2100, 12352, False),   # 128 x 64 tiles in three K groups, ragged M, N and K
 ]
 
@@ -468,7 +470,7 @@ def test_hadamard_quant_act_f6(orc, dev, M, K, with_gain):
 F6_FORWARD_CASES = [
     (1, 100, 256), (3, 77, 4096), (64, 333, 1024), (200, 900, 2048), (100, 250, 320),
     (2100, 14000, 256),   # 448 x 128 tiles
-    (2000, 4100, 192),    # 256 x 128 tiles, K not a multiple of the 256-deep stage
+    (2000, 4100, 192),    # 128 x 128 tiles, K not a multiple of the 256-deep stage
     (512, 4096, 64),
     (100, 333, 12352),    # 64 x 64 tiles in four K groups
 ]

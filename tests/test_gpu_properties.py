@@ -108,7 +108,7 @@ def test_every_entry_point_is_deterministic(dev):
 
 def test_token_counts_across_kernels_agree(dev):
     # the first rows through the GEMV (M <= 4), the skinny kernel (M <= 16) and
-    # the GEMM tilings (64x64 at small M; 256x128 at N = 4096 and 448x128 at
+    # the GEMM tilings (64x64 at small M; 128x128 at N = 4096 and 448x128 at
     # N = 14336 for M = 2048) must equal the M = 2048 result row for row
     K = 4096
     for N in (4096, 14336):
