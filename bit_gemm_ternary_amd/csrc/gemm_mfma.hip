@@ -627,7 +627,8 @@ struct Tiles {
     using Large = GemmCfg<448, 128, 7, 2, 1, 2, XF>;        // 14 waves, wave tile 64 x 64
     using Square = GemmCfg<128, 128, 4, 2, 1, 2, XF>;       // 8 waves, wave tile 32 x 64
     using TallK3 = GemmCfg<128, 64, 2, 2, 1, 2, XF, 3>;     // 3 K groups of 4 waves (64 x 32)
-    using Tiny = GemmCfg<64, 64, 2, 2, 2, 2, XF>;           // 4 waves, wave tile 32 x 32
+    using TallK2 = GemmCfg<128, 64, 2, 2, 1, 2, XF, 2>;     // 2 K groups of 4 waves (64 x 32)
+    using Tiny = GemmCfg<64, 64, 2, 2, 2, 2, XF>;           // 4 waves, wave tile 32 x 32 (tile count only)
     using TinyK2 = GemmCfg<64, 64, 2, 2, 2, 2, XF, 2>;      // 2 K groups of 4 waves
     using TinyK4 = GemmCfg<64, 64, 2, 2, 1, 2, XF, 4>;      // 4 K groups of 4 waves
 };
@@ -636,10 +637,14 @@ constexpr int64_t kCus = 256;
 
 // Tile choice.  The 448 x 128 tile when it gives two or more full rounds of
 // the 256 CUs, or between three quarters of one round and one round; else the
-// 128 x 128 tile when it gives at least 7/8 of a round; below that the 64 x 64
-// tile, whose waves (one 32 x 32 block each) have little to overlap a stage's
-// LDS reads and dependent MFMAs with: K groups add waves that work on other
-// stages of the same tile, the more the longer K.  Measured (graph replays
+// 128 x 128 tile when it gives at least 7/8 of a round; below that 128 x 64
+// and 64 x 64 tiles, whose waves (one 64 x 32 or 32 x 32 block each) have
+// little to overlap a stage's LDS reads and dependent MFMAs with: K groups add
+// waves that work on other stages of the same tile, the more the longer K or
+// the fewer the tiles (128 x 64 tiles in two K groups when there are >= 384
+// 64 x 64 tiles' worth of output and <= 32 stages: 5% ahead of one group of
+// 64 x 64 tiles at M 256 x N 6144 and M 512 x N 4096; four K groups of 64 x 64
+// tiles up to one round: 7-9% ahead of two at M 256, N 4096 and 1024).  Measured (graph replays
 // over >= 1 GiB of weight copies) on the prefill, H-BitLinear (M 512) and
 // Llama-block (M 256) shapes and on M 256 ... 2048 at N 8192 ... 28672: the
 // 128 x 128 tile beat the 256 x 128 and 256 x 64 tiles it replaced by 3-15%
@@ -664,7 +669,9 @@ hipError_t launch_tiled(const int8_t* xq, const float* x_scale, const int32_t* x
     if (stages >= 48)
         return launch_cfg<typename T::TinyK4>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     if (tiles >= 384 && stages <= 32)
-        return launch_cfg<typename T::Tiny>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+        return launch_cfg<typename T::TallK2>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
+    if (tiles <= kCus)
+        return launch_cfg<typename T::TinyK4>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
     return launch_cfg<typename T::TinyK2>(xq, x_scale, x_qsum, packed, scales, M, N, K, y, acc, stream);
 }
 

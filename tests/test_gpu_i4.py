@@ -77,8 +77,10 @@ I4_FORWARD_CASES = [
     (2100, 14000, 192),   # 448 x 128 tiles
     (2000, 4100, 64),     # 128 x 128 tiles
     (250, 16400, 192),    # 128 x 128 tiles (few tokens, many rows)
-    (999, 4100, 320),     # 64 x 64 tiles
-    (200, 900, 4160),     # 64 x 64 tiles, two K groups, 17 stages
+    (999, 4100, 320),     # 128 x 128 tiles, about one round
+    (300, 5000, 320),     # 128 x 64 tiles, two K groups
+    (300, 4000, 320),     # 64 x 64 tiles, two K groups
+    (200, 900, 4160),     # 64 x 64 tiles, four K groups, 17 stages
     (100, 333, 12352),    # 64 x 64 tiles, four K groups
 ]
 

@@ -186,8 +186,9 @@ FORWARD_FULL_CASES = [
     (2000, 4100, 64),    # 128 x 128 tiles
     (999, 4100, 320),    # 128 x 128 tiles, about one round
     (250, 16400, 192),   # 128 x 128 tiles (few tokens, many rows)
-    (300, 5000, 320),    # 64 x 64 tiles
-    (200, 900, 4160),    # 64 x 64 tiles in two K groups (17 stages: one group runs past K)
+    (300, 5000, 320),    # 128 x 64 tiles in two K groups
+    (300, 4000, 320),    # 64 x 64 tiles in two K groups
+    (200, 900, 4160),    # 64 x 64 tiles in four K groups (17 stages: three groups run past K)
     (100, 333, 12352),   # 64 x 64 tiles in four K groups (49 stages)
     (9, 4100, 576),      # skinny, one row block per workgroup, K split over eight waves
     (16, 9000, 1088),    # skinny, two row blocks
@@ -471,7 +472,8 @@ F6_FORWARD_CASES = [
     (1, 100, 256), (3, 77, 4096), (64, 333, 1024), (200, 900, 2048), (100, 250, 320),
     (2100, 14000, 256),   # 448 x 128 tiles
     (2000, 4100, 192),    # 128 x 128 tiles, K not a multiple of the 256-deep stage
-    (512, 4096, 64),
+    (512, 4096, 64),      # 128 x 64 tiles in two K groups
+    (300, 4000, 320),     # 64 x 64 tiles in two K groups
     (100, 333, 12352),    # 64 x 64 tiles in four K groups
 ]
 
